@@ -1,0 +1,121 @@
+"""Pins of the oracle projection and gate/up pair: exact rational brute force on
+tiny shapes, numpy fp64 matmul, one-hot and zero special cases, the hand-worked
+row, row and selection independence, and scipy's logistic function for SiLU."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import workloads
+from test_oracle_quantizer import load_kv
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _gamma(k):
+    u = 2.0 ** -53
+    return k * u / (1 - k * u)
+
+
+def test_worked_row_gemv(oracle_lib):
+    g = load_kv("worked_row.txt")
+    W = np.array([float(v) for v in g["W"]], np.float32)[None, :]
+    codes, scales, sg = oracle_lib.quantize(W)
+    x = workloads.bf16_bits(np.array([[float(v) for v in g["x"]]], np.float32))
+    y, a, yb = oracle_lib.gemv(codes, scales, sg, x)
+    assert y[0, 0] == float(g["y"][0])
+    assert a[0, 0] == float(g["absdot"][0])
+    assert yb[0, 0] == int(g["y_bf16"][0], 16)
+
+
+def test_gemv_exact_rational_brute_force(oracle_lib):
+    rng = np.random.default_rng(21)
+    for n, k, rows in [(3, 16, 1), (5, 48, 3), (8, 64, 8)]:
+        c = workloads.case(n, k, rows, seed=int(rng.integers(1 << 30)))
+        codes, scales, sg = oracle_lib.quantize(c["W"])
+        D = oracle_lib.dequant(codes, scales, sg)
+        y, a, yb = oracle_lib.gemv(codes, scales, sg, c["x"])
+        xf = _bf16_to_f64(c["x"])
+        for r in range(rows):
+            for j in range(n):
+                exact = sum(Fraction(float(D[j, t])) * Fraction(float(xf[r, t])) for t in range(k))
+                absd = sum(abs(Fraction(float(D[j, t])) * Fraction(float(xf[r, t]))) for t in range(k))
+                bound = _gamma(k) * float(absd)
+                assert abs(Fraction(y[r, j]) - exact) <= Fraction(bound)
+                assert abs(Fraction(a[r, j]) - absd) <= Fraction(bound)
+                # bf16 of the exact value, by search over neighbouring bf16 values
+                yf = float(exact)
+                cand = np.array([workloads.bf16_bits(np.array([yf], np.float32))[0]], np.uint16)
+                nb = [int(cand[0]) + d for d in (-2, -1, 0, 1, 2)]
+                nb = [b for b in nb if 0 <= b < 65536]
+                dist = [(abs(Fraction(float(_bf16_to_f64(np.array([b], np.uint16))[0])) - exact), b) for b in nb]
+                dmin = min(d for d, _ in dist)
+                assert any(b == int(yb[r, j]) and d == dmin for d, b in dist)
+
+
+def test_gemv_vs_numpy_matmul(oracle_lib):
+    c = workloads.case(200, 784, 5, seed=9)
+    codes, scales, sg = oracle_lib.quantize(c["W"])
+    D = oracle_lib.dequant(codes, scales, sg).astype(np.float64)
+    xf = _bf16_to_f64(c["x"])
+    ref = xf @ D.T
+    refabs = np.abs(xf) @ np.abs(D).T
+    y, a, _ = oracle_lib.gemv(codes, scales, sg, c["x"])
+    bound = 2 * _gamma(784) * refabs
+    assert np.all(np.abs(y - ref) <= bound)
+    assert np.all(np.abs(a - refabs) <= bound)
+
+
+def test_gemv_one_hot_zero_and_selection(oracle_lib):
+    c = workloads.case(64, 256, 1, seed=10)
+    codes, scales, sg = oracle_lib.quantize(c["W"])
+    D = oracle_lib.dequant(codes, scales, sg)
+    for col in (0, 17, 255):
+        x = np.zeros((1, 256), np.float32)
+        x[0, col] = 1.0
+        y, _, _ = oracle_lib.gemv(codes, scales, sg, workloads.bf16_bits(x))
+        assert np.array_equal(y[0], D[:, col].astype(np.float64))
+    y, a, yb = oracle_lib.gemv(codes, scales, sg, np.zeros((2, 256), np.uint16))
+    assert not y.any() and not a.any() and not yb.any()
+    assert not np.signbit(y).any()
+    zc = np.zeros_like(codes)
+    y, _, _ = oracle_lib.gemv(zc, scales, sg, c["x"])
+    assert not y.any()
+    # a row's result does not depend on the other rows; selection = columns
+    c8 = workloads.case(64, 256, 8, seed=12)
+    y8, a8, b8 = oracle_lib.gemv(codes, scales, sg, c8["x"])
+    y3, _, _ = oracle_lib.gemv(codes, scales, sg, c8["x"][3:4])
+    assert np.array_equal(y8[3], y3[0])
+    sel = np.array([63, 0, 5, 5, 40])
+    ys, as_, bs = oracle_lib.gemv(codes, scales, sg, c8["x"], sel=sel)
+    assert np.array_equal(ys, y8[:, sel]) and np.array_equal(bs, b8[:, sel])
+
+
+def test_dual_silu_vs_scipy(oracle_lib):
+    c = workloads.case(48, 320, 4, seed=13, dual=True)
+    gq = oracle_lib.quantize(c["W"])
+    uq = oracle_lib.quantize(c["W_up"])
+    out = oracle_lib.gemv_dual_silu(gq, uq, c["x"])
+    g, _, _ = oracle_lib.gemv(*gq, c["x"])
+    u, _, _ = oracle_lib.gemv(*uq, c["x"])
+    assert np.array_equal(out["g"], g) and np.array_equal(out["u"], u)
+    ref = g * expit(g) * u
+    assert np.allclose(out["o"], ref, rtol=1e-14, atol=1e-300)
+
+
+def test_dual_silu_extremes(oracle_lib):
+    # a weight row that yields g = 0 and one with large |g|: check the composition
+    W = np.zeros((2, 16), np.float32)
+    W[1, 0] = 100.0
+    U = np.ones((2, 16), np.float32)
+    gq = oracle_lib.quantize(W)
+    uq = oracle_lib.quantize(U)
+    x = workloads.bf16_bits(np.array([[1.0] * 16, [-1.0] + [0.0] * 15], np.float32))
+    out = oracle_lib.gemv_dual_silu(gq, uq, x)
+    assert out["o"][0, 0] == 0.0
+    assert out["o"][0, 1] == pytest.approx(100.0 * 16.0, rel=1e-12)   # silu(100) = 100
+    assert abs(out["o"][1, 1]) < 1e-40                                  # silu(-100) ~ 0
