@@ -1,0 +1,275 @@
+"""MI355X (gfx950) weight-only NVFP4 projection GEMV -- Python binding.
+
+Thin ctypes layer over ``libnvfp4_hip.so`` (C ABI in ``include/nvfp4.h``).  It
+only marshals arguments: torch owns device memory and streams, and every step
+of the computation runs in the library's HIP kernels.  There is no CPU
+fallback; calling into the library without a built ``libnvfp4_hip.so`` raises.
+
+Entry points (same names as the C ABI):
+  nvfp4_packed_bytes, nvfp4_pack, nvfp4_unpack, nvfp4_dequant,
+  nvfp4_quantize_workspace_bytes, nvfp4_quantize,
+  nvfp4_workspace_bytes, nvfp4_gemv, nvfp4_gemv_dual_silu,
+  nvfp4_abi_version, nvfp4_strerror, nvfp4_last_error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4_hip.so")
+
+NVFP4_LAYOUT_MAGIC = 0x34465056
+NVFP4_LAYOUT_VERSION = 1
+NVFP4_MAX_ROWS = 8
+NVFP4_OUT_BF16 = 0
+NVFP4_OUT_F32 = 1
+
+STATUS = {
+    0: "NVFP4_OK", -1: "NVFP4_E_NULL", -2: "NVFP4_E_SHAPE", -3: "NVFP4_E_ROWS", -4: "NVFP4_E_ALIGN",
+    -5: "NVFP4_E_DTYPE", -6: "NVFP4_E_WORKSPACE", -7: "NVFP4_E_LAYOUT", -8: "NVFP4_E_DEVICE",
+    -9: "NVFP4_E_HIP",
+}
+
+EXPORTS = (
+    "nvfp4_abi_version", "nvfp4_strerror", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
+    "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
+    "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu",
+)
+
+
+class nvfp4_weight(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("layout", ctypes.c_uint32),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("data", ctypes.c_void_p),
+    ]
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d): %s" % (fn, STATUS.get(status, "?"), status, detail))
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libnvfp4_hip.so is not built (%s); run __graft_entry__.build() or "
+                              "python bit_weight_only_nvfp4_amd/build.py" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        wp = ctypes.POINTER(nvfp4_weight)
+        sig = {
+            "nvfp4_abi_version": ([], ctypes.c_int),
+            "nvfp4_strerror": ([ctypes.c_int], ctypes.c_char_p),
+            "nvfp4_last_error": ([], ctypes.c_char_p),
+            "nvfp4_packed_bytes": ([i64, i64], sz),
+            "nvfp4_pack": ([vp, vp, ctypes.c_float, i64, i64, vp, sz, wp, vp], ctypes.c_int),
+            "nvfp4_unpack": ([wp, vp, vp, vp, vp], ctypes.c_int),
+            "nvfp4_dequant": ([wp, vp, vp], ctypes.c_int),
+            "nvfp4_quantize_workspace_bytes": ([i64, i64], sz),
+            "nvfp4_quantize": ([vp, i64, i64, vp, sz, vp, sz, wp, vp], ctypes.c_int),
+            "nvfp4_workspace_bytes": ([i64, i64, ctypes.c_int, ctypes.c_int], sz),
+            "nvfp4_gemv": ([wp, vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp], ctypes.c_int),
+            "nvfp4_gemv_dual_silu": ([wp, wp, vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp], ctypes.c_int),
+        }
+        for name, (argt, rest) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = argt
+            f.restype = rest
+        _lib = L
+        return L
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise Nvfp4Error(fn, status, lib().nvfp4_last_error().decode(errors="replace"))
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def nvfp4_abi_version() -> int:
+    return lib().nvfp4_abi_version()
+
+
+def nvfp4_strerror(status: int) -> str:
+    return lib().nvfp4_strerror(status).decode()
+
+
+def nvfp4_last_error() -> str:
+    return lib().nvfp4_last_error().decode(errors="replace")
+
+
+class PackedWeight:
+    """A packed NVFP4 weight: the device byte buffer plus its C descriptor."""
+
+    def __init__(self, data: torch.Tensor, desc: nvfp4_weight):
+        self.data = data
+        self.desc = desc
+
+    @property
+    def n(self) -> int:
+        return self.desc.n
+
+    @property
+    def k(self) -> int:
+        return self.desc.k
+
+    @property
+    def device(self):
+        return self.data.device
+
+    def global_scale(self) -> float:
+        """s_g as stored in the packed header (synchronizes)."""
+        return float(self.data[:4].view(torch.float32).item())
+
+
+def nvfp4_packed_bytes(n: int, k: int) -> int:
+    return int(lib().nvfp4_packed_bytes(n, k))
+
+
+def _alloc_packed(n, k, device, out):
+    need = nvfp4_packed_bytes(n, k)
+    if need == 0:
+        raise ValueError("invalid NVFP4 shape n=%d k=%d (k must be a positive multiple of 16)" % (n, k))
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=device)
+    return out, need
+
+
+def nvfp4_pack(codes: torch.Tensor, scales: torch.Tensor, global_scale: float,
+               out: torch.Tensor | None = None) -> PackedWeight:
+    """codes uint8 [n, k/2], scales uint8 [n, k/16] (device) -> PackedWeight."""
+    n, half = codes.shape
+    k = 2 * half
+    codes = codes.contiguous()
+    scales = scales.contiguous()
+    buf, need = _alloc_packed(n, k, codes.device, out)
+    desc = nvfp4_weight()
+    _check("nvfp4_pack", lib().nvfp4_pack(_ptr(codes), _ptr(scales), float(global_scale), n, k,
+                                          _ptr(buf), buf.numel(), ctypes.byref(desc), _stream(codes.device)))
+    return PackedWeight(buf, desc)
+
+
+def nvfp4_unpack(w: PackedWeight):
+    """-> (codes uint8 [n, k/2], scales uint8 [n, k/16], s_g float32 [1]) on the device."""
+    codes = torch.empty((w.n, w.k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((w.n, w.k // 16), dtype=torch.uint8, device=w.device)
+    sg = torch.empty(1, dtype=torch.float32, device=w.device)
+    _check("nvfp4_unpack", lib().nvfp4_unpack(ctypes.byref(w.desc), _ptr(codes), _ptr(scales), _ptr(sg),
+                                              _stream(w.device)))
+    return codes, scales, sg
+
+
+def nvfp4_dequant(w: PackedWeight) -> torch.Tensor:
+    out = torch.empty((w.n, w.k), dtype=torch.float32, device=w.device)
+    _check("nvfp4_dequant", lib().nvfp4_dequant(ctypes.byref(w.desc), _ptr(out), _stream(w.device)))
+    return out
+
+
+def nvfp4_quantize_workspace_bytes(n: int, k: int) -> int:
+    return int(lib().nvfp4_quantize_workspace_bytes(n, k))
+
+
+def nvfp4_quantize(W: torch.Tensor, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> PackedWeight:
+    """fp32 weights [n, k] on the device -> PackedWeight (quantized on the GPU)."""
+    if W.dtype != torch.float32:
+        raise TypeError("W must be float32")
+    W = W.contiguous()
+    n, k = W.shape
+    buf, need = _alloc_packed(n, k, W.device, out)
+    wneed = nvfp4_quantize_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(wneed, dtype=torch.uint8, device=W.device)
+    desc = nvfp4_weight()
+    _check("nvfp4_quantize", lib().nvfp4_quantize(_ptr(W), n, k, _ptr(buf), buf.numel(), _ptr(workspace),
+                                                  workspace.numel(), ctypes.byref(desc), _stream(W.device)))
+    return PackedWeight(buf, desc)
+
+
+def nvfp4_workspace_bytes(n: int, k: int, rows: int, dual: bool = False) -> int:
+    return int(lib().nvfp4_workspace_bytes(n, k, rows, int(bool(dual))))
+
+
+# Zeroed split-K workspaces, one per (device, stream): every call leaves its
+# arrival counters at zero, so a workspace is reusable by later calls on the
+# same stream.
+_ws_cache: dict = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(device, need: int) -> torch.Tensor | None:
+    if need == 0:
+        return None
+    key = (device, _stream(device))
+    with _ws_lock:
+        t = _ws_cache.get(key)
+        if t is None or t.numel() < need:
+            t = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+            _ws_cache[key] = t
+        return t
+
+
+_OUT = {torch.bfloat16: NVFP4_OUT_BF16, torch.float32: NVFP4_OUT_F32}
+
+
+def _gemv_common(x, rows_k, out_dtype, out, n):
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if out_dtype not in _OUT:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    x = x.contiguous()
+    rows = x.shape[0]
+    if out is None:
+        out = torch.empty((rows, n), dtype=out_dtype, device=x.device)
+    return x, rows, out
+
+
+def nvfp4_gemv(w: PackedWeight, x: torch.Tensor, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[rows, n] = x[rows, k] @ dequant(w)^T (fp32 accumulation)."""
+    x, rows, out = _gemv_common(x, None, out_dtype, out, w.n)
+    need = nvfp4_workspace_bytes(w.n, w.k, rows, False)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    _check("nvfp4_gemv", lib().nvfp4_gemv(ctypes.byref(w.desc), _ptr(x), rows, _ptr(out), _OUT[out.dtype],
+                                          _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                          _stream(x.device)))
+    return out
+
+
+def nvfp4_gemv_dual_silu(gate: PackedWeight, up: PackedWeight, x: torch.Tensor, out_dtype=torch.bfloat16,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """o[rows, n] = silu(x @ gate^T) * (x @ up^T)."""
+    x, rows, out = _gemv_common(x, None, out_dtype, out, gate.n)
+    need = nvfp4_workspace_bytes(gate.n, gate.k, rows, True)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    _check("nvfp4_gemv_dual_silu",
+           lib().nvfp4_gemv_dual_silu(ctypes.byref(gate.desc), ctypes.byref(up.desc), _ptr(x), rows, _ptr(out),
+                                      _OUT[out.dtype], _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(), _stream(x.device)))
+    return out

@@ -1,0 +1,252 @@
+// nvfp4_api.hip -- the C ABI declared in include/nvfp4.h: argument validation
+// (all of it before any HIP call), the gfx950 capability check, and dispatch to
+// the kernels' launchers on the caller's stream.  No allocation, no
+// synchronization, no state other than the thread-local error message and a
+// per-device cache of the architecture check.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "nvfp4_internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return NVFP4_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_shape(int64_t n, int64_t k) {
+    return n >= 1 && k >= 16 && k % 16 == 0 && n <= kMaxN && k <= (int64_t)1 << 24;
+}
+
+// 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_dev_state[64];
+
+int check_device(const char *fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0)
+        return fail(NVFP4_E_DEVICE, "%s: no HIP device available (%s); NVFP4 on this library needs gfx950", fn,
+                    hipGetErrorString(e));
+    if (dev < 64) {
+        int st = g_dev_state[dev].load(std::memory_order_relaxed);
+        if (st == 1) return NVFP4_OK;
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: hipGetDeviceProperties: %s", fn, hipGetErrorString(e));
+    const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_state[dev].store(is950 ? 1 : 2, std::memory_order_relaxed);
+    if (!is950)
+        return fail(NVFP4_E_DEVICE,
+                    "%s: device %d is %s; NVFP4 weights on this library need gfx950 (E2M1/E4M3 conversion and "
+                    "bf16 dot instructions)",
+                    fn, dev, prop.gcnArchName);
+    return NVFP4_OK;
+}
+
+int hip_status(const char *fn, hipError_t e) {
+    if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+int check_weight(const char *fn, const char *name, const nvfp4_weight *w) {
+    if (!w) return fail(NVFP4_E_NULL, "%s: %s is NULL", fn, name);
+    if (w->magic != NVFP4_LAYOUT_MAGIC || w->layout != NVFP4_LAYOUT_VERSION)
+        return fail(NVFP4_E_LAYOUT, "%s: %s has magic 0x%08x layout %u, expected 0x%08x layout %u", fn, name,
+                    w->magic, w->layout, NVFP4_LAYOUT_MAGIC, NVFP4_LAYOUT_VERSION);
+    if (!valid_shape(w->n, w->k))
+        return fail(NVFP4_E_SHAPE, "%s: %s has n=%lld k=%lld (need 1 <= n <= 2^20, k a positive multiple of 16, k <= 2^24)", fn,
+                    name, (long long)w->n, (long long)w->k);
+    if (!w->data) return fail(NVFP4_E_NULL, "%s: %s->data is NULL", fn, name);
+    if (!aligned(w->data, 16)) return fail(NVFP4_E_ALIGN, "%s: %s->data is not 16-byte aligned", fn, name);
+    return NVFP4_OK;
+}
+
+int check_gemv_args(const char *fn, const void *x, int rows, const void *y, int out_dtype, int64_t n,
+                    int64_t k, int dual, const void *workspace, size_t workspace_bytes) {
+    if (!x) return fail(NVFP4_E_NULL, "%s: x is NULL", fn);
+    if (!y) return fail(NVFP4_E_NULL, "%s: y is NULL", fn);
+    if (rows < 1 || rows > NVFP4_MAX_ROWS)
+        return fail(NVFP4_E_ROWS, "%s: rows=%d outside 1..%d", fn, rows, NVFP4_MAX_ROWS);
+    if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_F32)
+        return fail(NVFP4_E_DTYPE, "%s: out_dtype=%d (0 = bf16, 1 = fp32)", fn, out_dtype);
+    if (!aligned(x, 16)) return fail(NVFP4_E_ALIGN, "%s: x is not 16-byte aligned", fn);
+    if (!aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2))
+        return fail(NVFP4_E_ALIGN, "%s: y is not aligned to its element size", fn);
+    const GemvPlan pl = make_gemv_plan(n, k, rows, dual);
+    const size_t need = pl.counter_bytes + pl.partial_bytes;
+    if (need > 0) {
+        if (!workspace)
+            return fail(NVFP4_E_WORKSPACE, "%s: workspace is NULL but %zu bytes are needed", fn, need);
+        if (workspace_bytes < need)
+            return fail(NVFP4_E_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(NVFP4_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char *nvfp4_strerror(int status) {
+    switch (status) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_E_NULL: return "null pointer";
+        case NVFP4_E_SHAPE: return "invalid shape";
+        case NVFP4_E_ROWS: return "rows out of range";
+        case NVFP4_E_ALIGN: return "misaligned pointer";
+        case NVFP4_E_DTYPE: return "invalid dtype";
+        case NVFP4_E_WORKSPACE: return "workspace missing or too small";
+        case NVFP4_E_LAYOUT: return "packed weight layout mismatch";
+        case NVFP4_E_DEVICE: return "unsupported device";
+        case NVFP4_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *nvfp4_last_error(void) { return g_err; }
+
+size_t nvfp4_packed_bytes(int64_t n, int64_t k) {
+    if (!valid_shape(n, k)) return 0;
+    return (size_t)kHeaderBytes + (size_t)num_strips(n) * (size_t)num_supers(k) * kSuperBytes;
+}
+
+int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, float global_scale, int64_t n, int64_t k,
+               void *packed, size_t packed_bytes, nvfp4_weight *out, void *stream) {
+    static const char *fn = "nvfp4_pack";
+    if (!codes || !scales || !packed || !out) return fail(NVFP4_E_NULL, "%s: a pointer argument is NULL", fn);
+    if (!valid_shape(n, k))
+        return fail(NVFP4_E_SHAPE, "%s: n=%lld k=%lld (need 1 <= n <= 2^20, k a positive multiple of 16, k <= 2^24)", fn,
+                    (long long)n, (long long)k);
+    if (!aligned(packed, 16)) return fail(NVFP4_E_ALIGN, "%s: packed is not 16-byte aligned", fn);
+    const size_t need = nvfp4_packed_bytes(n, k);
+    if (packed_bytes < need)
+        return fail(NVFP4_E_LAYOUT, "%s: packed buffer has %zu bytes, %zu needed", fn, packed_bytes, need);
+    int st = check_device(fn);
+    if (st) return st;
+    st = hip_status(fn, launch_pack(codes, scales, global_scale, n, k, packed, static_cast<hipStream_t>(stream)));
+    if (st) return st;
+    out->magic = NVFP4_LAYOUT_MAGIC;
+    out->layout = NVFP4_LAYOUT_VERSION;
+    out->n = n;
+    out->k = k;
+    out->data = packed;
+    return NVFP4_OK;
+}
+
+int nvfp4_unpack(const nvfp4_weight *w, uint8_t *codes, uint8_t *scales, float *global_scale, void *stream) {
+    static const char *fn = "nvfp4_unpack";
+    int st = check_weight(fn, "w", w);
+    if (st) return st;
+    if (!codes || !scales) return fail(NVFP4_E_NULL, "%s: codes or scales is NULL", fn);
+    if (global_scale && !aligned(global_scale, 4))
+        return fail(NVFP4_E_ALIGN, "%s: global_scale is not 4-byte aligned", fn);
+    st = check_device(fn);
+    if (st) return st;
+    return hip_status(fn, launch_unpack(w->data, w->n, w->k, codes, scales, global_scale,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_dequant(const nvfp4_weight *w, float *out, void *stream) {
+    static const char *fn = "nvfp4_dequant";
+    int st = check_weight(fn, "w", w);
+    if (st) return st;
+    if (!out) return fail(NVFP4_E_NULL, "%s: out is NULL", fn);
+    if (!aligned(out, 16)) return fail(NVFP4_E_ALIGN, "%s: out is not 16-byte aligned", fn);
+    st = check_device(fn);
+    if (st) return st;
+    return hip_status(fn, launch_dequant(w->data, w->n, w->k, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t nvfp4_quantize_workspace_bytes(int64_t n, int64_t k) {
+    if (!valid_shape(n, k)) return 0;
+    return quantize_workspace_bytes(n, k);
+}
+
+int nvfp4_quantize(const float *W, int64_t n, int64_t k, void *packed, size_t packed_bytes, void *workspace,
+                   size_t workspace_bytes, nvfp4_weight *out, void *stream) {
+    static const char *fn = "nvfp4_quantize";
+    if (!W || !packed || !workspace || !out) return fail(NVFP4_E_NULL, "%s: a pointer argument is NULL", fn);
+    if (!valid_shape(n, k))
+        return fail(NVFP4_E_SHAPE, "%s: n=%lld k=%lld (need 1 <= n <= 2^20, k a positive multiple of 16, k <= 2^24)", fn,
+                    (long long)n, (long long)k);
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(workspace, 16))
+        return fail(NVFP4_E_ALIGN, "%s: W, packed and workspace must be 16-byte aligned", fn);
+    const size_t need = nvfp4_packed_bytes(n, k);
+    if (packed_bytes < need)
+        return fail(NVFP4_E_LAYOUT, "%s: packed buffer has %zu bytes, %zu needed", fn, packed_bytes, need);
+    const size_t wneed = quantize_workspace_bytes(n, k);
+    if (workspace_bytes < wneed)
+        return fail(NVFP4_E_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, wneed);
+    int st = check_device(fn);
+    if (st) return st;
+    st = hip_status(fn, launch_quantize(W, n, k, packed, workspace, static_cast<hipStream_t>(stream)));
+    if (st) return st;
+    out->magic = NVFP4_LAYOUT_MAGIC;
+    out->layout = NVFP4_LAYOUT_VERSION;
+    out->n = n;
+    out->k = k;
+    out->data = packed;
+    return NVFP4_OK;
+}
+
+size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual) {
+    if (!valid_shape(n, k) || rows < 1 || rows > NVFP4_MAX_ROWS) return 0;
+    const GemvPlan pl = make_gemv_plan(n, k, rows, dual != 0);
+    return pl.counter_bytes + pl.partial_bytes;
+}
+
+int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    static const char *fn = "nvfp4_gemv";
+    int st = check_weight(fn, "w", w);
+    if (st) return st;
+    st = check_gemv_args(fn, x, rows, y, out_dtype, w->n, w->k, 0, workspace, workspace_bytes);
+    if (st) return st;
+    st = check_device(fn);
+    if (st) return st;
+    const GemvPlan pl = make_gemv_plan(w->n, w->k, rows, 0);
+    return hip_status(fn, launch_gemv(pl, w->data, nullptr, x, y, out_dtype == NVFP4_OUT_F32, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const void *x, int rows, void *y,
+                         int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "nvfp4_gemv_dual_silu";
+    int st = check_weight(fn, "gate", gate);
+    if (st) return st;
+    st = check_weight(fn, "up", up);
+    if (st) return st;
+    if (gate->n != up->n || gate->k != up->k)
+        return fail(NVFP4_E_SHAPE, "%s: gate is %lldx%lld but up is %lldx%lld", fn, (long long)gate->n,
+                    (long long)gate->k, (long long)up->n, (long long)up->k);
+    st = check_gemv_args(fn, x, rows, y, out_dtype, gate->n, gate->k, 1, workspace, workspace_bytes);
+    if (st) return st;
+    st = check_device(fn);
+    if (st) return st;
+    const GemvPlan pl = make_gemv_plan(gate->n, gate->k, rows, 1);
+    return hip_status(fn, launch_gemv(pl, gate->data, up->data, x, y, out_dtype == NVFP4_OUT_F32, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

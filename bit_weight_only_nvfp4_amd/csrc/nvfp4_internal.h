@@ -1,0 +1,119 @@
+// nvfp4_internal.h -- layout constants, device codecs and launcher declarations
+// shared by the translation units of the gfx950 NVFP4 library.
+//
+// Device codecs (verified exhaustively against the CPU oracle through
+// nvfp4_dequant and the quantizer tests):
+//   * E2M1 pair -> bf16 pair: v_cvt_scalef32_pk_bf16_fp4 with scale 1.0.  The
+//     instruction applies only the exponent of its fp32 scale operand, so the
+//     E4M3 group scale (which has mantissa bits) is applied separately; the low
+//     nibble becomes the low bf16.
+//   * OCP E4M3 byte -> fp32: v_cvt_f32_fp8 (OCP encoding on gfx950, NaN kept).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+// ---- packed layout (version 1) -------------------------------------------
+constexpr int kHeaderBytes = 256;
+constexpr int kStripN = 64;        // output features per strip = lanes of a wave
+constexpr int kSuperK = 256;       // k per super-tile
+constexpr int kTileK = 32;         // k per 16-byte code chunk (one lane)
+constexpr int kTilesPerSuper = kSuperK / kTileK;          // 8
+constexpr int kChunkBytes = 16 * kStripN;                  // 1024: one wave load
+constexpr int kScaleOffset = kTilesPerSuper * kChunkBytes; // 8192
+constexpr int kSuperBytes = kScaleOffset + kChunkBytes;    // 9216
+
+// Split-K arrival counters live in a fixed region at the front of every
+// projection workspace, one per strip, for up to kMaxStrips strips (n <= 2^20).
+// The region does not depend on the call's shape, so partial sums of one call
+// can never land where another call's counters are: a zero-filled workspace
+// stays valid for calls of any shape, since every call returns its counters
+// to zero.
+constexpr int64_t kMaxN = (int64_t)1 << 20;
+constexpr int64_t kMaxStrips = kMaxN / kStripN;                 // 16384
+constexpr size_t kCounterRegionBytes = (size_t)kMaxStrips * 4;  // 64 KiB
+
+struct Header {
+    float global_scale;
+    uint32_t magic;
+    uint32_t layout;
+    uint32_t reserved;
+    int64_t n;
+    int64_t k;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t num_strips(int64_t n) { return ceil_div(n, kStripN); }
+inline int64_t num_supers(int64_t k) { return ceil_div(k, kSuperK); }
+
+// ---- device codecs ----------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// byte `sel` of `word` (two E2M1 codes) -> two bf16, low nibble first
+template <int SEL>
+__device__ __forceinline__ bf16x2_t e2m1x2_to_bf16x2(uint32_t word) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
+}
+
+// byte `sel` of `word` (OCP E4M3) -> fp32
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t word) {
+    return __builtin_amdgcn_cvt_f32_fp8(word, SEL);
+}
+
+__device__ __forceinline__ float e4m3_to_f32_dyn(uint32_t word, int sel) {
+    switch (sel & 3) {
+        case 0: return e4m3_to_f32<0>(word);
+        case 1: return e4m3_to_f32<1>(word);
+        case 2: return e4m3_to_f32<2>(word);
+        default: return e4m3_to_f32<3>(word);
+    }
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(bf16x2_t v) {
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) << 16);
+}
+__device__ __forceinline__ float bf16_hi_to_f32(bf16x2_t v) {
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFF0000u);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---- launchers (host side, defined in the .hip files) -----------------------
+struct GemvPlan {
+    int64_t n, k;
+    int rows, nmat;
+    int strips, supers;       // S, T
+    int waves;                // waves per workgroup
+    int supers_per_part;      // super-tiles one workgroup covers
+    int parts;                // split-K factor P
+    size_t counter_bytes;     // per-strip arrival counters (0 if parts == 1)
+    size_t partial_bytes;     // fp32 partial sums [P][nmat][rows][n_pad]
+    size_t lds_bytes;
+};
+
+GemvPlan make_gemv_plan(int64_t n, int64_t k, int rows, int dual);
+
+hipError_t launch_gemv(const GemvPlan &plan, const void *w0, const void *w1, const void *x,
+                       void *y, int out_f32, void *workspace, hipStream_t stream);
+hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
+                       int64_t n, int64_t k, void *packed, hipStream_t stream);
+hipError_t launch_unpack(const void *packed, int64_t n, int64_t k, uint8_t *codes,
+                         uint8_t *scales, float *global_scale, hipStream_t stream);
+hipError_t launch_dequant(const void *packed, int64_t n, int64_t k, float *out,
+                          hipStream_t stream);
+size_t quantize_workspace_bytes(int64_t n, int64_t k);
+hipError_t launch_quantize(const float *W, int64_t n, int64_t k, void *packed,
+                           void *workspace, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,163 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) weight-only NVFP4 projection library.
+ *
+ * Weight-only 4-bit projection ("w4a16" GEMV): weights are NVFP4 -- E2M1 codes,
+ * one OCP E4M3 scale per 16 consecutive weights of an output row, one FP32
+ * per-tensor scale -- and activations are bf16, 1..8 rows per call.  The
+ * format and kernel family are the ones named on the Qwen3.8-27B-NVFP4
+ * blueprint page: "Precision" table (weights nvfp4/g16, activations bf16) and
+ * "Kernels" table (w4a16_gemv_qg / _sw / _dual / _dual_sw, with the planner
+ * setting row_tiers=by_rows choosing a variant per row count).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are device memory of the current HIP device; host
+ *     pointers are marked "host".  The caller owns every buffer; the library
+ *     never allocates, frees, or keeps a pointer after returning.
+ *   - All work is enqueued on `stream` (a hipStream_t, NULL = default stream)
+ *     with no synchronization, so calls are capturable in a HIP graph.
+ *   - Status: 0 (NVFP4_OK) or a negative NVFP4_E_* code, returned
+ *     synchronously.  Every argument check happens before any HIP call, so
+ *     argument errors never touch the device.  nvfp4_last_error() gives a
+ *     thread-local message for the last failure.  Faults inside a kernel
+ *     surface asynchronously, at the caller's next synchronization.
+ *   - The library refuses devices other than gfx950 (NVFP4_E_DEVICE), with a
+ *     message naming the architecture found and the one required -- as the
+ *     TensorFold issue #603 thread asks of an engine: refuse a format the device
+ *     cannot run and name the missing capability.
+ *
+ * Canonical (unpacked) NVFP4 tensors, row-major:
+ *   codes  [n][k/2]  byte j of a row: element 2j in bits 0..3, 2j+1 in bits 4..7;
+ *                    code bit 3 = sign, bits 2..1 = exponent (bias 1), bit 0 =
+ *                    mantissa: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6;
+ *   scales [n][k/16] OCP E4M3 byte per group of 16 consecutive k (bytes 0x7F
+ *                    and 0xFF are NaN; the quantizer never produces them);
+ *   global_scale     FP32 multiplier s_g: weight = code * scale * s_g.
+ *   k must be a positive multiple of 16 and at most 2^24; 1 <= n <= 2^20.
+ *
+ * Packed (device-tiled) weight, produced by nvfp4_pack / nvfp4_quantize:
+ *   [256-byte header][strip 0: super-tiles 0..T-1][strip 1 ...] ...
+ *   strip = 64 output features, super-tile = 64 features x 256 k = 9216 bytes:
+ *   8 code chunks of 1024 bytes (chunk t, lane l: 16 bytes = codes of feature
+ *   64*s+l for k = 256*u + 32*t .. +31, canonical nibble order) followed by a
+ *   1024-byte scale chunk (lane l: 16 bytes = the 16 group scales of feature
+ *   64*s+l in the super-tile).  Features >= n and k >= k are zero padding.
+ *   The header holds s_g (float at byte 0), the layout magic and version, n, k.
+ *   One wave instruction therefore reads one whole, aligned 1 KB run.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+#define NVFP4_LAYOUT_MAGIC 0x34465056u /* "VPF4" */
+#define NVFP4_LAYOUT_VERSION 1u
+#define NVFP4_MAX_ROWS 8
+
+enum {
+    NVFP4_OK = 0,
+    NVFP4_E_NULL = -1,      /* a required pointer is NULL                      */
+    NVFP4_E_SHAPE = -2,     /* n or k out of range, k % 16 != 0, mismatched pair */
+    NVFP4_E_ROWS = -3,      /* rows outside 1..NVFP4_MAX_ROWS                  */
+    NVFP4_E_ALIGN = -4,     /* a pointer is not aligned as documented          */
+    NVFP4_E_DTYPE = -5,     /* unknown out_dtype                               */
+    NVFP4_E_WORKSPACE = -6, /* workspace missing or smaller than required      */
+    NVFP4_E_LAYOUT = -7,    /* nvfp4_weight magic/version/size mismatch        */
+    NVFP4_E_DEVICE = -8,    /* no HIP device, or not gfx950                    */
+    NVFP4_E_HIP = -9        /* a HIP runtime call or launch failed             */
+};
+
+enum { NVFP4_OUT_BF16 = 0, NVFP4_OUT_F32 = 1 };
+
+/* Descriptor of a packed weight.  A plain value: copy it freely.  `data` is
+ * caller-owned device memory of nvfp4_packed_bytes(n, k) bytes, 16-byte
+ * aligned. */
+typedef struct nvfp4_weight {
+    uint32_t magic;   /* NVFP4_LAYOUT_MAGIC                         */
+    uint32_t layout;  /* NVFP4_LAYOUT_VERSION                       */
+    int64_t n;        /* output features                            */
+    int64_t k;        /* input features, multiple of 16             */
+    void *data;       /* device: header + super-tiles               */
+} nvfp4_weight;
+
+int nvfp4_abi_version(void);
+const char *nvfp4_strerror(int status);
+/* thread-local detail of the last failure on this thread ("" if none) */
+const char *nvfp4_last_error(void);
+
+/* Bytes of the packed buffer for an [n x k] weight; 0 if the shape is invalid. */
+size_t nvfp4_packed_bytes(int64_t n, int64_t k);
+
+/* Re-tile canonical codes/scales (device) into the packed layout and write the
+ * header (s_g = global_scale).  The weight-preparation step that the pages'
+ * runtimes run on the device before decode (kern README: "weight_prep" kernel
+ * and the device "load" program that assembles fused qkv / gate_up buffers).
+ * Byte permutation only -- no arithmetic.  codes/scales need no alignment;
+ * packed must be 16-byte aligned with packed_bytes >= nvfp4_packed_bytes(n,k).
+ * *out (host) is filled on success. */
+int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
+               int64_t n, int64_t k, void *packed, size_t packed_bytes,
+               nvfp4_weight *out, void *stream);
+
+/* Inverse of nvfp4_pack (test and inspection use): writes canonical codes
+ * [n][k/2], scales [n][k/16] and, if global_scale is not NULL, s_g (device
+ * float). */
+int nvfp4_unpack(const nvfp4_weight *w, uint8_t *codes, uint8_t *scales,
+                 float *global_scale, void *stream);
+
+/* Dequantize to fp32 out[n][k] = fp32(fp32(e2m1 * e4m3) * s_g), using the same
+ * device decode routines as the projection kernels.  out 16-byte aligned. */
+int nvfp4_dequant(const nvfp4_weight *w, float *out, void *stream);
+
+/* Quantize fp32 weights W[n][k] (device, 16-byte aligned) straight into the
+ * packed layout: s_g = amax/(448*6); per 16-group E4M3 scale
+ * RNE_sat((amax_g/6)/s_g); codes E2M1 RNE_sat(w / (e4m3(scale)*s_g)); a group
+ * whose scale decodes to 0 gets all-zero codes.  Bit-identical to the CPU
+ * quantizer it is tested against.  The step before the projection: the
+ * veloGB10 setup page's "--quantize all" from the bf16 checkpoint, which it
+ * says gives output identical to the published NVFP4 artifact.
+ * workspace: device, >= nvfp4_quantize_workspace_bytes(n, k) bytes, 16-byte
+ * aligned; no initialization needed.  The status word (int32 at workspace
+ * byte 0) is set by the device to nonzero if a weight is not finite (the
+ * packed contents are then unspecified) and to zero otherwise. */
+size_t nvfp4_quantize_workspace_bytes(int64_t n, int64_t k);
+int nvfp4_quantize(const float *W, int64_t n, int64_t k, void *packed, size_t packed_bytes,
+                   void *workspace, size_t workspace_bytes, nvfp4_weight *out, void *stream);
+
+/* Workspace needed by nvfp4_gemv (dual = 0) or nvfp4_gemv_dual_silu (dual = 1)
+ * for this shape and row count: split-K partial sums plus per-strip arrival
+ * counters.  0 means none.  Deterministic in (n, k, rows, dual). */
+size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual);
+
+/* y[r][j] = s_g * sum_k (code * scale)[j][k] * x[r][k]  for r < rows, j < n.
+ * x: device bf16 [rows][k], 16-byte aligned.  y: device [rows][n], bf16
+ * (NVFP4_OUT_BF16, round to nearest even) or fp32 (NVFP4_OUT_F32), aligned
+ * to its element size; y must not overlap x, the weight or the workspace.
+ * fp32 accumulation; results are bitwise deterministic run to run.
+ * workspace: >= nvfp4_workspace_bytes(n, k, rows, 0) bytes, 16-byte aligned,
+ * ZERO-FILLED before its first use.  Its first 64 KiB hold per-strip arrival
+ * counters at fixed positions and every call returns them to zero, so one
+ * workspace serves any sequence of calls of any shape on one stream; calls
+ * that may run concurrently need distinct workspaces. */
+int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Fused gate/up pair of the SwiGLU FFN: o = silu(g) * u with
+ * g = x W_gate^T, u = x W_up^T (both as in nvfp4_gemv, fp32), silu(g) =
+ * g / (1 + exp(-g)), evaluated after the full reduction -- the blueprint
+ * page's w4a16_gemv_dual kernels with the silu_mul step (its planner splits
+ * that step out as decode_split_silu; here it is the epilogue).  gate and up
+ * must have the same n and k.  workspace as for nvfp4_gemv with dual = 1. */
+int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const void *x,
+                         int rows, void *y, int out_dtype, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/nvfp4.h declares, sizes its buffers as documented, and rejects bad
+arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import bit_weight_only_nvfp4_amd as nv
+    if not os.path.exists(nv.LIB_PATH):
+        from bit_weight_only_nvfp4_amd import build
+        build.build()
+    nv.lib()
+    return nv
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(nv):
+    names = _declared_functions()
+    assert len(names) == 12, names
+    L = ctypes.CDLL(nv.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(nv.EXPORTS)
+
+
+def test_version_and_strerror(nv):
+    assert nv.nvfp4_abi_version() == 1
+    for code in nv.STATUS:
+        assert nv.nvfp4_strerror(code) != "unknown status"
+    assert nv.nvfp4_strerror(-99) == "unknown status"
+
+
+def test_packed_bytes(nv):
+    # header + strips(64 features) * super-tiles(256 k) * 9216 bytes
+    assert nv.nvfp4_packed_bytes(256, 512) == 256 + 4 * 2 * 9216
+    assert nv.nvfp4_packed_bytes(12288, 5120) == 256 + 192 * 20 * 9216
+    assert nv.nvfp4_packed_bytes(65, 272) == 256 + 2 * 2 * 9216
+    assert nv.nvfp4_packed_bytes(1, 16) == 256 + 9216
+    for n, k in [(0, 512), (-1, 512), (256, 0), (256, 24), (256, 8)]:
+        assert nv.nvfp4_packed_bytes(n, k) == 0
+
+
+def test_workspace_bytes(nv):
+    assert nv.nvfp4_workspace_bytes(256, 512, 1) == 0          # one part: no split-K
+    assert nv.nvfp4_workspace_bytes(256, 1024, 8) == 0
+    w1 = nv.nvfp4_workspace_bytes(12288, 5120, 1)
+    assert w1 > 0 and w1 == nv.nvfp4_workspace_bytes(12288, 5120, 1)
+    assert nv.nvfp4_workspace_bytes(12288, 5120, 8) > w1
+    assert nv.nvfp4_workspace_bytes(17408, 5120, 1, dual=True) > nv.nvfp4_workspace_bytes(17408, 5120, 1)
+    for bad in [(256, 512, 0), (256, 512, 9), (0, 512, 1), (256, 24, 1)]:
+        assert nv.nvfp4_workspace_bytes(*bad) == 0
+    assert nv.nvfp4_quantize_workspace_bytes(256, 512) > 0
+    assert nv.nvfp4_quantize_workspace_bytes(256, 20) == 0
+
+
+FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
+
+
+def _weight(nv, n=256, k=512, magic=None, layout=None, data=FAKE):
+    w = nv.nvfp4_weight()
+    w.magic = nv.NVFP4_LAYOUT_MAGIC if magic is None else magic
+    w.layout = nv.NVFP4_LAYOUT_VERSION if layout is None else layout
+    w.n, w.k, w.data = n, k, data
+    return w
+
+
+def _gemv(nv, w, x=FAKE, rows=1, y=FAKE, dtype=0, ws=None, wsb=0):
+    return nv.lib().nvfp4_gemv(ctypes.byref(w) if w is not None else None, x, rows, y, dtype, ws, wsb, None)
+
+
+def test_gemv_argument_errors(nv):
+    E = {v: k for k, v in nv.STATUS.items()}
+    assert _gemv(nv, None) == E["NVFP4_E_NULL"]
+    assert "w is NULL" in nv.nvfp4_last_error()
+    assert _gemv(nv, _weight(nv, magic=0x1234)) == E["NVFP4_E_LAYOUT"]
+    assert _gemv(nv, _weight(nv, layout=7)) == E["NVFP4_E_LAYOUT"]
+    assert _gemv(nv, _weight(nv, k=24)) == E["NVFP4_E_SHAPE"]
+    assert _gemv(nv, _weight(nv, n=0)) == E["NVFP4_E_SHAPE"]
+    assert _gemv(nv, _weight(nv, data=None)) == E["NVFP4_E_NULL"]
+    assert _gemv(nv, _weight(nv, data=FAKE + 8)) == E["NVFP4_E_ALIGN"]
+    assert _gemv(nv, _weight(nv), x=None) == E["NVFP4_E_NULL"]
+    assert _gemv(nv, _weight(nv), y=None) == E["NVFP4_E_NULL"]
+    assert _gemv(nv, _weight(nv), rows=0) == E["NVFP4_E_ROWS"]
+    assert _gemv(nv, _weight(nv), rows=9) == E["NVFP4_E_ROWS"]
+    assert _gemv(nv, _weight(nv), dtype=2) == E["NVFP4_E_DTYPE"]
+    assert _gemv(nv, _weight(nv), x=FAKE + 2) == E["NVFP4_E_ALIGN"]
+    assert _gemv(nv, _weight(nv), y=FAKE + 1) == E["NVFP4_E_ALIGN"]
+    assert _gemv(nv, _weight(nv), y=FAKE + 2, dtype=1) == E["NVFP4_E_ALIGN"]
+    big = _weight(nv, n=12288, k=5120)
+    need = nv.nvfp4_workspace_bytes(12288, 5120, 1)
+    assert _gemv(nv, big) == E["NVFP4_E_WORKSPACE"]
+    assert _gemv(nv, big, ws=FAKE, wsb=need - 1) == E["NVFP4_E_WORKSPACE"]
+    assert _gemv(nv, big, ws=FAKE + 4, wsb=need) == E["NVFP4_E_ALIGN"]
+
+
+def test_dual_and_pack_argument_errors(nv):
+    E = {v: k for k, v in nv.STATUS.items()}
+    L = nv.lib()
+    g, u = _weight(nv, 256, 512), _weight(nv, 256, 1024)
+    assert L.nvfp4_gemv_dual_silu(ctypes.byref(g), ctypes.byref(u), FAKE, 1, FAKE, 0, None, 0, None) == \
+        E["NVFP4_E_SHAPE"]
+    assert L.nvfp4_gemv_dual_silu(ctypes.byref(g), None, FAKE, 1, FAKE, 0, None, 0, None) == E["NVFP4_E_NULL"]
+    out = nv.nvfp4_weight()
+    need = nv.nvfp4_packed_bytes(256, 512)
+    assert L.nvfp4_pack(None, FAKE, 1.0, 256, 512, FAKE, need, ctypes.byref(out), None) == E["NVFP4_E_NULL"]
+    assert L.nvfp4_pack(FAKE, FAKE, 1.0, 256, 520, FAKE, need, ctypes.byref(out), None) == E["NVFP4_E_SHAPE"]
+    assert L.nvfp4_pack(FAKE, FAKE, 1.0, 256, 512, FAKE + 4, need, ctypes.byref(out), None) == E["NVFP4_E_ALIGN"]
+    assert L.nvfp4_pack(FAKE, FAKE, 1.0, 256, 512, FAKE, need - 1, ctypes.byref(out), None) == \
+        E["NVFP4_E_LAYOUT"]
+    qneed = nv.nvfp4_quantize_workspace_bytes(256, 512)
+    assert L.nvfp4_quantize(FAKE, 256, 512, FAKE, need, FAKE, qneed - 1, ctypes.byref(out), None) == \
+        E["NVFP4_E_WORKSPACE"]
+    assert L.nvfp4_quantize(FAKE + 4, 256, 512, FAKE, need, FAKE, qneed, ctypes.byref(out), None) == \
+        E["NVFP4_E_ALIGN"]
+    w = _weight(nv)
+    assert L.nvfp4_dequant(ctypes.byref(w), FAKE + 4, None) == E["NVFP4_E_ALIGN"]
+    assert L.nvfp4_unpack(ctypes.byref(w), None, FAKE, None, None) == E["NVFP4_E_NULL"]
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="valid arguments would launch on a real device")
+def test_no_device_is_refused(nv):
+    E = {v: k for k, v in nv.STATUS.items()}
+    assert _gemv(nv, _weight(nv)) == E["NVFP4_E_DEVICE"]
+    assert "gfx950" in nv.nvfp4_last_error()
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, nv):
+    import bit_weight_only_nvfp4_amd as pkg
+    monkeypatch.setattr(pkg, "_lib", None)
+    monkeypatch.setattr(pkg, "LIB_PATH", "/nonexistent/libnvfp4_hip.so")
+    with pytest.raises(ImportError):
+        pkg.lib()

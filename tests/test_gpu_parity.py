@@ -1,0 +1,372 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+* pack/unpack: byte-exact; the packed buffer equals the layout written out
+  independently here in numpy.
+* dequant: bit-exact (including the sign of zero) over every finite E4M3 scale
+  byte and every E2M1 code.
+* projection / gate-up pair: fp32 within 1e-3 * sum|w*x| of the fp64 oracle,
+  bf16 = RNE of the device fp32 and within one ulp of the oracle's bf16
+  (oracle.check); exact equality on "exact-arithmetic" inputs where every
+  partial sum is representable in fp32, so any dropped, duplicated or misplaced
+  term shows; run-to-run bitwise determinism.
+* device quantizer: codes, scales and s_g bit-identical to the oracle's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import bit_weight_only_nvfp4_amd as nv
+    nv.lib()
+    return nv
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _x_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _pack(nv, q):
+    return nv.nvfp4_pack(_dev(q[0]), _dev(q[1]), float(q[2]))
+
+
+def _run_gemv(nv, w, xb):
+    x = _x_dev(xb)
+    y32 = nv.nvfp4_gemv(w, x, out_dtype=torch.float32)
+    y16 = nv.nvfp4_gemv(w, x, out_dtype=torch.bfloat16)
+    y32b = nv.nvfp4_gemv(w, x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a = y32.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), y32b.cpu().numpy().view(np.uint32)), "not deterministic"
+    return a, _bits(y16)
+
+
+def _run_dual(nv, gw, uw, xb):
+    x = _x_dev(xb)
+    o32 = nv.nvfp4_gemv_dual_silu(gw, uw, x, out_dtype=torch.float32)
+    o16 = nv.nvfp4_gemv_dual_silu(gw, uw, x, out_dtype=torch.bfloat16)
+    o32b = nv.nvfp4_gemv_dual_silu(gw, uw, x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a = o32.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), o32b.cpu().numpy().view(np.uint32)), "not deterministic"
+    return a, _bits(o16)
+
+
+# ---- layout -----------------------------------------------------------------
+
+def _layout_numpy(codes, scales, sg, n, k):
+    """The packed layout, written out from its definition."""
+    S, T = -(-n // 64), -(-k // 256)
+    out = np.zeros(256 + S * T * 9216, np.uint8)
+    out[0:4] = np.frombuffer(np.float32(sg).tobytes(), np.uint8)
+    out[4:8] = np.frombuffer(np.uint32(0x34465056).tobytes(), np.uint8)
+    out[8:12] = np.frombuffer(np.uint32(1).tobytes(), np.uint8)
+    out[16:24] = np.frombuffer(np.int64(n).tobytes(), np.uint8)
+    out[24:32] = np.frombuffer(np.int64(k).tobytes(), np.uint8)
+    cpad = np.zeros((S * 64, T * 128), np.uint8)
+    cpad[:n, : k // 2] = codes
+    spad = np.zeros((S * 64, T * 16), np.uint8)
+    spad[:n, : k // 16] = scales
+    for s in range(S):
+        for u in range(T):
+            base = 256 + (s * T + u) * 9216
+            for t in range(8):
+                blk = cpad[64 * s: 64 * s + 64, 128 * u + 16 * t: 128 * u + 16 * t + 16]
+                out[base + 1024 * t: base + 1024 * (t + 1)] = blk.reshape(-1)
+            out[base + 8192: base + 9216] = spad[64 * s: 64 * s + 64, 16 * u: 16 * u + 16].reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("n,k", [(1, 16), (64, 256), (65, 272), (200, 784), (130, 1040)])
+def test_pack_layout_and_roundtrip(nv, n, k):
+    rng = np.random.default_rng(n * 1000 + k)
+    codes = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (n, k // 16), dtype=np.uint8)
+    w = nv.nvfp4_pack(_dev(codes), _dev(scales), 0.375)
+    torch.cuda.synchronize()
+    assert np.array_equal(w.data.cpu().numpy(), _layout_numpy(codes, scales, 0.375, n, k))
+    c2, s2, g2 = nv.nvfp4_unpack(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(c2.cpu().numpy(), codes)
+    assert np.array_equal(s2.cpu().numpy(), scales)
+    assert g2.item() == 0.375
+    assert w.global_scale() == 0.375
+
+
+# ---- dequant ------------------------------------------------------------------
+
+@pytest.mark.parametrize("sg", [1.0, 0.0123, 2.0 ** -20])
+def test_dequant_exhaustive_codes_and_scales(nv, sg):
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)   # 254 bytes
+    n, k = finite.size, 32
+    scales = np.stack([finite, finite], axis=1)
+    up = np.arange(16, dtype=np.uint8)
+    down = up[::-1]
+    row = np.concatenate([up[0::2] | (up[1::2] << 4), down[0::2] | (down[1::2] << 4)]).astype(np.uint8)
+    codes = np.tile(row, (n, 1))
+    w = nv.nvfp4_pack(_dev(codes), _dev(scales), sg)
+    D = nv.nvfp4_dequant(w)
+    torch.cuda.synchronize()
+    got = D.cpu().numpy()
+    ref = oracle.dequant(codes, scales, np.float32(sg))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_random_ragged(nv):
+    c = workloads.case(200, 784, 1, seed=31)
+    q = oracle.quantize(c["W"])
+    D = nv.nvfp4_dequant(_pack(nv, q))
+    torch.cuda.synchronize()
+    ref = oracle.dequant(*q)
+    assert np.array_equal(D.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# ---- exact-arithmetic projections ---------------------------------------------
+
+def _exact_case(rng, n, k, rows):
+    """codes random; scales in {0.5, 1, 2}; s_g = 1; x in {0, +-0.5, +-1}: every
+    product is a multiple of 2^-3 and |partial sums| < 2^17, so every fp32
+    partial sum in any order is exact."""
+    codes = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = rng.choice(np.array([0x30, 0x38, 0x40], np.uint8), size=(n, k // 16))
+    xv = rng.choice(np.array([-1.0, -0.5, 0.0, 0.5, 1.0], np.float32), size=(rows, k))
+    return codes, scales, np.float32(1.0), workloads.bf16_bits(xv)
+
+
+@pytest.mark.parametrize("n,k", [(1, 16), (64, 256), (200, 784), (130, 4112), (300, 4352)])
+def test_gemv_exact_arithmetic_all_rows(nv, n, k):
+    assert k * 6 * 2 < 2 ** 17
+    rng = np.random.default_rng(n + k)
+    for rows in range(1, 9):
+        codes, scales, sg, xb = _exact_case(rng, n, k, rows)
+        w = nv.nvfp4_pack(_dev(codes), _dev(scales), float(sg))
+        y32, y16 = _run_gemv(nv, w, xb)
+        ref, _, ref16 = oracle.gemv(codes, scales, sg, xb)
+        assert np.array_equal(y32.astype(np.float64), ref), (n, k, rows)
+        assert np.array_equal(y16, ref16), (n, k, rows)
+
+
+@pytest.mark.parametrize("n,k", [(64, 256), (200, 784), (130, 2064)])
+def test_dual_exact_arithmetic(nv, n, k):
+    """gate rows give g = 192 exactly (silu(192) = 192 in fp32 and fp64), so
+    o = 192 * u must match the oracle exactly."""
+    rng = np.random.default_rng(7 * n + k)
+    for rows in (1, 3, 8):
+        ucodes, uscales, sg, xb = _exact_case(rng, n, k, rows)
+        xv = ((xb.astype(np.uint32) << 16).view(np.float32)).copy()
+        xv[:, :16] = 1.0
+        xb = workloads.bf16_bits(xv)
+        gcodes = np.zeros((n, k // 2), np.uint8)
+        gcodes[:, :8] = 0x77                          # sixteen +6 codes in group 0
+        gscales = np.zeros((n, k // 16), np.uint8)
+        gscales[:, 0] = 0x40                          # scale 2: 16 * 6 * 2 * 1 = 192
+        gw = nv.nvfp4_pack(_dev(gcodes), _dev(gscales), 1.0)
+        uw = nv.nvfp4_pack(_dev(ucodes), _dev(uscales), 1.0)
+        o32, o16 = _run_dual(nv, gw, uw, xb)
+        d = oracle.gemv_dual_silu((gcodes, gscales, 1.0), (ucodes, uscales, 1.0), xb)
+        assert np.all(d["g"] == 192.0)
+        assert np.array_equal(o32.astype(np.float64), d["o"]), rows
+        assert np.array_equal(o16, d["o_bf16"])
+
+
+# ---- random projections, every row count --------------------------------------
+
+SHAPES = [(256, 512), (200, 784), (64, 2048), (130, 4112), (72, 17408)]
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_gemv_random_all_rows(nv, n, k):
+    for rows in range(1, 9):
+        c = workloads.case(n, k, rows, seed=100 * rows + n, outlier_frac=0.01)
+        q = oracle.quantize(c["W"])
+        w = _pack(nv, q)
+        y32, y16 = _run_gemv(nv, w, c["x"])
+        ref, absd, ref16 = oracle.gemv(*q, c["x"])
+        check.check_gemv(y32, y16, ref, absd, ref16, label="gemv %dx%d rows=%d" % (n, k, rows))
+
+
+@pytest.mark.parametrize("n,k", [(256, 512), (200, 784), (130, 4112)])
+def test_dual_random_all_rows(nv, n, k):
+    for rows in range(1, 9):
+        c = workloads.case(n, k, rows, seed=200 * rows + n, dual=True)
+        gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
+        o32, o16 = _run_dual(nv, _pack(nv, gq), _pack(nv, uq), c["x"])
+        d = oracle.gemv_dual_silu(gq, uq, c["x"])
+        check.check_dual(o32, o16, d, label="dual %dx%d rows=%d" % (n, k, rows))
+
+
+def test_gemv_zero_inputs(nv):
+    c = workloads.case(130, 784, 3, seed=5)
+    q = oracle.quantize(c["W"])
+    w = _pack(nv, q)
+    y32, y16 = _run_gemv(nv, w, np.zeros_like(c["x"]))
+    assert not y32.any() and not np.signbit(y32).any() and not y16.any()
+    zq = oracle.quantize(np.zeros((130, 784), np.float32))
+    y32, _ = _run_gemv(nv, _pack(nv, zq), c["x"])
+    assert not y32.any()
+
+
+def test_workspace_reuse_and_mixed_calls(nv):
+    """Counters are left at zero: interleaved calls of different shapes, few and
+    many strips, that share one workspace stay correct."""
+    cases = [workloads.case(300, 4352, r, seed=40 + r) for r in (1, 8, 3)]
+    cases.append(workloads.case(4480, 2048, 2, seed=44))
+    qs = [oracle.quantize(c["W"]) for c in cases]
+    need = max(nv.nvfp4_workspace_bytes(c["n"], c["k"], c["rows"]) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        for c, q in zip(cases, qs):
+            w = _pack(nv, q)
+            y = nv.nvfp4_gemv(w, _x_dev(c["x"]), out_dtype=torch.float32, workspace=ws)
+            torch.cuda.synchronize()
+            ref, absd, ref16 = oracle.gemv(*q, c["x"])
+            check.check_gemv(y.cpu().numpy(), None, ref, absd, ref16)
+    torch.cuda.synchronize()
+    assert not ws[: 4 * 70].any().item()     # the strip counters are back at zero
+
+
+# ---- device quantizer ------------------------------------------------------------
+
+def _quantize_dev(nv, W):
+    wt = _dev(W)
+    ws = torch.zeros(nv.nvfp4_quantize_workspace_bytes(*W.shape), dtype=torch.uint8, device="cuda")
+    pw = nv.nvfp4_quantize(wt, workspace=ws)
+    c, s, g = nv.nvfp4_unpack(pw)
+    torch.cuda.synchronize()
+    return pw, c.cpu().numpy(), s.cpu().numpy(), np.float32(g.item()), int(ws[:4].view(torch.int32).item())
+
+
+def _assert_same_quant(nv, W):
+    pw, c, s, g, status = _quantize_dev(nv, W)
+    assert status == 0
+    rc, rs, rg = oracle.quantize(W)
+    assert g == rg
+    assert np.array_equal(s, rs), int(np.sum(s != rs))
+    assert np.array_equal(c, rc), int(np.sum(c != rc))
+    return pw
+
+
+@pytest.mark.parametrize("n,k,outl", [(256, 512, 0.0), (200, 784, 0.01), (65, 4112, 0.2), (1, 16, 0.0)])
+def test_quantize_device_bit_exact_random(nv, n, k, outl):
+    c = workloads.case(n, k, 1, seed=n + k, outlier_frac=outl)
+    _assert_same_quant(nv, c["W"])
+    _assert_same_quant(nv, -c["W"] * np.float32(3.7))
+
+
+def test_quantize_device_special_cases(nv):
+    from test_oracle_quantizer import load_kv
+    g = load_kv("worked_row.txt")
+    _assert_same_quant(nv, np.array([[float(v) for v in g["W"]]], np.float32))
+    _assert_same_quant(nv, np.zeros((3, 32), np.float32))
+    W = np.zeros((2, 48), np.float32)
+    W[0, 0] = 2688.0
+    W[0, 16] = 6.0 * 2.0 ** -9 * 3
+    W[0, 32] = 6.0 * 2.0 ** -9 * 0.4
+    W[1, 16:32] = -1e-9
+    _assert_same_quant(nv, W)
+    # exact E2M1 ties everywhere: W/S lands on every midpoint
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    row = np.concatenate([mids, -mids])
+    W = np.tile(row * np.float32(1.75), (64, 4)).astype(np.float32)
+    W[:, 7::16] = np.float32(10.5)         # 6 * S with S = 1.75 -> scale 448 per group
+    _assert_same_quant(nv, W)
+
+
+def test_quantize_device_flags_non_finite(nv):
+    W = np.ones((64, 256), np.float32)
+    W[5, 7] = np.inf
+    _, _, _, _, status = _quantize_dev(nv, W)
+    assert status != 0
+
+
+# ---- the four single-call workloads at full size ---------------------------------
+
+def _full_gemv(nv, c):
+    pw = _assert_same_quant(nv, c["W"])
+    q = oracle.quantize(c["W"])
+    y32, y16 = _run_gemv(nv, pw, c["x"])
+    ref, absd, ref16 = oracle.gemv(*q, c["x"])
+    return check.check_gemv(y32, y16, ref, absd, ref16, label="full %dx%d rows=%d" % (c["n"], c["k"], c["rows"]))
+
+
+def test_full_tiny(nv):
+    st = _full_gemv(nv, workloads.tiny())
+    assert st["max_err_over_absdot"] < 1e-5
+
+
+def test_full_qkv_rows1(nv):
+    st = _full_gemv(nv, workloads.qkv_rows1())
+    assert st["max_err_over_absdot"] < 1e-5
+
+
+def test_full_down_rows8_outliers(nv):
+    st = _full_gemv(nv, workloads.down_rows8())
+    assert st["max_err_over_absdot"] < 1e-5
+
+
+def test_full_gate_up_rows1(nv):
+    c = workloads.gate_up_rows1()
+    gw = _assert_same_quant(nv, c["W"])
+    uw = _assert_same_quant(nv, c["W_up"])
+    gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
+    o32, o16 = _run_dual(nv, gw, uw, c["x"])
+    d = oracle.gemv_dual_silu(gq, uq, c["x"])
+    st = check.check_dual(o32, o16, d, label="full gate/up")
+    assert st["max_err_over_bound"] < 0.05
+
+
+# ---- the decode-step sweep: one layer, sampled outputs -------------------------------
+
+def test_sweep_layer_sampled(nv):
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(77)
+    layer = 0
+    mats = {}
+    for pi, (name, n, k) in enumerate(workloads.LAYER_PROJECTIONS):
+        Wd = workloads.draw_weights_device(n, k, workloads.sweep_seed(layer, pi), dev)
+        ws = torch.empty(nv.nvfp4_quantize_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+        pw = nv.nvfp4_quantize(Wd, workspace=ws)
+        W = Wd.cpu().numpy()
+        q = oracle.quantize(W)
+        c, s, g = nv.nvfp4_unpack(pw)
+        torch.cuda.synchronize()
+        assert np.float32(g.item()) == q[2]
+        assert np.array_equal(c.cpu().numpy(), q[0]) and np.array_equal(s.cpu().numpy(), q[1])
+        mats[name] = (pw, q)
+        del Wd
+    for rows in workloads.SWEEP_ROWS:
+        for name, n, k in workloads.LAYER_PROJECTIONS:
+            if name == "up":
+                continue
+            xd = workloads.draw_x_device(rows, k, 999 + rows, dev)
+            xb = _bits(xd)
+            sel = np.sort(rng.choice(n, 256, replace=False))
+            if name == "gate":
+                o = nv.nvfp4_gemv_dual_silu(mats["gate"][0], mats["up"][0], xd, out_dtype=torch.float32)
+                o16 = nv.nvfp4_gemv_dual_silu(mats["gate"][0], mats["up"][0], xd)
+                torch.cuda.synchronize()
+                d = oracle.gemv_dual_silu(mats["gate"][1], mats["up"][1], xb, sel=sel)
+                check.check_dual(o.cpu().numpy()[:, sel], _bits(o16)[:, sel], d, label="sweep gate/up r%d" % rows)
+            else:
+                y = nv.nvfp4_gemv(mats[name][0], xd, out_dtype=torch.float32)
+                y16 = nv.nvfp4_gemv(mats[name][0], xd)
+                torch.cuda.synchronize()
+                ref, absd, ref16 = oracle.gemv(*mats[name][1], xb, sel=sel)
+                check.check_gemv(y.cpu().numpy()[:, sel], _bits(y16)[:, sel], ref, absd, ref16,
+                                 label="sweep %s r%d" % (name, rows))
