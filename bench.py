@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the MI355X NVFP4 projection library.
+
+One step = the weight-only NVFP4 projections of a 64-layer 27B-class decoder
+at one row count: per layer qkv [12288x5120], o [5120x6144], the gate/up pair
+2x[17408x5120] with SiLU*mul, down [5120x17408] (whose input is the pair's
+output), 256 launches, 13,023,313,920 bytes of packed weights (E2M1 codes +
+E4M3 scales, 9/16 byte per weight).  Weights ~ N(0, 0.02^2) are drawn on the
+device from seeded generators and quantized on the device; activations are
+bf16 ~ N(0, 1).  All weights stay resident in HBM (no cache reuse between
+layers: 13 GB >> the 256 MB Infinity Cache).
+
+The headline value is the aggregate packed-weight read rate (GB/s) of the
+rows=1 step; rows 2, 4, 8 are reported alongside.  Timing: W untimed warmup
+steps, then K steps bracketed by device synchronization and HIP events on the
+launch stream.  Each step is enqueued by one nvfp4_gemv_sequence call; within
+the timed steps a HIP event pair brackets one gate/up launch per step (a
+different layer each step) for the roofline's per-launch duration.
+
+The CPU baseline times the fp64 CPU oracle on layer 0 of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 GEMV weight-read GB/s and % of HBM peak at rows=1 and rows=8"
+HBM_PEAK_GBS = 8000.0
+PAIR_NAME = "gate"
+KERNEL_SOURCES = ("bit_weight_only_nvfp4_amd/csrc/nvfp4_gemv.hip", "bit_weight_only_nvfp4_amd/csrc/nvfp4_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_pair_rows1_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def packed_weight_bytes(n: int, k: int) -> int:
+    return n * k // 2 + n * k // 16
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rows", default="1,2,4,8", help="row counts to time; the first is the headline")
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (known bytes) to scale PMC byte counters")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def build_sweep(nv, workloads, torch, dev, layers):
+    qws = torch.empty(max(nv.nvfp4_quantize_workspace_bytes(n, k) for _, n, k in workloads.LAYER_PROJECTIONS),
+                      dtype=torch.uint8, device=dev)
+    mats = []
+    for layer in range(layers):
+        lm = {}
+        for pi, (name, n, k) in enumerate(workloads.LAYER_PROJECTIONS):
+            W = workloads.draw_weights_device(n, k, workloads.sweep_seed(layer, pi), dev)
+            lm[name] = nv.nvfp4_quantize(W, workspace=qws)
+            del W
+        mats.append(lm)
+    torch.cuda.synchronize()
+    status = int(qws[:4].view(torch.int32).item())
+    if status != 0:
+        raise RuntimeError("device quantizer flagged a non-finite weight")
+    return mats
+
+
+def make_sequence(nv, torch, dev, workloads, mats, rows):
+    x5120 = workloads.draw_x_device(rows, 5120, 5_000_000 + rows, dev)
+    x6144 = workloads.draw_x_device(rows, 6144, 5_000_100 + rows, dev)
+    y_qkv = torch.empty((rows, 12288), dtype=torch.bfloat16, device=dev)
+    y_o = torch.empty((rows, 5120), dtype=torch.bfloat16, device=dev)
+    o_gu = torch.empty((rows, 17408), dtype=torch.bfloat16, device=dev)
+    y_down = torch.empty((rows, 5120), dtype=torch.bfloat16, device=dev)
+    calls = []
+    pair_index = []
+    for lm in mats:
+        calls.append((lm["qkv"], None, x5120, y_qkv))
+        calls.append((lm["o"], None, x6144, y_o))
+        pair_index.append(len(calls))
+        calls.append((lm["gate"], lm["up"], x5120, o_gu))
+        calls.append((lm["down"], None, o_gu, y_down))
+    return nv.Sequence(calls), pair_index
+
+
+def time_rows(nv, torch, seq, pair_index, ws, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        seq.launch(ws)
+    # per-step event pairs around one gate/up launch (created by a first record)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    handles = []
+    for i in range(steps):
+        h = [None] * (2 * seq.n)
+        j = pair_index[i % len(pair_index)]
+        h[2 * j] = evs[i][0].cuda_event
+        h[2 * j + 1] = evs[i][1].cuda_event
+        handles.append(h)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        seq.launch(ws, events=handles[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    pair_ms = [a.elapsed_time(b) for a, b in evs]
+    return total_ms / steps, sum(pair_ms) / len(pair_ms)
+
+
+def cpu_baseline(workloads, torch, dev, target_s):
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    q = {}
+    nbytes = 0
+    for pi, (name, n, k) in enumerate(workloads.LAYER_PROJECTIONS):
+        W = workloads.draw_weights_device(n, k, workloads.sweep_seed(0, pi), dev).cpu().numpy()
+        q[name] = oracle.quantize(W)
+        nbytes += packed_weight_bytes(n, k)
+        del W
+    rng = np.random.default_rng(0)
+    xs = {k: workloads.draw_x(rng, 1, k) for k in (5120, 6144, 17408)}
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemv(*q["qkv"], xs[5120])
+        oracle.gemv(*q["o"], xs[6144])
+        oracle.gemv_dual_silu(q["gate"], q["up"], xs[5120])
+        oracle.gemv(*q["down"], xs[17408])
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el * (passes + 1) / passes > 30.0:
+            break
+    return {
+        "value": round(nbytes * passes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "layer 0 of the decode-step sweep (qkv, o, gate/up pair with SiLU, down), rows=1, "
+                  "fp64 CPU oracle (dequantize then dot), %d pass(es) in %.1f s, %d packed bytes per pass"
+                  % (passes, el, nbytes),
+    }
+
+
+def load_traffic(bytes_per_launch):
+    """HBM bytes per launch of the gate/up pair from the committed PMC summary,
+    or None when it is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the NVFP4 projection path here has no multi-GPU mode "
+              "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_weight_only_nvfp4_amd as nv
+    import workloads
+
+    nv.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows_list = [int(r) for r in args.rows.split(",")]
+
+    t0 = time.time()
+    mats = build_sweep(nv, workloads, torch, dev, args.layers)
+    layer_bytes = sum(packed_weight_bytes(n, k) for _, n, k in workloads.LAYER_PROJECTIONS)
+    step_bytes = layer_bytes * args.layers
+    pair_bytes = 2 * packed_weight_bytes(17408, 5120)
+    log("sweep built: %d layers, %d packed weight bytes per step (%.1f s)" % (args.layers, step_bytes,
+                                                                             time.time() - t0))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 1 GiB device-to-device copy done")
+
+    seqs = {r: make_sequence(nv, torch, dev, workloads, mats, r) for r in rows_list}
+    ws = torch.zeros(max(s.workspace_bytes for s, _ in seqs.values()), dtype=torch.uint8, device=dev)
+    by_rows = {}
+    for r in rows_list:
+        seq, pidx = seqs[r]
+        ms, pair_ms = time_rows(nv, torch, seq, pidx, ws, args.steps, args.warmup)
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        by_rows[str(r)] = {
+            "ms_per_step": round(ms, 4),
+            "GB_per_s": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "gate_up_pair_us": round(pair_ms * 1e3, 3),
+            "gate_up_pair_GB_per_s": round(pair_bytes / (pair_ms * 1e-3) / 1e9, 1),
+        }
+        log("rows=%d: %.4f ms/step, %.1f GB/s (%.1f%% of 8 TB/s); gate/up pair %.2f us" % (
+            r, ms, gbs, 100 * gbs / HBM_PEAK_GBS, pair_ms * 1e3))
+
+    head = by_rows[str(rows_list[0])]
+    pair_s = head["gate_up_pair_us"] * 1e-6
+    achieved = pair_bytes / pair_s / 1e9
+    roofline = {
+        "bound": "hbm",
+        "kernel": "gemv_kernel<rows=%d, pair> (gate/up 2x[17408x5120] + SiLU*mul)" % rows_list[0],
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": load_traffic(pair_bytes),
+        "bytes_per_launch": pair_bytes,
+        "avg_launch_us": head["gate_up_pair_us"],
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on layer 0 ...")
+        cpu = cpu_baseline(workloads, torch, dev, args.cpu_seconds)
+        log("cpu baseline: %.3f GB/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    line = {
+        "metric": METRIC,
+        "value": head["GB_per_s"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded N(0,0.02^2) weights quantized to NVFP4 on the device, bf16 N(0,1) activations",
+        "config": {
+            "workload": "64-layer decode-step sweep: per layer qkv 12288x5120, o 5120x6144, gate/up pair "
+                        "2x17408x5120 + SiLU*mul, down 5120x17408; rows=%d" % rows_list[0],
+            "layers": args.layers,
+            "rows": rows_list[0],
+            "packed_weight_bytes_per_step": step_bytes,
+            "launches_per_step": 4 * args.layers,
+        },
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "by_rows": by_rows,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
   nvfp4_packed_bytes, nvfp4_pack, nvfp4_unpack, nvfp4_dequant,
   nvfp4_quantize_workspace_bytes, nvfp4_quantize,
   nvfp4_workspace_bytes, nvfp4_gemv, nvfp4_gemv_dual_silu,
+  nvfp4_sequence_workspace_bytes, nvfp4_gemv_sequence,
   nvfp4_abi_version, nvfp4_strerror, nvfp4_last_error.
 """
 from __future__ import annotations
@@ -37,7 +38,8 @@ STATUS = {
 EXPORTS = (
     "nvfp4_abi_version", "nvfp4_strerror", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
     "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
-    "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu",
+    "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
+    "nvfp4_gemv_sequence",
 )
 
 
@@ -48,6 +50,17 @@ class nvfp4_weight(ctypes.Structure):
         ("n", ctypes.c_int64),
         ("k", ctypes.c_int64),
         ("data", ctypes.c_void_p),
+    ]
+
+
+class nvfp4_call(ctypes.Structure):
+    _fields_ = [
+        ("w", ctypes.POINTER(nvfp4_weight)),
+        ("up", ctypes.POINTER(nvfp4_weight)),
+        ("x", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("rows", ctypes.c_int),
+        ("out_dtype", ctypes.c_int),
     ]
 
 
@@ -88,6 +101,9 @@ def lib() -> ctypes.CDLL:
             "nvfp4_workspace_bytes": ([i64, i64, ctypes.c_int, ctypes.c_int], sz),
             "nvfp4_gemv": ([wp, vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp], ctypes.c_int),
             "nvfp4_gemv_dual_silu": ([wp, wp, vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp], ctypes.c_int),
+            "nvfp4_sequence_workspace_bytes": ([ctypes.POINTER(nvfp4_call), ctypes.c_int], sz),
+            "nvfp4_gemv_sequence": ([ctypes.POINTER(nvfp4_call), ctypes.c_int, vp, sz,
+                                     ctypes.POINTER(ctypes.c_void_p), vp], ctypes.c_int),
         }
         for name, (argt, rest) in sig.items():
             f = getattr(L, name)
@@ -273,3 +289,56 @@ def nvfp4_gemv_dual_silu(gate: PackedWeight, up: PackedWeight, x: torch.Tensor, 
                                       _OUT[out.dtype], _ptr(workspace),
                                       0 if workspace is None else workspace.numel(), _stream(x.device)))
     return out
+
+
+class Sequence:
+    """A prepared list of projection calls (the projections of a decode step),
+    built once and enqueued with one native call each time it runs.
+
+    ``calls``: iterable of (weight, up_or_None, x, y) with x bf16 [rows, k] and y
+    [rows, n] (bf16 or fp32) device tensors; a call may take an earlier call's y
+    as its x.
+    """
+
+    def __init__(self, calls):
+        calls = list(calls)
+        self._keep = []
+        self.n = len(calls)
+        self._arr = (nvfp4_call * max(self.n, 1))()
+        for i, (w, up, x, y) in enumerate(calls):
+            if x.dtype != torch.bfloat16 or y.dtype not in _OUT:
+                raise TypeError("call %d: x must be bfloat16 and y bfloat16 or float32" % i)
+            c = self._arr[i]
+            c.w = ctypes.pointer(w.desc)
+            c.up = ctypes.pointer(up.desc) if up is not None else None
+            c.x = x.data_ptr()
+            c.y = y.data_ptr()
+            c.rows = x.shape[0]
+            c.out_dtype = _OUT[y.dtype]
+            self._keep.append((w, up, x, y))
+        self.workspace_bytes = int(lib().nvfp4_sequence_workspace_bytes(self._arr, self.n))
+
+    def launch(self, workspace: torch.Tensor | None = None, events=None, stream=None):
+        """Enqueue every call on ``stream`` (default: the current stream).
+        ``events``: None or a list of 2*n raw hipEvent_t handles (or None)."""
+        dev = self._keep[0][2].device if self._keep else torch.device("cuda")
+        if workspace is None:
+            workspace = _workspace(dev, self.workspace_bytes)
+        ev = None
+        if events is not None:
+            if len(events) != 2 * self.n:
+                raise ValueError("events must hold 2 entries per call")
+            ev = (ctypes.c_void_p * (2 * self.n))(*[e if e else None for e in events])
+        st = stream if stream is not None else _stream(dev)
+        _check("nvfp4_gemv_sequence",
+               lib().nvfp4_gemv_sequence(self._arr, self.n, _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(), ev, st))
+
+
+def nvfp4_sequence_workspace_bytes(calls) -> int:
+    return Sequence(calls).workspace_bytes
+
+
+def nvfp4_gemv_sequence(calls, workspace: torch.Tensor | None = None, events=None) -> None:
+    """One-shot form of Sequence(calls).launch(...)."""
+    Sequence(calls).launch(workspace, events)

@@ -249,4 +249,62 @@ int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls) {
+    if (!calls || ncalls < 0) return 0;
+    size_t need = 0;
+    for (int i = 0; i < ncalls; ++i) {
+        const nvfp4_call &c = calls[i];
+        if (!c.w || !valid_shape(c.w->n, c.w->k) || c.rows < 1 || c.rows > NVFP4_MAX_ROWS) continue;
+        const size_t b = nvfp4_workspace_bytes(c.w->n, c.w->k, c.rows, c.up != nullptr);
+        if (b > need) need = b;
+    }
+    return need;
+}
+
+int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
+                        void *const *events, void *stream) {
+    static const char *fn = "nvfp4_gemv_sequence";
+    if (ncalls < 0) return fail(NVFP4_E_SHAPE, "%s: ncalls=%d", fn, ncalls);
+    if (ncalls == 0) return ok();
+    if (!calls) return fail(NVFP4_E_NULL, "%s: calls is NULL", fn);
+    char name[64];
+    for (int i = 0; i < ncalls; ++i) {
+        const nvfp4_call &c = calls[i];
+        snprintf(name, sizeof name, "%s call %d", fn, i);
+        int st = check_weight(name, c.up ? "gate" : "w", c.w);
+        if (st) return st;
+        if (c.up) {
+            st = check_weight(name, "up", c.up);
+            if (st) return st;
+            if (c.up->n != c.w->n || c.up->k != c.w->k)
+                return fail(NVFP4_E_SHAPE, "%s: gate is %lldx%lld but up is %lldx%lld", name, (long long)c.w->n,
+                            (long long)c.w->k, (long long)c.up->n, (long long)c.up->k);
+        }
+        st = check_gemv_args(name, c.x, c.rows, c.y, c.out_dtype, c.w->n, c.w->k, c.up != nullptr, workspace,
+                             workspace_bytes);
+        if (st) return st;
+    }
+    int st = check_device(fn);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < ncalls; ++i) {
+        const nvfp4_call &c = calls[i];
+        if (events && events[2 * i]) {
+            hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[2 * i]), s);
+            if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: hipEventRecord before call %d: %s", fn, i,
+                                             hipGetErrorString(e));
+        }
+        const GemvPlan pl = make_gemv_plan(c.w->n, c.w->k, c.rows, c.up != nullptr);
+        hipError_t e = launch_gemv(pl, c.w->data, c.up ? c.up->data : nullptr, c.x, c.y,
+                                   c.out_dtype == NVFP4_OUT_F32, workspace, s);
+        if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: launch of call %d failed: %s", fn, i, hipGetErrorString(e));
+        if (events && events[2 * i + 1]) {
+            e = hipEventRecord(static_cast<hipEvent_t>(events[2 * i + 1]), s);
+            if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: hipEventRecord after call %d: %s", fn, i,
+                                             hipGetErrorString(e));
+        }
+    }
+    return ok();
+}
+
 }  // extern "C"

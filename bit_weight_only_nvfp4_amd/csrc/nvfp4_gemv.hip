@@ -62,8 +62,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     float *red = reinterpret_cast<float *>(smem + (size_t)ROWS * xstride * 2);
 
     // 1. activation chunks (8 bf16 each) of this workgroup's k-range; zero past k.
-    //    Issued before the weight loads so that waiting for them does not wait
-    //    for the weights (the vector memory counter drains in issue order).
+    //    Issued before the weight loads and without branches, so the wait for
+    //    them does not also wait for the weights (the vector memory counter
+    //    drains in issue order and the compiler can count exactly).
     constexpr int XMAX = (ROWS + 1) / 2;       // spp == nwaves: ROWS*32*spp / (64*nwaves)
     const int xchunks_per_row = xstride / 8;
     uint4 xr[XMAX];
@@ -72,26 +73,27 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         const int c = tid + i * nthreads;
         const int r = c / xchunks_per_row;
         const int kk = (c - r * xchunks_per_row) * 8;
-        xr[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (r < ROWS && kbase + kk < a.k)
-            xr[i] = *reinterpret_cast<const uint4 *>(a.x + (size_t)r * a.k + kbase + kk);
+        const bool in = r < ROWS && kbase + kk < a.k;
+        const size_t off = in ? (size_t)r * a.k + kbase + kk : 0;   // row 0, k 0 is always valid
+        xr[i] = *reinterpret_cast<const uint4 *>(a.x + off);
+        if (!in) xr[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 
-    // 2. this wave's super-tile of every matrix
-    const int u = u0 + wave;
-    const bool active = u < u1;
+    // 2. this wave's super-tile of every matrix.  A wave past the end of the
+    //    part (only when the part is short) re-reads the part's last super-tile,
+    //    which another wave of this workgroup is reading (an L2 hit), and
+    //    discards it; keeping the loads unconditional keeps the waits exact.
+    const bool active = u0 + wave < u1;
+    const int u = active ? u0 + wave : u1 - 1;
     uint4 wc[NMAT][kTilesPerSuper];
     uint4 wsc[NMAT];
-    if (active) {
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-            const uint8_t *base = (m == 0 ? a.w0 : a.w1) + kHeaderBytes +
-                                  ((size_t)s * a.T + u) * kSuperBytes + lane * 16;
+    for (int m = 0; m < NMAT; ++m) {
+        const uint8_t *base = (m == 0 ? a.w0 : a.w1) + kHeaderBytes + ((size_t)s * a.T + u) * kSuperBytes + lane * 16;
 #pragma unroll
-            for (int t = 0; t < kTilesPerSuper; ++t)
-                wc[m][t] = *reinterpret_cast<const uint4 *>(base + t * kChunkBytes);
-            wsc[m] = *reinterpret_cast<const uint4 *>(base + kScaleOffset);
-        }
+        for (int t = 0; t < kTilesPerSuper; ++t)
+            wc[m][t] = *reinterpret_cast<const uint4 *>(base + t * kChunkBytes);
+        wsc[m] = *reinterpret_cast<const uint4 *>(base + kScaleOffset);
     }
 
     // 3. activations to LDS
@@ -111,8 +113,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) acc[m][r] = 0.0f;
 
-    if (active) {
-        const uint16_t *xw = xs + wave * kSuperK;
+    {
+        const uint16_t *xw = xs + (u - u0) * kSuperK;
 #pragma unroll
         for (int t = 0; t < kTilesPerSuper; ++t) {
 #pragma unroll
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int r = 0; r < ROWS; ++r)
-            red[((wave * NMAT + m) * ROWS + r) * kStripN + lane] = acc[m][r];
+            red[((wave * NMAT + m) * ROWS + r) * kStripN + lane] = active ? acc[m][r] : 0.0f;
     __syncthreads();
     if (wave != 0) return;
 
@@ -173,7 +175,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 
     const int f = s * kStripN + lane;
 
-    // 6. split-K: publish this part, the last arrival sums parts 0..P-1 in order
+    // 6. split-K: publish this part, the last arrival sums parts 0..P-1 in order.
+    //    Partials and counters are touched only by device-scope atomic accesses
+    //    (sc1: performed at the device coherence point, past the per-XCD L2), so
+    //    no cache-wide writeback or invalidate is needed; the explicit wait makes
+    //    this part's stores complete before its arrival is counted, and the
+    //    reader's loads are issued only after the count returns.
     if (a.P > 1) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -181,14 +188,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
             for (int r = 0; r < ROWS; ++r)
                 __hip_atomic_store(&a.partial[(((size_t)p * NMAT + m) * ROWS + r) * a.n_pad + f], v[m][r],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __threadfence();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         unsigned last = 0;
         if (lane == 0)
-            last = __hip_atomic_fetch_add(&a.counters[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+            last = __hip_atomic_fetch_add(&a.counters[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned)(a.P - 1);
         last = __shfl(last, 0);
         if (!last) return;
-        __threadfence();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll

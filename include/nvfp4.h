@@ -157,6 +157,34 @@ int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const
                          int rows, void *y, int out_dtype, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/* One projection (up == NULL) or gate/up pair (up != NULL) of a sequence. */
+typedef struct nvfp4_call {
+    const nvfp4_weight *w;   /* the projection's weight; the gate weight of a pair */
+    const nvfp4_weight *up;  /* NULL, or the pair's up weight (same n, k as w)     */
+    const void *x;           /* device bf16 [rows][k], 16-byte aligned             */
+    void *y;                 /* device [rows][n], bf16 or fp32 per out_dtype       */
+    int rows;                /* 1..NVFP4_MAX_ROWS                                  */
+    int out_dtype;           /* NVFP4_OUT_BF16 or NVFP4_OUT_F32                    */
+} nvfp4_call;
+
+/* Workspace for nvfp4_gemv_sequence: the largest any of its calls needs. */
+size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
+
+/* Enqueue a whole decode step's projections with one host call: every call is
+ * validated first (nothing is launched if any is invalid; the message names
+ * the failing call's index), then the calls are launched in order on `stream`,
+ * each exactly as nvfp4_gemv / nvfp4_gemv_dual_silu would, sharing the one
+ * workspace (same-stream order makes that safe).  The pages drive a decode step
+ * of several hundred launches as one captured graph (kern README, "decode"
+ * programs; the NVFP4 blueprint's 755 launches per step); this is the
+ * graph-free equivalent, and it is itself capturable.  A call may read the y
+ * of an earlier call as its x.
+ * events: NULL, or 2*ncalls hipEvent_t handles (entries may be NULL);
+ * events[2i] is recorded on `stream` right before call i and events[2i+1]
+ * right after it, for per-launch device timing. */
+int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
+                        void *const *events, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(nv):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     L = ctypes.CDLL(nv.LIB_PATH)
     for name in names:
         assert hasattr(L, name), name
@@ -129,6 +129,36 @@ def test_dual_and_pack_argument_errors(nv):
     w = _weight(nv)
     assert L.nvfp4_dequant(ctypes.byref(w), FAKE + 4, None) == E["NVFP4_E_ALIGN"]
     assert L.nvfp4_unpack(ctypes.byref(w), None, FAKE, None, None) == E["NVFP4_E_NULL"]
+
+
+def test_sequence_argument_errors(nv):
+    E = {v: k for k, v in nv.STATUS.items()}
+    L = nv.lib()
+    arr = (nv.nvfp4_call * 3)()
+    good = _weight(nv, 256, 512)
+    bad = _weight(nv, 256, 512, magic=1)
+    for c in arr:
+        c.w = ctypes.pointer(good)
+        c.x, c.y, c.rows, c.out_dtype = FAKE, FAKE, 1, 0
+    assert L.nvfp4_gemv_sequence(arr, 0, None, 0, None, None) == 0       # nothing to do
+    arr[2].w = ctypes.pointer(bad)
+    assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_LAYOUT"]
+    assert "call 2" in nv.nvfp4_last_error()
+    arr[2].w = ctypes.pointer(good)
+    arr[1].rows = 9
+    assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_ROWS"]
+    assert "call 1" in nv.nvfp4_last_error()
+    arr[1].rows = 8
+    up = _weight(nv, 256, 1024)
+    arr[0].up = ctypes.pointer(up)
+    assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_SHAPE"]
+    arr[0].up = None
+    big = _weight(nv, 12288, 5120)
+    arr[1].w = ctypes.pointer(big)
+    need = L.nvfp4_sequence_workspace_bytes(arr, 3)
+    assert need == nv.nvfp4_workspace_bytes(12288, 5120, 8)
+    assert L.nvfp4_gemv_sequence(arr, 3, FAKE, need - 16, None, None) == E["NVFP4_E_WORKSPACE"]
+    assert L.nvfp4_gemv_sequence(None, 3, None, 0, None, None) == E["NVFP4_E_NULL"]
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="valid arguments would launch on a real device")

@@ -370,3 +370,50 @@ def test_sweep_layer_sampled(nv):
                 ref, absd, ref16 = oracle.gemv(*mats[name][1], xb, sel=sel)
                 check.check_gemv(y.cpu().numpy()[:, sel], _bits(y16)[:, sel], ref, absd, ref16,
                                  label="sweep %s r%d" % (name, rows))
+
+
+# ---- sequence executor -------------------------------------------------------------
+
+def test_sequence_matches_individual_calls(nv):
+    """A small decode step (qkv, o, gate/up pair, down fed by the pair) through
+    nvfp4_gemv_sequence equals the same calls made one by one, bit for bit, and
+    event handles are recorded around the requested calls."""
+    shapes = {"qkv": (384, 512), "o": (128, 768), "gate": (512, 512), "up": (512, 512), "down": (128, 512)}
+    rng = np.random.default_rng(3)
+    layers = []
+    for li in range(3):
+        lm = {}
+        for name, (n, k) in shapes.items():
+            W = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+            lm[name] = _pack(nv, oracle.quantize(W))
+        layers.append(lm)
+    for rows in (1, 3, 8):
+        x512 = _x_dev(workloads.draw_x(rng, rows, 512))
+        x768 = _x_dev(workloads.draw_x(rng, rows, 768))
+        outs = [torch.empty((rows, n), dtype=torch.bfloat16 if i % 2 else torch.float32, device="cuda")
+                for i, n in enumerate((384, 128, 512, 128))]
+        pair16 = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")   # feeds down
+        calls = []
+        for lm in layers:
+            calls += [(lm["qkv"], None, x512, outs[0]), (lm["o"], None, x768, outs[1]),
+                      (lm["gate"], lm["up"], x512, pair16), (lm["down"], None, pair16, outs[3])]
+        seq = nv.Sequence(calls)
+        ws = torch.zeros(max(seq.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for e in ev:
+            e.record()
+        handles = [None] * (2 * seq.n)
+        handles[2 * 2], handles[2 * 2 + 1] = ev[0].cuda_event, ev[1].cuda_event
+        seq.launch(ws, events=handles)
+        torch.cuda.synchronize()
+        got = [o.clone() for o in (outs[0], outs[1], pair16, outs[3])]
+        assert ev[0].elapsed_time(ev[1]) >= 0.0
+        # one by one
+        for lm in layers:
+            nv.nvfp4_gemv(lm["qkv"], x512, out=outs[0], out_dtype=outs[0].dtype, workspace=ws)
+            nv.nvfp4_gemv(lm["o"], x768, out=outs[1], out_dtype=outs[1].dtype, workspace=ws)
+            nv.nvfp4_gemv_dual_silu(lm["gate"], lm["up"], x512, out=pair16, workspace=ws)
+            nv.nvfp4_gemv(lm["down"], pair16, out=outs[3], out_dtype=outs[3].dtype, workspace=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(got, (outs[0], outs[1], pair16, outs[3])):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rows
