@@ -89,6 +89,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Row counts from which the projection uses the matrix-core variant.
+#ifndef NVFP4_MFMA_MIN_ROWS
+#define NVFP4_MFMA_MIN_ROWS 1
+#endif
+
 // ---- launchers (host side, defined in the .hip files) -----------------------
 struct GemvPlan {
     int64_t n, k;
@@ -97,6 +102,7 @@ struct GemvPlan {
     int waves;                // waves per workgroup
     int supers_per_part;      // super-tiles one workgroup covers
     int parts;                // split-K factor P
+    bool mfma;                // matrix-core (4x4x4 bf16) variant, else v_dot2
     size_t counter_bytes;     // per-strip arrival counters (0 if parts == 1)
     size_t partial_bytes;     // fp32 partial sums [P][nmat][rows][n_pad]
     size_t lds_bytes;
