@@ -35,7 +35,8 @@ if ROOT not in sys.path:
 METRIC = "NVFP4 GEMV weight-read GB/s and % of HBM peak at rows=1 and rows=8"
 HBM_PEAK_GBS = 8000.0
 PAIR_NAME = "gate"
-KERNEL_SOURCES = ("bit_weight_only_nvfp4_amd/csrc/nvfp4_gemv.hip", "bit_weight_only_nvfp4_amd/csrc/nvfp4_internal.h")
+KERNEL_SOURCES = ("bit_weight_only_nvfp4_amd/csrc/nvfp4_stream.hip", "bit_weight_only_nvfp4_amd/csrc/nvfp4_core.h",
+                  "bit_weight_only_nvfp4_amd/csrc/nvfp4_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_pair_rows1_traffic.json")
 
 

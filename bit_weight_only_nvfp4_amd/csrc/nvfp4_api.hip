@@ -90,7 +90,7 @@ int check_gemv_args(const char *fn, const void *x, int rows, const void *y, int 
     if (!aligned(x, 16)) return fail(NVFP4_E_ALIGN, "%s: x is not 16-byte aligned", fn);
     if (!aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2))
         return fail(NVFP4_E_ALIGN, "%s: y is not aligned to its element size", fn);
-    const GemvPlan pl = make_gemv_plan(n, k, rows, dual);
+    const StreamPlan pl = make_stream_plan(n, k, rows, dual);
     const size_t need = pl.counter_bytes + pl.partial_bytes;
     if (need > 0) {
         if (!workspace)
@@ -212,7 +212,7 @@ int nvfp4_quantize(const float *W, int64_t n, int64_t k, void *packed, size_t pa
 
 size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual) {
     if (!valid_shape(n, k) || rows < 1 || rows > NVFP4_MAX_ROWS) return 0;
-    const GemvPlan pl = make_gemv_plan(n, k, rows, dual != 0);
+    const StreamPlan pl = make_stream_plan(n, k, rows, dual != 0);
     return pl.counter_bytes + pl.partial_bytes;
 }
 
@@ -225,9 +225,9 @@ int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_
     if (st) return st;
     st = check_device(fn);
     if (st) return st;
-    const GemvPlan pl = make_gemv_plan(w->n, w->k, rows, 0);
-    return hip_status(fn, launch_gemv(pl, w->data, nullptr, x, y, out_dtype == NVFP4_OUT_F32, workspace,
-                                      static_cast<hipStream_t>(stream)));
+    const StreamPlan pl = make_stream_plan(w->n, w->k, rows, 0);
+    return hip_status(fn, launch_stream(pl, w->data, nullptr, x, y, out_dtype == NVFP4_OUT_F32, workspace,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const void *x, int rows, void *y,
@@ -244,9 +244,9 @@ int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const
     if (st) return st;
     st = check_device(fn);
     if (st) return st;
-    const GemvPlan pl = make_gemv_plan(gate->n, gate->k, rows, 1);
-    return hip_status(fn, launch_gemv(pl, gate->data, up->data, x, y, out_dtype == NVFP4_OUT_F32, workspace,
-                                      static_cast<hipStream_t>(stream)));
+    const StreamPlan pl = make_stream_plan(gate->n, gate->k, rows, 1);
+    return hip_status(fn, launch_stream(pl, gate->data, up->data, x, y, out_dtype == NVFP4_OUT_F32, workspace,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls) {
@@ -294,9 +294,9 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
             if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: hipEventRecord before call %d: %s", fn, i,
                                              hipGetErrorString(e));
         }
-        const GemvPlan pl = make_gemv_plan(c.w->n, c.w->k, c.rows, c.up != nullptr);
-        hipError_t e = launch_gemv(pl, c.w->data, c.up ? c.up->data : nullptr, c.x, c.y,
-                                   c.out_dtype == NVFP4_OUT_F32, workspace, s);
+        const StreamPlan pl = make_stream_plan(c.w->n, c.w->k, c.rows, c.up != nullptr);
+        hipError_t e = launch_stream(pl, c.w->data, c.up ? c.up->data : nullptr, c.x, c.y,
+                                     c.out_dtype == NVFP4_OUT_F32, workspace, s);
         if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: launch of call %d failed: %s", fn, i, hipGetErrorString(e));
         if (events && events[2 * i + 1]) {
             e = hipEventRecord(static_cast<hipEvent_t>(events[2 * i + 1]), s);

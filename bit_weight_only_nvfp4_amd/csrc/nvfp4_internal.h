@@ -37,6 +37,10 @@ constexpr int64_t kMaxN = (int64_t)1 << 20;
 constexpr int64_t kMaxStrips = kMaxN / kStripN;                 // 16384
 constexpr size_t kCounterRegionBytes = (size_t)kMaxStrips * 4;  // 64 KiB
 
+// Bytes 32..255 of the header are always zero (pack and quantize write them);
+// kernels use them as a 16-byte source of zeros.
+constexpr int kHeaderZeroOffset = 64;
+
 struct Header {
     float global_scale;
     uint32_t magic;
@@ -83,35 +87,42 @@ __device__ __forceinline__ float bf16_hi_to_f32(bf16x2_t v) {
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const uint32_t rne = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t nan = (u >> 16) | 0x40u;   // quiet NaN, sign and payload top kept
+    return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? nan : rne);   // a select, no branch
 }
 
-// Row counts from which the projection uses the matrix-core variant.
-#ifndef NVFP4_MFMA_MIN_ROWS
-#define NVFP4_MFMA_MIN_ROWS 1
+// Launch shape of the persistent streaming projection kernel.
+constexpr int kMaxWorkgroups = 256;      // one per CU on MI355X
+constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workgroup
+constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
+constexpr int kMaxWavesPerWg = 8;
+#ifndef NVFP4_STREAM_WAVES_SINGLE
+#define NVFP4_STREAM_WAVES_SINGLE 4
 #endif
+#ifndef NVFP4_STREAM_WAVES_PAIR
+#define NVFP4_STREAM_WAVES_PAIR 4
+#endif
+constexpr int kStreamWavesSingle = NVFP4_STREAM_WAVES_SINGLE;
+constexpr int kStreamWavesPair = NVFP4_STREAM_WAVES_PAIR;
 
-// ---- launchers (host side, defined in the .hip files) -----------------------
-struct GemvPlan {
+struct StreamPlan {
     int64_t n, k;
     int rows, nmat;
     int strips, supers;       // S, T
+    int G, F, R;              // workgroups, owned strips per workgroup, shared strips
     int waves;                // waves per workgroup
-    int supers_per_part;      // super-tiles one workgroup covers
-    int parts;                // split-K factor P
-    bool mfma;                // matrix-core (4x4x4 bf16) variant, else v_dot2
-    size_t counter_bytes;     // per-strip arrival counters (0 if parts == 1)
-    size_t partial_bytes;     // fp32 partial sums [P][nmat][rows][n_pad]
+    int max_pieces;           // most pieces any shared strip is cut into
+    size_t counter_bytes;     // arrival counters (0 if no strip is cut)
+    size_t partial_bytes;     // fp32 partial sums [R][max_pieces][nmat][rows][64]
     size_t lds_bytes;
 };
 
-GemvPlan make_gemv_plan(int64_t n, int64_t k, int rows, int dual);
+StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual);
+hipError_t launch_stream(const StreamPlan &plan, const void *w0, const void *w1, const void *x, void *y,
+                         int out_f32, void *workspace, hipStream_t stream);
 
-hipError_t launch_gemv(const GemvPlan &plan, const void *w0, const void *w1, const void *x,
-                       void *y, int out_f32, void *workspace, hipStream_t stream);
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
                        int64_t n, int64_t k, void *packed, hipStream_t stream);
 hipError_t launch_unpack(const void *packed, int64_t n, int64_t k, uint8_t *codes,

@@ -55,12 +55,15 @@ def test_packed_bytes(nv):
 
 
 def test_workspace_bytes(nv):
-    assert nv.nvfp4_workspace_bytes(256, 512, 1) == 0          # one part: no split-K
+    # whole strips per workgroup (short k, or enough strips to fill the GPU): no split-K
+    assert nv.nvfp4_workspace_bytes(256, 512, 1) == 0
     assert nv.nvfp4_workspace_bytes(256, 1024, 8) == 0
-    w1 = nv.nvfp4_workspace_bytes(12288, 5120, 1)
-    assert w1 > 0 and w1 == nv.nvfp4_workspace_bytes(12288, 5120, 1)
-    assert nv.nvfp4_workspace_bytes(12288, 5120, 8) > w1
-    assert nv.nvfp4_workspace_bytes(17408, 5120, 1, dual=True) > nv.nvfp4_workspace_bytes(17408, 5120, 1)
+    assert nv.nvfp4_workspace_bytes(12288, 5120, 1) == 0
+    # skinny shapes and the strips left over past 256 workgroups are cut into pieces
+    w1 = nv.nvfp4_workspace_bytes(5120, 17408, 1)
+    assert w1 > 0 and w1 == nv.nvfp4_workspace_bytes(5120, 17408, 1)
+    assert nv.nvfp4_workspace_bytes(5120, 17408, 8) > w1
+    assert nv.nvfp4_workspace_bytes(17408, 5120, 1, dual=True) > nv.nvfp4_workspace_bytes(17408, 5120, 1) > 0
     for bad in [(256, 512, 0), (256, 512, 9), (0, 512, 1), (256, 24, 1)]:
         assert nv.nvfp4_workspace_bytes(*bad) == 0
     assert nv.nvfp4_quantize_workspace_bytes(256, 512) > 0
@@ -100,8 +103,8 @@ def test_gemv_argument_errors(nv):
     assert _gemv(nv, _weight(nv), x=FAKE + 2) == E["NVFP4_E_ALIGN"]
     assert _gemv(nv, _weight(nv), y=FAKE + 1) == E["NVFP4_E_ALIGN"]
     assert _gemv(nv, _weight(nv), y=FAKE + 2, dtype=1) == E["NVFP4_E_ALIGN"]
-    big = _weight(nv, n=12288, k=5120)
-    need = nv.nvfp4_workspace_bytes(12288, 5120, 1)
+    big = _weight(nv, n=5120, k=17408)
+    need = nv.nvfp4_workspace_bytes(5120, 17408, 1)
     assert _gemv(nv, big) == E["NVFP4_E_WORKSPACE"]
     assert _gemv(nv, big, ws=FAKE, wsb=need - 1) == E["NVFP4_E_WORKSPACE"]
     assert _gemv(nv, big, ws=FAKE + 4, wsb=need) == E["NVFP4_E_ALIGN"]
@@ -153,10 +156,10 @@ def test_sequence_argument_errors(nv):
     arr[0].up = ctypes.pointer(up)
     assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_SHAPE"]
     arr[0].up = None
-    big = _weight(nv, 12288, 5120)
+    big = _weight(nv, 5120, 17408)
     arr[1].w = ctypes.pointer(big)
     need = L.nvfp4_sequence_workspace_bytes(arr, 3)
-    assert need == nv.nvfp4_workspace_bytes(12288, 5120, 8)
+    assert need == nv.nvfp4_workspace_bytes(5120, 17408, 8)
     assert L.nvfp4_gemv_sequence(arr, 3, FAKE, need - 16, None, None) == E["NVFP4_E_WORKSPACE"]
     assert L.nvfp4_gemv_sequence(None, 3, None, 0, None, None) == E["NVFP4_E_NULL"]
 
