@@ -1,11 +1,24 @@
-// nvfp4_core.h -- per-super-tile compute cores of the gfx950 NVFP4 projection.
+// nvfp4_core.h -- per-super-tile compute of the gfx950 NVFP4 projection on the
+// block-scaled matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4, fp8 x fp4).
 //
-// A wave holds one super-tile of one strip in registers: lane l owns output
-// feature 64*s + l and, per 32-k tile t, 16 bytes of E2M1 codes (two 16-element
-// groups, low nibble first) plus the 16 E4M3 scales of its feature in a 16-byte
-// scale chunk.  The activation rows of the super-tile's 256 k sit in LDS, row r
-// at xw + r * xstride.  Each core adds sum_k (code * scale) * x[r][k] into
-// acc[m][r] (fp32); s_g is applied by the caller's epilogue.
+// The E2M1 codes are the fp4 B operand exactly as stored: no per-weight
+// conversion.  One product covers 16 features x 64 k and 16 "slots" (rows of
+// A): slot 4 G + R is activation row 4 rq + R restricted to group G (16 k) of
+// the 64-k block.  Each activation value is split exactly into an fp8 E4M3
+// high part and an fp8 low part (x = hi + lo for all values within 13 binades
+// of their group's largest), both scaled by powers of two that ride in the
+// instruction's per-block E8M0 A scales.  The 128-k operand holds the block's
+// 64 codes twice: the high parts meet the first copy, the low parts the
+// second, so each slot's result is already hi + lo.  The result for slot
+// (G, R) of feature j is then a 16-element group sum, multiplied by the E4M3
+// group scale of (j, G) and accumulated in fp32.
+//
+// Operand lane layouts of the 16x16x128 product (measured on gfx950):
+//   A (fp8, 32 B per lane): lane 16 q + i holds row i, bytes 0..15 = k 16 q ..,
+//     bytes 16..31 = k 64 + 16 q ..;
+//   B (fp4, 16 B per lane): lane 16 q + n holds column n, k = 32 q .. 32 q + 31;
+//   A scale of (row i, 32-k block b): lane 16 b + i; B scale likewise;
+//   D: lane 16 q + n holds rows 4 q .. 4 q + 3 of column n.
 #pragma once
 
 #include "nvfp4_internal.h"
@@ -13,138 +26,156 @@
 namespace nvfp4 {
 namespace core {
 
-__device__ __forceinline__ uint32_t word_of(const uint4 &v, int i) {
-    switch (i & 3) {
-        case 0: return v.x;
-        case 1: return v.y;
-        case 2: return v.z;
-        default: return v.w;
-    }
-}
-
-__device__ __forceinline__ float dot2(bf16x2_t w, uint32_t xbits, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2_t, xbits), acc, false);
-}
-
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ bf16x4_t as_bf16x4(uint32_t lo, uint32_t hi) {
-    const u32x2_t v = {lo, hi};
-    return __builtin_bit_cast(bf16x4_t, v);
+// LDS image of one super-tile's activations, per wave.
+template <int ROWS>
+struct XStage {
+    static constexpr int NRQ = (ROWS + 3) / 4;             // quads of activation rows
+    static constexpr int XR = (ROWS * 32 + 63) / 64;       // 16-byte activation chunks per lane
+    // slot (kb, rq, G, R): 16 bytes hi then 16 bytes lo, 16 consecutive k
+    static constexpr int SLOT_BYTES = 4 * NRQ * 16 * 32;
+    // per slot: E8M0 exponent of the hi part | (of the lo part << 8)
+    static constexpr int EXP_OFF = SLOT_BYTES;
+    static constexpr int ZERO_OFF = EXP_OFF + 4 * NRQ * 16 * 4;   // 32 zero bytes
+    static constexpr int BYTES = ZERO_OFF + 32;
+};
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
 }
 
-// Keep each 16-element group's work in place.  Left alone, the compiler hoists
-// every group's activation reads ahead and sinks the arithmetic behind them
-// (it does so for the gate/up pair), which multiplies register pressure.  An
-// empty asm statement that takes the accumulators as in/out operands and
-// clobbers memory is a compiler-only barrier: the group's arithmetic must be
-// done before it and later LDS reads cannot move above it.  It emits no
-// instruction and no wait.
-template <int NMAT, int ROWS>
-__device__ __forceinline__ void pin_group(float (&acc)[NMAT][ROWS]) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) __asm__ volatile("" : "+v"(acc[m][r])::"memory");
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Dot-product core: per 16-element group, 8 v_dot2 (two bf16 weights x two
-// bf16 activations into fp32) per activation row, then one fma with the
-// group's E4M3 scale.  Activations are wave-uniform LDS broadcasts.
-template <int ROWS, int NMAT>
-__device__ __forceinline__ void core_dot2(const uint4 (&wc)[NMAT][kTilesPerSuper], const uint4 (&wsc)[NMAT],
-                                          const uint16_t *xw, int xstride, float (&acc)[NMAT][ROWS]) {
+// Split the super-tile's activation chunks into hi/lo fp8 parts and stage them.
+// Chunk c = lane + 64 i holds row c / 32, k = 8 (c % 32) .. + 7 of the
+// super-tile; lanes l and l ^ 1 hold the two halves of one 16-element group.
+// Group exponent: the largest |x| of the group is below 2^(E+1); the hi parts
+// are x / 2^(E-7) (below 256, inside E4M3's range) and the lo parts
+// (x - hi) / 2^(E-12) (below 256 again: |x - hi| <= 2^(E-4)).
+template <int ROWS>
+__device__ __forceinline__ void stage_x(const uint4 (&xv)[XStage<ROWS>::XR], uint8_t *xs, int lane) {
+    using S = XStage<ROWS>;
 #pragma unroll
-    for (int t = 0; t < kTilesPerSuper; ++t) {
+    for (int i = 0; i < S::XR; ++i) {
+        const int c = lane + 64 * i;
+        const int r = c >> 5, kk = (c & 31) * 8;
+        const int gt = kk >> 4, h = (kk >> 3) & 1;
+        const int slot = (((gt >> 2) * S::NRQ + (r >> 2)) * 4 + (gt & 3)) * 4 + (r & 3);
+        const uint32_t d[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        uint32_t m = pk_max_u16(pk_max_u16(d[0] & 0x7fff7fffu, d[1] & 0x7fff7fffu),
+                                pk_max_u16(d[2] & 0x7fff7fffu, d[3] & 0x7fff7fffu));
+        m = max(m & 0xffffu, m >> 16);
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+        const int ef = (int)(m >> 7);   // biased bf16 exponent of the group's largest |x|
+        const int ehi = max(ef, 8) - 7, elo = max(ef, 13) - 12;
+        const float shi = __builtin_bit_cast(float, ehi << 23), slo = __builtin_bit_cast(float, elo << 23);
+        i16x2_t hw0 = {0, 0}, hw1 = {0, 0};
+        hw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw0, __builtin_bit_cast(bf16x2_t, d[0]), shi, false);
+        hw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw0, __builtin_bit_cast(bf16x2_t, d[1]), shi, true);
+        hw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw1, __builtin_bit_cast(bf16x2_t, d[2]), shi, false);
+        hw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw1, __builtin_bit_cast(bf16x2_t, d[3]), shi, true);
+        const uint32_t h0 = __builtin_bit_cast(uint32_t, hw0), h1 = __builtin_bit_cast(uint32_t, hw1);
+        const f32x2_t back[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h0, shi, false),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h0, shi, true),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h1, shi, false),
+                                 __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h1, shi, true)};
+        float lo[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint4 xa[ROWS], xb[ROWS];
-#pragma unroll
-            for (int r = 0; r < ROWS; ++r) {
-                const uint4 *xp = reinterpret_cast<const uint4 *>(xw + r * xstride + 32 * t + 16 * h);
-                xa[r] = xp[0];
-                xb[r] = xp[1];
-            }
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                const uint32_t d0 = word_of(wc[m][t], 2 * h);
-                const uint32_t d1 = word_of(wc[m][t], 2 * h + 1);
-                const bf16x2_t w0 = e2m1x2_to_bf16x2<0>(d0), w1 = e2m1x2_to_bf16x2<1>(d0);
-                const bf16x2_t w2 = e2m1x2_to_bf16x2<2>(d0), w3 = e2m1x2_to_bf16x2<3>(d0);
-                const bf16x2_t w4 = e2m1x2_to_bf16x2<0>(d1), w5 = e2m1x2_to_bf16x2<1>(d1);
-                const bf16x2_t w6 = e2m1x2_to_bf16x2<2>(d1), w7 = e2m1x2_to_bf16x2<3>(d1);
-                const int g = 2 * t + h;
-                const float sc = e4m3_to_f32_dyn(word_of(wsc[m], g >> 2), g & 3);
-#pragma unroll
-                for (int r = 0; r < ROWS; ++r) {
-                    float part = 0.0f;
-                    part = dot2(w0, xa[r].x, part);
-                    part = dot2(w1, xa[r].y, part);
-                    part = dot2(w2, xa[r].z, part);
-                    part = dot2(w3, xa[r].w, part);
-                    part = dot2(w4, xb[r].x, part);
-                    part = dot2(w5, xb[r].y, part);
-                    part = dot2(w6, xb[r].z, part);
-                    part = dot2(w7, xb[r].w, part);
-                    acc[m][r] = __builtin_fmaf(part, sc, acc[m][r]);
-                }
-            }
-            pin_group(acc);
+        for (int q = 0; q < 4; ++q) {   // exact: x and hi share the exponent range
+            lo[2 * q] = __builtin_bit_cast(float, d[q] << 16) - back[q].x;
+            lo[2 * q + 1] = __builtin_bit_cast(float, d[q] & 0xffff0000u) - back[q].y;
         }
+        i16x2_t lw0 = {0, 0}, lw1 = {0, 0};
+        lw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw0, lo[0], lo[1], slo, false);
+        lw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw0, lo[2], lo[3], slo, true);
+        lw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw1, lo[4], lo[5], slo, false);
+        lw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw1, lo[6], lo[7], slo, true);
+        uint8_t *p = xs + slot * 32 + h * 8;
+        *reinterpret_cast<uint2 *>(p) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2 *>(p + 16) =
+            make_uint2(__builtin_bit_cast(uint32_t, lw0), __builtin_bit_cast(uint32_t, lw1));
+        *reinterpret_cast<uint32_t *>(xs + S::EXP_OFF + slot * 4) = (uint32_t)ehi | ((uint32_t)elo << 8);
     }
 }
 
-// Matrix-core: v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products.
-// Block b (lanes 4b..4b+3) takes as B the 4 weights (4 consecutive k) of the 4
-// features 4b..4b+3 -- lane l keeps feature l, as in the packed layout -- and,
-// broadcast from block 0 (cbsz 4, abid 0), A = 4 activation rows x the same 4
-// k; lane l receives D[row 0..3][feature l].  Four such products cover one
-// 16-element group; the group sum is scaled into the fp32 accumulators, so
-// each weight costs half a convert and ROWS/16 fma instead of ROWS/2 dot2.
-template <int ROWS, int NMAT>
-__device__ __forceinline__ void core_mfma(const uint4 (&wc)[NMAT][kTilesPerSuper], const uint4 (&wsc)[NMAT],
-                                          const uint16_t *xw, int xstride, int lane, float (&acc)[NMAT][ROWS]) {
-    constexpr int RB = (ROWS + 3) / 4;   // blocks of 4 activation rows
-    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+// Duplicate a 1 KB load of code chunks (c | c + 1) -- lanes 0..31 hold chunk
+// c, lanes 32..63 chunk c + 1 -- into the two matrix-core operands
+// (c | c) and (c + 1 | c + 1): the 128-k operand holds a 64-k block twice.
+__device__ __forceinline__ void dup_halves(const uint4 &v, i32x4_t &lo, i32x4_t &hi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int t = 0; t < kTilesPerSuper; ++t) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // A operands: lane i (mod 4) holds activation row 4*rb+i, 16 k of the group
-            uint4 xa[RB], xb[RB];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int row = min(4 * rb + (lane & 3), ROWS - 1);
-                const uint4 *xp = reinterpret_cast<const uint4 *>(xw + row * xstride + 32 * t + 16 * h);
-                xa[rb] = xp[0];
-                xb[rb] = xp[1];
-            }
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                const uint32_t d0 = word_of(wc[m][t], 2 * h);
-                const uint32_t d1 = word_of(wc[m][t], 2 * h + 1);
-                const bf16x4_t b0 = __builtin_shufflevector(e2m1x2_to_bf16x2<0>(d0), e2m1x2_to_bf16x2<1>(d0), 0, 1, 2, 3);
-                const bf16x4_t b1 = __builtin_shufflevector(e2m1x2_to_bf16x2<2>(d0), e2m1x2_to_bf16x2<3>(d0), 0, 1, 2, 3);
-                const bf16x4_t b2 = __builtin_shufflevector(e2m1x2_to_bf16x2<0>(d1), e2m1x2_to_bf16x2<1>(d1), 0, 1, 2, 3);
-                const bf16x4_t b3 = __builtin_shufflevector(e2m1x2_to_bf16x2<2>(d1), e2m1x2_to_bf16x2<3>(d1), 0, 1, 2, 3);
-                const int g = 2 * t + h;
-                const float sc = e4m3_to_f32_dyn(word_of(wsc[m], g >> 2), g & 3);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    f32x4_t d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_bf16x4(xa[rb].x, xa[rb].y), b0, zero, 4, 0, 0);
-                    d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_bf16x4(xa[rb].z, xa[rb].w), b1, d, 4, 0, 0);
-                    d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_bf16x4(xb[rb].x, xb[rb].y), b2, d, 4, 0, 0);
-                    d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_bf16x4(xb[rb].z, xb[rb].w), b3, d, 4, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (4 * rb + i < ROWS) acc[m][4 * rb + i] = __builtin_fmaf(d[i], sc, acc[m][4 * rb + i]);
-                }
-            }
-            pin_group(acc);
-        }
+    for (int q = 0; q < 4; ++q) {
+        const auto r = __builtin_amdgcn_permlane32_swap(w[q], w[q], false, false);
+        lo[q] = (int32_t)r[0];
+        hi[q] = (int32_t)r[1];
     }
+}
+
+// acc[fb][r] += this lane's share of one matrix's super-tile.  Lane 16 g + n
+// accumulates feature 16 fb + n over the groups 4 kb + g; the four lane groups
+// together hold the super-tile's sums.  wc[l] is the super-tile's l-th KB of
+// codes (chunks 2 l, 2 l + 1) as loaded by lane 16 g + n at 16 * lane; ws is
+// scale entry 16 g + n.
+template <int ROWS>
+__device__ __forceinline__ void core_mx(const uint4 (&wc)[kCodeChunks / 2], const uint4 &ws, const uint8_t *xs,
+                                        int lane, float (&acc)[4][ROWS]) {
+    using S = XStage<ROWS>;
+    const int g = lane >> 4, i = lane & 15, G = i >> 2, R = i & 3;
+    const bool data_lane = g == G;                         // holds slot i's parts
+    const bool hi_scale = g == (G >> 1), lo_scale = g == 2 + (G >> 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t sw = word_of(ws, kb);   // bytes fb = 0..3: scales of group 4 kb + g
+        const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+        const f32x2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, true);
+        const float sc[4] = {s01.x, s01.y, s23.x, s23.y};
+        i32x4_t b4[4];
+        dup_halves(wc[2 * kb], b4[0], b4[1]);
+        dup_halves(wc[2 * kb + 1], b4[2], b4[3]);
+#pragma unroll
+        for (int rq = 0; rq < S::NRQ; ++rq) {
+            const int slot = ((kb * S::NRQ + rq) * 4 + G) * 4 + R;
+            const i32x8_t A = *reinterpret_cast<const i32x8_t *>(xs + (data_lane ? slot * 32 : S::ZERO_OFF));
+            const uint32_t e = *reinterpret_cast<const uint32_t *>(xs + S::EXP_OFF + slot * 4);
+            const int sa = hi_scale ? (int)(e & 0xff) : lo_scale ? (int)((e >> 8) & 0xff) : 127;
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+                const i32x8_t B = __builtin_shufflevector(b4[fb], b4[fb], 0, 1, 2, 3, -1, -1, -1, -1);
+                const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                // A: fp8 E4M3 (format 0), B: fp4 E2M1 (format 4), B scale 2^0
+                const f32x4_t D = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, 127);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (4 * rq + v < ROWS) acc[fb][4 * rq + v] = __builtin_fmaf(D[v], sc[fb], acc[fb][4 * rq + v]);
+            }
+        }
+        // one k block at a time: bounds the products in flight (registers)
+        if (ROWS > 4) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Sum over the four lane groups; lane 16 g + n returns the total of feature
+// 16 g + n (the strip's features in lane order).
+__device__ __forceinline__ float strip_total(const float (&a)[4], int lane) {
+    float t[4];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+        float v = a[fb];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        t[fb] = v;
+    }
+    const int g = lane >> 4;
+    return g == 0 ? t[0] : g == 1 ? t[1] : g == 2 ? t[2] : t[3];
 }
 
 }  // namespace core

@@ -17,15 +17,32 @@
 
 namespace nvfp4 {
 
-// ---- packed layout (version 1) -------------------------------------------
+// ---- packed layout (version 2) -------------------------------------------
+// A super-tile (strip s of 64 features, k from 256 u) is an array of 16-byte
+// entries: 16 code chunks of 32 entries (chunk c = 4 kb + fb, entry 16 h + j:
+// codes of feature 16 fb + j, k = 64 kb + 32 h .. + 31 of the super-tile),
+// then 64 scale entries (entry 16 g + j, byte 4 kb + fb: scale of feature
+// 16 fb + j, group 4 kb + g of the super-tile).
 constexpr int kHeaderBytes = 256;
-constexpr int kStripN = 64;        // output features per strip = lanes of a wave
+constexpr int kStripN = 64;        // output features per strip
 constexpr int kSuperK = 256;       // k per super-tile
-constexpr int kTileK = 32;         // k per 16-byte code chunk (one lane)
-constexpr int kTilesPerSuper = kSuperK / kTileK;          // 8
-constexpr int kChunkBytes = 16 * kStripN;                  // 1024: one wave load
-constexpr int kScaleOffset = kTilesPerSuper * kChunkBytes; // 8192
-constexpr int kSuperBytes = kScaleOffset + kChunkBytes;    // 9216
+constexpr int kFeatureBlock = 16;  // features per matrix-core product
+constexpr int kKBlock = 64;        // k per matrix-core product
+constexpr int kCodeChunks = (kStripN / kFeatureBlock) * (kSuperK / kKBlock);   // 16
+constexpr int kCodeChunkBytes = kFeatureBlock * kKBlock / 2;                    // 512
+constexpr int kScaleOffset = kCodeChunks * kCodeChunkBytes;                     // 8192
+constexpr int kSuperBytes = kScaleOffset + 16 * kStripN;                        // 9216
+constexpr int kEntriesPerSuper = kSuperBytes / 16;                              // 576
+
+// Byte offset, within a super-tile, of the code entry holding feature f (0..63
+// in the strip) and k = kr .. kr + 31 (kr a multiple of 32 below 256).
+__host__ __device__ inline int code_entry_offset(int f, int kr) {
+    return ((kr >> 6) * 4 + (f >> 4)) * kCodeChunkBytes + ((((kr >> 5) & 1) << 4) + (f & 15)) * 16;
+}
+// Byte offset, within a super-tile, of the scale of feature f, group gt (0..15).
+__host__ __device__ inline int scale_byte_offset(int f, int gt) {
+    return kScaleOffset + (((gt & 3) << 4) + (f & 15)) * 16 + (gt >> 2) * 4 + (f >> 4);
+}
 
 // Split-K arrival counters live in a fixed region at the front of every
 // projection workspace, one per strip, for up to kMaxStrips strips (n <= 2^20).
@@ -98,11 +115,16 @@ constexpr int kMaxWorkgroups = 256;      // one per CU on MI355X
 constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workgroup
 constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
 constexpr int kMaxWavesPerWg = 8;
+// Up to 4 activation rows a wave needs at most 256 registers, so two waves
+// share each SIMD (8 per workgroup) and hide each other's latencies; more rows
+// need up to 512 registers: one wave per SIMD.
+constexpr int kWideRowsMax = 4;
+__host__ __device__ constexpr int max_waves_for_rows(int rows) { return rows <= kWideRowsMax ? 8 : 4; }
 #ifndef NVFP4_STREAM_WAVES_SINGLE
-#define NVFP4_STREAM_WAVES_SINGLE 4
+#define NVFP4_STREAM_WAVES_SINGLE 8
 #endif
 #ifndef NVFP4_STREAM_WAVES_PAIR
-#define NVFP4_STREAM_WAVES_PAIR 4
+#define NVFP4_STREAM_WAVES_PAIR 8
 #endif
 constexpr int kStreamWavesSingle = NVFP4_STREAM_WAVES_SINGLE;
 constexpr int kStreamWavesPair = NVFP4_STREAM_WAVES_PAIR;

@@ -12,7 +12,6 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kChunksPerSuper = kTilesPerSuper + 1;   // 8 code chunks + 1 scale chunk
 
 // the whole 256-byte header: fields in the first 32 bytes, zeros after
 __device__ void write_header(void *packed, float global_scale, int64_t n, int64_t k) {
@@ -23,7 +22,38 @@ __device__ void write_header(void *packed, float global_scale, int64_t n, int64_
     for (int i = 2; i < kHeaderBytes / 16; ++i) h[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// one thread per 16-byte chunk of the packed body
+// Feature (in the strip), first k (in the super-tile) and kind of entry e of
+// a super-tile: code entries e < 512, scale entries after.
+struct Entry {
+    bool code;
+    int f;    // code entry: its feature; scale entry: feature of byte 0 (fb = 0)
+    int kr;   // code entry: first k; scale entry: group g (0..3) of its bytes
+};
+__device__ __forceinline__ Entry entry_of(int e) {
+    Entry d;
+    d.code = e < kCodeChunks * 32;
+    if (d.code) {
+        const int c = e >> 5, le = e & 31;
+        d.f = (c & 3) * 16 + (le & 15);
+        d.kr = (c >> 2) * kKBlock + (le >> 4) * 32;
+    } else {
+        const int l = e - kCodeChunks * 32;
+        d.f = l & 15;
+        d.kr = l >> 4;
+    }
+    return d;
+}
+
+__device__ __forceinline__ uint4 pack16(const uint8_t (&b)[16]) {
+    uint4 o;
+    o.x = b[0] | (b[1] << 8) | (b[2] << 16) | ((uint32_t)b[3] << 24);
+    o.y = b[4] | (b[5] << 8) | (b[6] << 16) | ((uint32_t)b[7] << 24);
+    o.z = b[8] | (b[9] << 8) | (b[10] << 16) | ((uint32_t)b[11] << 24);
+    o.w = b[12] | (b[13] << 8) | (b[14] << 16) | ((uint32_t)b[15] << 24);
+    return o;
+}
+
+// one thread per 16-byte entry of the packed body
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ codes,
                                                    const uint8_t *__restrict__ scales, float global_scale,
                                                    int64_t n, int64_t k, int64_t T, int64_t total,
@@ -31,33 +61,28 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id == 0) write_header(packed, global_scale, n, k);
     if (id >= total) return;
-    const int64_t st = id / (kChunksPerSuper * kStripN);
-    const int rem = (int)(id - st * (kChunksPerSuper * kStripN));
-    const int c = rem / kStripN, lane = rem % kStripN;
+    const int64_t st = id / kEntriesPerSuper;
+    const int e = (int)(id - st * kEntriesPerSuper);
     const int64_t s = st / T, u = st % T;
-    const int64_t f = s * kStripN + lane;
+    const Entry d = entry_of(e);
     uint8_t b[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) b[i] = 0;
-    if (f < n) {
-        if (c < kTilesPerSuper) {
-            const int64_t k0 = u * kSuperK + c * kTileK;
+    if (d.code) {
+        const int64_t f = s * kStripN + d.f, k0 = u * kSuperK + d.kr;
+        if (f < n) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (k0 + 2 * i < k) b[i] = codes[f * (k / 2) + k0 / 2 + i];
-        } else {
-            const int64_t g0 = u * (kSuperK / 16);
+        }
+    } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (g0 + i < k / 16) b[i] = scales[f * (k / 16) + g0 + i];
+        for (int i = 0; i < 16; ++i) {   // byte 4 kb + fb
+            const int64_t f = s * kStripN + (i & 3) * 16 + d.f, gi = u * (kSuperK / 16) + (i >> 2) * 4 + d.kr;
+            if (f < n && gi < k / 16) b[i] = scales[f * (k / 16) + gi];
         }
     }
-    uint4 o;
-    o.x = b[0] | (b[1] << 8) | (b[2] << 16) | ((uint32_t)b[3] << 24);
-    o.y = b[4] | (b[5] << 8) | (b[6] << 16) | ((uint32_t)b[7] << 24);
-    o.z = b[8] | (b[9] << 8) | (b[10] << 16) | ((uint32_t)b[11] << 24);
-    o.w = b[12] | (b[13] << 8) | (b[14] << 16) | ((uint32_t)b[15] << 24);
-    *reinterpret_cast<uint4 *>(packed + kHeaderBytes + st * kSuperBytes + c * kChunkBytes + lane * 16) = o;
+    *reinterpret_cast<uint4 *>(packed + kHeaderBytes + st * kSuperBytes + e * 16) = pack16(b);
 }
 
 __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__ packed, int64_t n, int64_t k,
@@ -66,60 +91,57 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id == 0 && global_scale) *global_scale = reinterpret_cast<const Header *>(packed)->global_scale;
     if (id >= total) return;
-    const int64_t st = id / (kChunksPerSuper * kStripN);
-    const int rem = (int)(id - st * (kChunksPerSuper * kStripN));
-    const int c = rem / kStripN, lane = rem % kStripN;
+    const int64_t st = id / kEntriesPerSuper;
+    const int e = (int)(id - st * kEntriesPerSuper);
     const int64_t s = st / T, u = st % T;
-    const int64_t f = s * kStripN + lane;
-    if (f >= n) return;
-    const uint4 o = *reinterpret_cast<const uint4 *>(packed + kHeaderBytes + st * kSuperBytes +
-                                                     c * kChunkBytes + lane * 16);
+    const Entry d = entry_of(e);
+    const uint4 o = *reinterpret_cast<const uint4 *>(packed + kHeaderBytes + st * kSuperBytes + e * 16);
     const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-    if (c < kTilesPerSuper) {
-        const int64_t k0 = u * kSuperK + c * kTileK;
+    if (d.code) {
+        const int64_t f = s * kStripN + d.f, k0 = u * kSuperK + d.kr;
+        if (f >= n) return;
         for (int i = 0; i < 16; ++i)
             if (k0 + 2 * i < k) codes[f * (k / 2) + k0 / 2 + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
     } else {
-        const int64_t g0 = u * (kSuperK / 16);
-        for (int i = 0; i < 16; ++i)
-            if (g0 + i < k / 16) scales[f * (k / 16) + g0 + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        for (int i = 0; i < 16; ++i) {
+            const int64_t f = s * kStripN + (i & 3) * 16 + d.f, gi = u * (kSuperK / 16) + (i >> 2) * 4 + d.kr;
+            if (f < n && gi < k / 16) scales[f * (k / 16) + gi] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        }
     }
 }
 
-// one thread per code chunk: 32 weights of one feature
+// one thread per code entry: 32 weights of one feature
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ packed, int64_t n, int64_t k,
                                                       int64_t T, int64_t total, float *__restrict__ out) {
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= total) return;
-    const int64_t st = id / (kTilesPerSuper * kStripN);
-    const int rem = (int)(id - st * (kTilesPerSuper * kStripN));
-    const int t = rem / kStripN, lane = rem % kStripN;
+    const int64_t st = id / (kCodeChunks * 32);
+    const int e = (int)(id - st * (kCodeChunks * 32));
     const int64_t s = st / T, u = st % T;
-    const int64_t f = s * kStripN + lane;
+    const Entry d = entry_of(e);
+    const int64_t f = s * kStripN + d.f;
     if (f >= n) return;
     const uint8_t *sup = packed + kHeaderBytes + st * kSuperBytes;
-    const uint4 cw = *reinterpret_cast<const uint4 *>(sup + t * kChunkBytes + lane * 16);
-    const uint4 sw = *reinterpret_cast<const uint4 *>(sup + kScaleOffset + lane * 16);
+    const uint4 cw = *reinterpret_cast<const uint4 *>(sup + e * 16);
     const float sg = reinterpret_cast<const Header *>(packed)->global_scale;
     const uint32_t cwv[4] = {cw.x, cw.y, cw.z, cw.w};
-    const uint32_t swv[4] = {sw.x, sw.y, sw.z, sw.w};
-    const int64_t k0 = u * kSuperK + t * kTileK;
+    const int64_t k0 = u * kSuperK + d.kr;
     float *dst = out + f * k + k0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (k0 + 16 * h >= k) break;
-        const int g = 2 * t + h;
-        const float sc = e4m3_to_f32_dyn(swv[g >> 2], g & 3);
+        const uint32_t sbyte = sup[scale_byte_offset(d.f, (d.kr >> 4) + h)];
+        const float sc = e4m3_to_f32_dyn(sbyte, 0);
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const uint32_t word = cwv[2 * h + d];
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t word = cwv[2 * h + q];
             const bf16x2_t p[4] = {e2m1x2_to_bf16x2<0>(word), e2m1x2_to_bf16x2<1>(word),
                                    e2m1x2_to_bf16x2<2>(word), e2m1x2_to_bf16x2<3>(word)};
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 // code*scale is exact (<= 6 significant bits); one rounding for * s_g
-                dst[16 * h + 8 * d + 2 * b] = (bf16_lo_to_f32(p[b]) * sc) * sg;
-                dst[16 * h + 8 * d + 2 * b + 1] = (bf16_hi_to_f32(p[b]) * sc) * sg;
+                dst[16 * h + 8 * q + 2 * b] = (bf16_lo_to_f32(p[b]) * sc) * sg;
+                dst[16 * h + 8 * q + 2 * b + 1] = (bf16_hi_to_f32(p[b]) * sc) * sg;
             }
         }
     }
@@ -235,11 +257,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
             for (int j = 0; j < 8; ++j) hi |= e2m1_encode_rne_sat(w[8 + j] / S) << (4 * j);
         }
     }
-    const int64_t s = f / kStripN, lane = f % kStripN;
+    const int64_t s = f / kStripN, fs = f % kStripN;
     const int64_t u = g / (kSuperK / 16), q = g % (kSuperK / 16);
     uint8_t *sup = packed + kHeaderBytes + (s * T + u) * kSuperBytes;
-    *reinterpret_cast<uint2 *>(sup + (q >> 1) * kChunkBytes + lane * 16 + (q & 1) * 8) = make_uint2(lo, hi);
-    sup[kScaleOffset + lane * 16 + q] = (uint8_t)e;
+    *reinterpret_cast<uint2 *>(sup + code_entry_offset((int)fs, (int)(q * 16) & ~31) + (q & 1) * 8) = make_uint2(lo, hi);
+    sup[scale_byte_offset((int)fs, (int)q)] = (uint8_t)e;
 }
 
 inline unsigned grid_for(int64_t total, int block) { return (unsigned)ceil_div(total, block); }
@@ -249,7 +271,7 @@ inline unsigned grid_for(int64_t total, int block) { return (unsigned)ceil_div(t
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global_scale, int64_t n, int64_t k,
                        void *packed, hipStream_t stream) {
     const int64_t T = num_supers(k);
-    const int64_t total = num_strips(n) * T * kChunksPerSuper * kStripN;
+    const int64_t total = num_strips(n) * T * kEntriesPerSuper;
     hipLaunchKernelGGL(pack_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, codes, scales,
                        global_scale, n, k, T, total, static_cast<uint8_t *>(packed));
     return hipGetLastError();
@@ -258,7 +280,7 @@ hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global
 hipError_t launch_unpack(const void *packed, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales,
                          float *global_scale, hipStream_t stream) {
     const int64_t T = num_supers(k);
-    const int64_t total = num_strips(n) * T * kChunksPerSuper * kStripN;
+    const int64_t total = num_strips(n) * T * kEntriesPerSuper;
     hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
                        static_cast<const uint8_t *>(packed), n, k, T, total, codes, scales, global_scale);
     return hipGetLastError();
@@ -266,7 +288,7 @@ hipError_t launch_unpack(const void *packed, int64_t n, int64_t k, uint8_t *code
 
 hipError_t launch_dequant(const void *packed, int64_t n, int64_t k, float *out, hipStream_t stream) {
     const int64_t T = num_supers(k);
-    const int64_t total = num_strips(n) * T * kTilesPerSuper * kStripN;
+    const int64_t total = num_strips(n) * T * kCodeChunks * 32;
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
                        static_cast<const uint8_t *>(packed), n, k, T, total, out);
     return hipGetLastError();

@@ -27,6 +27,7 @@
 // strips form R*T shared units split into G contiguous ranges
 // [g*RT/G, (g+1)*RT/G), cut at strip boundaries into pieces.
 #include <atomic>
+#include <type_traits>
 
 #include "nvfp4_core.h"
 
@@ -62,64 +63,50 @@ __device__ __forceinline__ uint4 load_nt(const uint8_t *p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-// One super-tile's registers: codes and scales of every matrix plus this lane's
-// chunks of the activation window.
-template <int ROWS, int NMAT>
+// One super-tile of one matrix in registers: its 8 KB of codes as 8 wave-wide
+// 1 KB loads (lane l: bytes 16 l of each KB), the scale entry of the lane and
+// this lane's chunks of the activation window.
+template <int ROWS>
 struct Tile {
-    static constexpr int XR = (ROWS * 32 + 63) / 64;   // 16-byte x chunks per lane
-    uint4 wc[NMAT][kTilesPerSuper];
-    uint4 ws[NMAT];
+    static constexpr int XR = core::XStage<ROWS>::XR;
+    uint4 wc[kCodeChunks / 2];
+    uint4 ws;
     uint4 xv[XR];
 };
 
-// Issue the loads of super-tile u of strip s.  With real == false the same
-// loads read an always-valid location (the first super-tile of the weight and
-// the first row of x), so the number of loads in flight never depends on
-// control flow and the compiler can count them exactly; those results are
-// never used and the location stays cache-resident.
-template <int ROWS, int NMAT>
-__device__ __forceinline__ void load_tile(const StreamArgs &a, int s, int u, bool real, int lane,
-                                          Tile<ROWS, NMAT> &b) {
+// Issue the loads of super-tile u of strip s of matrix w (with its activation
+// window when WITH_X).  With real == false the same loads read an always-valid
+// location (the weight's first super-tile, the header's zero bytes), so the
+// number of loads in flight never depends on control flow and the compiler can
+// count them exactly; those results are never used.
+template <int ROWS, bool WITH_X>
+__device__ __forceinline__ void load_tile(const StreamArgs &a, const uint8_t *w, int s, int u, bool real,
+                                          int lane, Tile<ROWS> &b) {
     const size_t off = real ? ((size_t)s * a.T + u) * kSuperBytes : 0;
+    const uint8_t *base = w + kHeaderBytes + off;
+    // the activation window first: it is consumed first (staged into LDS)
+    // and, issued first, it can be waited for while the codes are in flight
+    if (WITH_X) {
+        const int kbase = u * kSuperK;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-        const uint8_t *base = (m == 0 ? a.w0 : a.w1) + kHeaderBytes + off + lane * 16;
-#pragma unroll
-        for (int t = 0; t < kTilesPerSuper; ++t)
-            b.wc[m][t] = load_nt(base + t * kChunkBytes);
-        b.ws[m] = load_nt(base + kScaleOffset);
+        for (int i = 0; i < Tile<ROWS>::XR; ++i) {
+            const int c = lane + 64 * i;
+            const int r = c >> 5, kk = (c & 31) * 8;
+            const bool in = real && r < ROWS && kbase + kk < a.k;
+            // chunks past the activations read 16 zero bytes from the packed
+            // header's padding instead: always issued, never masked afterwards
+            // (both addresses are formed, then one is selected: no branch)
+            const uint8_t *xp = reinterpret_cast<const uint8_t *>(a.x + (size_t)min(r, ROWS - 1) * a.k + kbase + kk);
+            const uint8_t *src = in ? xp : a.w0 + kHeaderZeroOffset;
+            b.xv[i] = *reinterpret_cast<const uint4 *>(src);
+        }
     }
-    const int kbase = u * kSuperK;
 #pragma unroll
-    for (int i = 0; i < Tile<ROWS, NMAT>::XR; ++i) {
-        const int c = lane + 64 * i;
-        const int r = c >> 5, kk = (c & 31) * 8;
-        const bool in = real && r < ROWS && kbase + kk < a.k;
-        // chunks past the activations read 16 zero bytes from the packed
-        // header's padding instead: always issued, never masked afterwards
-        // (both addresses are formed, then one is selected: no branch)
-        const uint8_t *xp = reinterpret_cast<const uint8_t *>(a.x + (size_t)min(r, ROWS - 1) * a.k + kbase + kk);
-        const uint8_t *src = in ? xp : a.w0 + kHeaderZeroOffset;
-        b.xv[i] = *reinterpret_cast<const uint4 *>(src);
-    }
+    for (int l = 0; l < kCodeChunks / 2; ++l) b.wc[l] = load_nt(base + l * 2 * kCodeChunkBytes + lane * 16);
+    b.ws = load_nt(base + kScaleOffset + lane * 16);
     // keep the whole tile's loads ahead of what follows (the scheduler would
     // otherwise sink them into the previous tile's arithmetic, after its wait)
     __builtin_amdgcn_sched_barrier(0);
-}
-
-// Stage the activation window of a loaded tile in the wave's LDS buffer
-// ([ROWS + 1][256] bf16; lanes past the last row write the spare row) and
-// accumulate the tile.
-template <int ROWS, int NMAT>
-__device__ __forceinline__ void consume_tile(const Tile<ROWS, NMAT> &b, uint16_t *xw, int lane,
-                                             float (&acc)[NMAT][ROWS]) {
-#pragma unroll
-    for (int i = 0; i < Tile<ROWS, NMAT>::XR; ++i) {
-        const int c = lane + 64 * i;
-        const int r = min(c >> 5, ROWS), kk = (c & 31) * 8;
-        *reinterpret_cast<uint4 *>(xw + r * kSuperK + kk) = b.xv[i];
-    }
-    core_mfma<ROWS, NMAT>(b.wc, b.ws, xw, kSuperK, lane, acc);
 }
 
 // Buffer resource over the outputs: stores at an offset past its size are
@@ -241,15 +228,17 @@ __device__ __forceinline__ Cursor cursor_at(const StreamArgs &a, const Geometry 
 template <int ROWS, int NMAT>
 __device__ __forceinline__ void finish_segment(const StreamArgs &a, const Geometry &q, int k, float *red,
                                                const float (&sg)[NMAT], __amdgpu_buffer_rsrc_t yr,
-                                               int wave, int nwaves, int lane, float (&acc)[NMAT][ROWS],
+                                               int wave, int nwaves, int lane, float (&acc)[NMAT][4][ROWS],
                                                int (&pub)[2]) {
     __syncthreads();   // the previous segment's reads of `red` are done
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            red[((wave * NMAT + m) * ROWS + r) * kStripN + lane] = acc[m][r];
-            acc[m][r] = 0.0f;
+            const float a4[4] = {acc[m][0][r], acc[m][1][r], acc[m][2][r], acc[m][3][r]};
+            red[((wave * NMAT + m) * ROWS + r) * kStripN + lane] = core::strip_total(a4, lane);
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) acc[m][fb][r] = 0.0f;
         }
     __syncthreads();
 #pragma unroll
@@ -330,7 +319,7 @@ __device__ __forceinline__ void final_sum(const StreamArgs &a, int sh, int np, f
 }
 
 template <int ROWS, int NMAT>
-__global__ __launch_bounds__(kMaxWavesPerWg * 64) void stream_kernel(StreamArgs a) {
+__global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void stream_kernel(StreamArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ unsigned s_last[2];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -338,9 +327,11 @@ __global__ __launch_bounds__(kMaxWavesPerWg * 64) void stream_kernel(StreamArgs 
     // branch below on the scalar unit (no exec-masked control flow around loads)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nwaves = blockDim.x >> 6;
-    uint16_t *xbuf = reinterpret_cast<uint16_t *>(smem) + (size_t)wave * 2 * (ROWS + 1) * kSuperK;
-    uint16_t *x0 = xbuf, *x1 = xbuf + (ROWS + 1) * kSuperK;
-    float *red = reinterpret_cast<float *>(smem + (size_t)nwaves * 2 * (ROWS + 1) * kSuperK * 2);
+    using XS = core::XStage<ROWS>;
+    static_assert(XS::BYTES == 2304 * ((ROWS + 3) / 4) + 32, "host LDS sizing assumes this staging size");
+    uint8_t *xs = smem + (size_t)wave * XS::BYTES;   // this wave's staged activations
+    float *red = reinterpret_cast<float *>(smem + (size_t)nwaves * XS::BYTES);
+    if (lane < 8) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
     const Geometry q = make_geometry(a);
     // tensor scales, loaded before any tile so that no later wait is for them
     float sg[NMAT];
@@ -352,21 +343,23 @@ __global__ __launch_bounds__(kMaxWavesPerWg * 64) void stream_kernel(StreamArgs 
     // through all its segments, two deep: the loads of the next super-tile are
     // in flight while one is computed and while a segment is closed.
     const int nw = wave < q.total ? (q.total - wave + nwaves - 1) / nwaves : 0;
-    float acc[NMAT][ROWS];
+    float acc[NMAT][4][ROWS];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) acc[m][r] = 0.0f;
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) acc[m][fb][r] = 0.0f;
     int pub[2] = {0, 0};   // pieces of shared strips fs, fs + 1 stored here
     Cursor lc, cc;   // load cursor (runs ahead) and the segment being accumulated
     lc = cursor_at(a, q, 0);
     cc = lc;
-    Tile<ROWS, NMAT> b0, b1;
-    // issue the loads of position i (dummy loads past the wave's last tile)
-    auto load_pos = [&](int i, bool real, Tile<ROWS, NMAT> &b) {
+    Tile<ROWS> b0, b1;
+    // issue the loads of matrix w at position i (dummy loads past the wave's last tile)
+    auto load_pos = [&](const uint8_t *w, int i, bool real, Tile<ROWS> &b, auto with_x) {
         if (real)
             while (i >= lc.end) lc = cursor_at(a, q, lc.k + 1);
-        load_tile<ROWS, NMAT>(a, lc.strip, lc.u0 + (i - lc.start), real, lane, b);
+        load_tile<ROWS, decltype(with_x)::value>(a, w, lc.strip, lc.u0 + (i - lc.start), real, lane, b);
     };
     // close every segment that ends before position i
     auto close_before = [&](int i) {
@@ -375,25 +368,47 @@ __global__ __launch_bounds__(kMaxWavesPerWg * 64) void stream_kernel(StreamArgs 
             cc = cursor_at(a, q, cc.k + 1);
         }
     };
-    // The wave's tile count is padded to even with one dummy tile whose scales
-    // are zeroed, so both tiles of every iteration are consumed and the loop
-    // has one exit: on the way back to its head the only loads in flight are
-    // those of the next tile, and no wait is needed before reusing registers.
-    if (nw > 0) {
-        load_pos(wave, true, b0);
-        for (int j = 0; j < nw; j += 2) {
-            const int i0 = wave + j * nwaves, i1 = i0 + nwaves;
-            const bool r1 = j + 1 < nw, r2 = j + 2 < nw;
-            load_pos(i1, r1, b1);
-            close_before(i0);
-            consume_tile<ROWS, NMAT>(b0, x0, lane, acc);
-            load_pos(i1 + nwaves, r2, b0);
-            if (!r1) {
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m) b1.ws[m] = make_uint4(0, 0, 0, 0);
+    using WithX = std::true_type;
+    using NoX = std::false_type;
+    if (NMAT == 1) {
+        // Two positions per iteration.  A tile's activations are staged into
+        // LDS (their registers freed) before the next tile's loads are issued;
+        // its codes are consumed after.  The wave's tile count is padded to
+        // even with one dummy tile whose scales are zeroed, so both tiles of
+        // every iteration are consumed and the loop has one exit: on the way
+        // back to its head the only loads in flight are those of the next
+        // tile, and no wait is needed before reusing registers.
+        if (nw > 0) {
+            load_pos(a.w0, wave, true, b0, WithX{});
+            for (int j = 0; j < nw; j += 2) {
+                const int i0 = wave + j * nwaves, i1 = i0 + nwaves;
+                const bool r1 = j + 1 < nw, r2 = j + 2 < nw;
+                core::stage_x<ROWS>(b0.xv, xs, lane);
+                load_pos(a.w0, i1, r1, b1, WithX{});
+                close_before(i0);
+                core::core_mx<ROWS>(b0.wc, b0.ws, xs, lane, acc[0]);
+                core::stage_x<ROWS>(b1.xv, xs, lane);
+                load_pos(a.w0, i1 + nwaves, r2, b0, WithX{});
+                if (!r1) b1.ws = make_uint4(0, 0, 0, 0);
+                close_before(i1);   // past the last tile this closes every segment left
+                core::core_mx<ROWS>(b1.wc, b1.ws, xs, lane, acc[0]);
             }
-            close_before(i1);   // past the last tile this closes every segment left
-            consume_tile<ROWS, NMAT>(b1, x1, lane, acc);
+        }
+    } else {
+        // One position per iteration: the gate super-tile (with the activation
+        // window, staged once) then the up super-tile of the same position,
+        // each in flight while the other is computed.
+        if (nw > 0) {
+            load_pos(a.w0, wave, true, b0, WithX{});
+            for (int j = 0; j < nw; ++j) {
+                const int i0 = wave + j * nwaves;
+                core::stage_x<ROWS>(b0.xv, xs, lane);
+                load_pos(a.w1, i0, true, b1, NoX{});
+                close_before(i0);
+                core::core_mx<ROWS>(b0.wc, b0.ws, xs, lane, acc[0]);
+                load_pos(a.w0, i0 + nwaves, j + 1 < nw, b0, WithX{});
+                core::core_mx<ROWS>(b1.wc, b1.ws, xs, lane, acc[NMAT - 1]);
+            }
         }
     }
     while (cc.k < q.nseg) {
@@ -479,6 +494,7 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
     // for the pair) -- enough to cover the memory latency at full bandwidth,
     // and few enough that the first tiles arrive early.
     int waves = pl.nmat == 1 ? kStreamWavesSingle : kStreamWavesPair;
+    if (waves > max_waves_for_rows(rows)) waves = max_waves_for_rows(rows);
     const long long per_wg = pl.F * (long long)T + (pl.R ? ((long long)pl.R * T + pl.G - 1) / pl.G : 0);
     if (waves > per_wg) waves = (int)per_wg;
     if (waves < 1) waves = 1;
@@ -495,7 +511,7 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
         pl.counter_bytes = kCounterRegionBytes;
         pl.partial_bytes = (size_t)pl.R * pl.max_pieces * pl.nmat * rows * kStripN * sizeof(float);
     }
-    const size_t lds_x = (size_t)pl.waves * 2 * (rows + 1) * kSuperK * 2;
+    const size_t lds_x = (size_t)pl.waves * (2304 * ((rows + 3) / 4) + 32);   // core::XStage<rows>::BYTES
     const size_t lds_red = (size_t)pl.waves * pl.nmat * rows * kStripN * sizeof(float);
     // at least ~81 KB so that no CU ever holds two of these workgroups
     pl.lds_bytes = lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;

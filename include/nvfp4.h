@@ -36,11 +36,16 @@
  *
  * Packed (device-tiled) weight, produced by nvfp4_pack / nvfp4_quantize:
  *   [256-byte header][strip 0: super-tiles 0..T-1][strip 1 ...] ...
- *   strip = 64 output features, super-tile = 64 features x 256 k = 9216 bytes:
- *   8 code chunks of 1024 bytes (chunk t, lane l: 16 bytes = codes of feature
- *   64*s+l for k = 256*u + 32*t .. +31, canonical nibble order) followed by a
- *   1024-byte scale chunk (lane l: 16 bytes = the 16 group scales of feature
- *   64*s+l in the super-tile).  Features >= n and k >= k are zero padding.
+ *   strip = 64 output features, super-tile = 64 features x 256 k = 9216 bytes,
+ *   an array of 576 entries of 16 bytes (layout version 2):
+ *     code entry e = 32 c + 16 h + j (e < 512), chunk c = 4 kb + fb: the 32
+ *       codes (canonical nibble order) of feature 64 s + 16 fb + j for
+ *       k = 256 u + 64 kb + 32 h .. + 31, i.e. 16 consecutive canonical bytes;
+ *     scale entry e = 512 + 16 g + j: byte 4 kb + fb is the E4M3 scale of
+ *       feature 64 s + 16 fb + j for group 16 u + 4 kb + g.
+ *   Features >= n and k >= k are zero padding.  Each 512-byte code chunk is
+ *   the weight operand of one block-scaled matrix-core product (16 features x
+ *   64 k); a wave reads it with one aligned 16-byte load per lane.
  *   The header holds s_g (float at byte 0), the layout magic and version, n, k.
  *   One wave instruction therefore reads one whole, aligned 1 KB run.
  */
@@ -56,7 +61,7 @@ extern "C" {
 
 #define NVFP4_ABI_VERSION 1
 #define NVFP4_LAYOUT_MAGIC 0x34465056u /* "VPF4" */
-#define NVFP4_LAYOUT_VERSION 1u
+#define NVFP4_LAYOUT_VERSION 2u
 #define NVFP4_MAX_ROWS 8
 
 enum {

@@ -71,12 +71,15 @@ def _run_dual(nv, gw, uw, xb):
 # ---- layout -----------------------------------------------------------------
 
 def _layout_numpy(codes, scales, sg, n, k):
-    """The packed layout, written out from its definition."""
+    """The packed layout (version 2), written out from its definition: per
+    super-tile, code entry 32 c + 16 h + j (chunk c = 4 kb + fb) = canonical
+    code bytes of feature 16 fb + j for k = 64 kb + 32 h .. + 31; scale entry
+    16 g + j, byte 4 kb + fb = scale of feature 16 fb + j, group 4 kb + g."""
     S, T = -(-n // 64), -(-k // 256)
     out = np.zeros(256 + S * T * 9216, np.uint8)
     out[0:4] = np.frombuffer(np.float32(sg).tobytes(), np.uint8)
     out[4:8] = np.frombuffer(np.uint32(0x34465056).tobytes(), np.uint8)
-    out[8:12] = np.frombuffer(np.uint32(1).tobytes(), np.uint8)
+    out[8:12] = np.frombuffer(np.uint32(2).tobytes(), np.uint8)
     out[16:24] = np.frombuffer(np.int64(n).tobytes(), np.uint8)
     out[24:32] = np.frombuffer(np.int64(k).tobytes(), np.uint8)
     cpad = np.zeros((S * 64, T * 128), np.uint8)
@@ -86,10 +89,18 @@ def _layout_numpy(codes, scales, sg, n, k):
     for s in range(S):
         for u in range(T):
             base = 256 + (s * T + u) * 9216
-            for t in range(8):
-                blk = cpad[64 * s: 64 * s + 64, 128 * u + 16 * t: 128 * u + 16 * t + 16]
-                out[base + 1024 * t: base + 1024 * (t + 1)] = blk.reshape(-1)
-            out[base + 8192: base + 9216] = spad[64 * s: 64 * s + 64, 16 * u: 16 * u + 16].reshape(-1)
+            for kb in range(4):
+                for fb in range(4):
+                    for h in range(2):
+                        for j in range(16):
+                            e = 32 * (4 * kb + fb) + 16 * h + j
+                            f, c0 = 64 * s + 16 * fb + j, 128 * u + 32 * kb + 16 * h
+                            out[base + 16 * e: base + 16 * e + 16] = cpad[f, c0: c0 + 16]
+                for g in range(4):
+                    for j in range(16):
+                        e = 512 + 16 * g + j
+                        for fb in range(4):
+                            out[base + 16 * e + 4 * kb + fb] = spad[64 * s + 16 * fb + j, 16 * u + 4 * kb + g]
     return out
 
 
