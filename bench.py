@@ -13,9 +13,9 @@ layers: 13 GB >> the 256 MB Infinity Cache).
 The headline value is the aggregate packed-weight read rate (GB/s) of the
 rows=1 step; rows 2, 4, 8 are reported alongside.  Timing: W untimed warmup
 steps, then K steps bracketed by device synchronization and HIP events on the
-launch stream.  Each step is enqueued by one nvfp4_gemv_sequence call; within
-the timed steps a HIP event pair brackets one gate/up launch per step (a
-different layer each step) for the roofline's per-launch duration.
+launch stream.  Each step is enqueued by one nvfp4_gemv_sequence call.  The
+roofline's per-launch duration of the gate/up pair kernel is timed the same
+way over the 64 layers' pairs launched back to back.
 
 The CPU baseline times the fp64 CPU oracle on layer 0 of the same workload.
 """
@@ -61,6 +61,9 @@ def parse_args():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the gate/up pair's HBM traffic per launch from two rocprofv3 --pmc counter "
+                         "collections (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (known bytes) to scale PMC byte counters")
     return ap.parse_args()
@@ -96,42 +99,39 @@ def make_sequence(nv, torch, dev, workloads, mats, rows):
     o_gu = torch.empty((rows, 17408), dtype=torch.bfloat16, device=dev)
     y_down = torch.empty((rows, 5120), dtype=torch.bfloat16, device=dev)
     calls = []
-    pair_index = []
     for lm in mats:
         calls.append((lm["qkv"], None, x5120, y_qkv))
         calls.append((lm["o"], None, x6144, y_o))
-        pair_index.append(len(calls))
         calls.append((lm["gate"], lm["up"], x5120, o_gu))
         calls.append((lm["down"], None, o_gu, y_down))
-    return nv.Sequence(calls), pair_index
+    return nv.Sequence(calls)
 
 
-def time_rows(nv, torch, seq, pair_index, ws, steps, warmup):
+def time_rows(torch, seq, ws, steps, warmup):
+    """Average ms per step over `steps` steps after `warmup` untimed ones."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         seq.launch(ws)
-    # per-step event pairs around one gate/up launch (created by a first record)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in evs:
-        a.record(stream)
-        b.record(stream)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    handles = []
-    for i in range(steps):
-        h = [None] * (2 * seq.n)
-        j = pair_index[i % len(pair_index)]
-        h[2 * j] = evs[i][0].cuda_event
-        h[2 * j + 1] = evs[i][1].cuda_event
-        handles.append(h)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(steps):
-        seq.launch(ws, events=handles[i])
+    for _ in range(steps):
+        seq.launch(ws)
     stop.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    pair_ms = [a.elapsed_time(b) for a, b in evs]
-    return total_ms / steps, sum(pair_ms) / len(pair_ms)
+    return start.elapsed_time(stop) / steps
+
+
+def time_pair(nv, torch, dev, mats, rows, ws, reps):
+    """Average duration of one gate/up pair launch: the 64 layers' pairs back to
+    back (distinct weights, so no cache reuse), `reps` times, between HIP events
+    on the launch stream."""
+    x = torch.zeros((rows, 5120), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((rows, 17408), dtype=torch.bfloat16, device=dev)
+    seq = nv.Sequence([(lm["gate"], lm["up"], x, o) for lm in mats])
+    seq.launch(ws)
+    ms = time_rows(torch, seq, ws, reps, 1)
+    return ms / len(mats)
 
 
 def cpu_baseline(workloads, torch, dev, target_s):
@@ -184,8 +184,65 @@ def load_traffic(bytes_per_launch):
     return t.get("bytes_per_launch")
 
 
+PAIR_KERNEL_TAG = "stream_kernel<1, 2>"     # rows=1 instance of the gate/up pair kernel
+COPY_BYTES = 1 << 30                         # --copy-calibration copies this many bytes
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """HBM bytes per launch of the rows=1 gate/up pair kernel from rocprofv3
+    counter collections.  FETCH_SIZE and WRITE_SIZE are reported in KiB per
+    dispatch; each is scaled by what the same counter reads for the 1 GiB
+    device copy of the same run (known bytes)."""
+    import csv
+
+    def per_kernel(path):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
+
+    def pick(table, pred):
+        keys = [k for k in table if pred(k)]
+        if not keys:
+            raise SystemExit("no matching kernel in the counter file")
+        vals = [v for k in keys for v in table[k]]
+        return sum(vals) / len(vals), len(vals), keys[0]
+
+    pair = lambda k: PAIR_KERNEL_TAG in k
+    # the torch copy of --copy-calibration: the only dispatch whose counters exceed 0.9 GiB
+    copy_f = max(v for vals in f.values() for v in vals)
+    copy_w = max(v for vals in w.values() for v in vals)
+    fetch_factor = COPY_BYTES / (copy_f * 1024.0)
+    write_factor = COPY_BYTES / (copy_w * 1024.0)
+    pf, n_f, name = pick(f, pair)
+    pw, n_w, _ = pick(w, pair)
+    fetch_bytes = pf * 1024.0 * fetch_factor
+    write_bytes = pw * 1024.0 * write_factor
+    t = {
+        "kernel": name,
+        "kernel_source_hash": kernel_source_hash(),
+        "dispatches": [n_f, n_w],
+        "fetch_kib_per_dispatch": round(pf, 1),
+        "write_kib_per_dispatch": round(pw, 1),
+        "copy_fetch_kib": round(copy_f, 1),
+        "copy_write_kib": round(copy_w, 1),
+        "fetch_factor": round(fetch_factor, 4),
+        "write_factor": round(write_factor, 4),
+        "algorithmic_bytes_per_launch": 2 * packed_weight_bytes(17408, 5120),
+        "bytes_per_launch": int(round(fetch_bytes + write_bytes)),
+    }
+    with open(TRAFFIC_FILE, "w") as fo:
+        json.dump(t, fo, indent=1)
+    print(json.dumps(t))
+
+
 def main():
     args = parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the NVFP4 projection path here has no multi-GPU mode "
@@ -220,11 +277,11 @@ def main():
         log("copy calibration: 1 GiB device-to-device copy done")
 
     seqs = {r: make_sequence(nv, torch, dev, workloads, mats, r) for r in rows_list}
-    ws = torch.zeros(max(s.workspace_bytes for s, _ in seqs.values()), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(s.workspace_bytes for s in seqs.values()), dtype=torch.uint8, device=dev)
     by_rows = {}
     for r in rows_list:
-        seq, pidx = seqs[r]
-        ms, pair_ms = time_rows(nv, torch, seq, pidx, ws, args.steps, args.warmup)
+        ms = time_rows(torch, seqs[r], ws, args.steps, args.warmup)
+        pair_ms = time_pair(nv, torch, dev, mats, r, ws, max(2, args.steps // 10))
         gbs = step_bytes / (ms * 1e-3) / 1e9
         by_rows[str(r)] = {
             "ms_per_step": round(ms, 4),
@@ -241,7 +298,7 @@ def main():
     achieved = pair_bytes / pair_s / 1e9
     roofline = {
         "bound": "hbm",
-        "kernel": "gemv_kernel<rows=%d, pair> (gate/up 2x[17408x5120] + SiLU*mul)" % rows_list[0],
+        "kernel": "stream_kernel<%d, 2> (gate/up pair 2x[17408x5120] + SiLU*mul)" % rows_list[0],
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
