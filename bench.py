@@ -4,8 +4,9 @@
 One step = the weight-only NVFP4 projections of a 64-layer 27B-class decoder
 at one row count: per layer qkv [12288x5120], o [5120x6144], the gate/up pair
 2x[17408x5120] with SiLU*mul, down [5120x17408] (whose input is the pair's
-output), 256 launches, 13,023,313,920 bytes of packed weights (E2M1 codes +
-E4M3 scales, 9/16 byte per weight).  Weights ~ N(0, 0.02^2) are drawn on the
+output), 256 calls, 13,023,313,920 bytes of packed weights (E2M1 codes +
+E4M3 scales, 9/16 byte per weight).  The calls run in order, each after the
+previous one has completed, in shared launches of up to 40 calls.  Weights ~ N(0, 0.02^2) are drawn on the
 device from seeded generators and quantized on the device; activations are
 bf16 ~ N(0, 1).  All weights stay resident in HBM (no cache reuse between
 layers: 13 GB >> the 256 MB Infinity Cache).
@@ -13,9 +14,10 @@ layers: 13 GB >> the 256 MB Infinity Cache).
 The headline value is the aggregate packed-weight read rate (GB/s) of the
 rows=1 step; rows 2, 4, 8 are reported alongside.  Timing: W untimed warmup
 steps, then K steps bracketed by device synchronization and HIP events on the
-launch stream.  Each step is enqueued by one nvfp4_gemv_sequence call.  The
-roofline's per-launch duration of the gate/up pair kernel is timed the same
-way over the 64 layers' pairs launched back to back.
+launch stream.  Each step is enqueued by one nvfp4_gemv_sequence call; the
+roofline's kernel is its shared launch (bytes and duration per launch).  The
+stand-alone gate/up pair launch (nvfp4_gemv_dual_silu) is timed as well, over
+the 64 layers' pairs launched back to back.
 
 The CPU baseline times the fp64 CPU oracle on layer 0 of the same workload.
 """
@@ -37,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 PAIR_NAME = "gate"
 KERNEL_SOURCES = ("bit_weight_only_nvfp4_amd/csrc/nvfp4_stream.hip", "bit_weight_only_nvfp4_amd/csrc/nvfp4_core.h",
                   "bit_weight_only_nvfp4_amd/csrc/nvfp4_internal.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_pair_rows1_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_rows1_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -52,6 +54,11 @@ def packed_weight_bytes(n: int, k: int) -> int:
     return n * k // 2 + n * k // 16
 
 
+# packed weight bytes of one 64-layer decode step
+STEP_BYTES_64 = 64 * (packed_weight_bytes(12288, 5120) + packed_weight_bytes(5120, 6144)
+                      + 2 * packed_weight_bytes(17408, 5120) + packed_weight_bytes(5120, 17408))
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,9 +68,10 @@ def parse_args():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the gate/up pair's HBM traffic per launch from two rocprofv3 --pmc counter "
-                         "collections (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run, then exit")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LAUNCHES_PER_STEP"),
+                    help="write the rows=1 decode-step kernel's HBM traffic per launch from two rocprofv3 "
+                         "--pmc counter collections (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run of "
+                         "the 64-layer sweep, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (known bytes) to scale PMC byte counters")
     return ap.parse_args()
@@ -123,15 +131,24 @@ def time_rows(torch, seq, ws, steps, warmup):
 
 
 def time_pair(nv, torch, dev, mats, rows, ws, reps):
-    """Average duration of one gate/up pair launch: the 64 layers' pairs back to
-    back (distinct weights, so no cache reuse), `reps` times, between HIP events
-    on the launch stream."""
+    """Average duration of one stand-alone gate/up pair launch (what
+    nvfp4_gemv_dual_silu runs): the 64 layers' pairs back to back, one launch
+    each (distinct weights, so no cache reuse), `reps` times, between HIP
+    events on the launch stream."""
     x = torch.zeros((rows, 5120), dtype=torch.bfloat16, device=dev)
     o = torch.empty((rows, 17408), dtype=torch.bfloat16, device=dev)
     seq = nv.Sequence([(lm["gate"], lm["up"], x, o) for lm in mats])
-    seq.launch(ws)
-    ms = time_rows(torch, seq, ws, reps, 1)
-    return ms / len(mats)
+    one_each = [None] * (2 * seq.n)   # event slots given: one launch per call
+    seq.launch(ws, events=one_each)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        seq.launch(ws, events=one_each)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / reps / len(mats)
 
 
 def cpu_baseline(workloads, torch, dev, target_s):
@@ -171,9 +188,10 @@ def cpu_baseline(workloads, torch, dev, target_s):
     }
 
 
-def load_traffic(bytes_per_launch):
-    """HBM bytes per launch of the gate/up pair from the committed PMC summary,
-    or None when it is missing or the kernel source changed since."""
+def load_traffic():
+    """HBM bytes per launch of the rows=1 decode-step kernel (64-layer sweep)
+    from the committed PMC summary, or None when it is missing or the kernel
+    source changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -184,12 +202,12 @@ def load_traffic(bytes_per_launch):
     return t.get("bytes_per_launch")
 
 
-PAIR_KERNEL_TAG = "stream_kernel<1, 2>"     # rows=1 instance of the gate/up pair kernel
+STEP_KERNEL_TAG = "seq_kernel<1, true>"     # rows=1 shared-launch kernel of the decode step
 COPY_BYTES = 1 << 30                         # --copy-calibration copies this many bytes
 
 
-def summarize_pmc(fetch_csv, write_csv):
-    """HBM bytes per launch of the rows=1 gate/up pair kernel from rocprofv3
+def summarize_pmc(fetch_csv, write_csv, launches_per_step):
+    """HBM bytes per launch of the rows=1 decode-step kernel from rocprofv3
     counter collections.  FETCH_SIZE and WRITE_SIZE are reported in KiB per
     dispatch; each is scaled by what the same counter reads for the 1 GiB
     device copy of the same run (known bytes)."""
@@ -210,7 +228,7 @@ def summarize_pmc(fetch_csv, write_csv):
         vals = [v for k in keys for v in table[k]]
         return sum(vals) / len(vals), len(vals), keys[0]
 
-    pair = lambda k: PAIR_KERNEL_TAG in k
+    pair = lambda k: STEP_KERNEL_TAG in k
     # the torch copy of --copy-calibration: the only dispatch whose counters exceed 0.9 GiB
     copy_f = max(v for vals in f.values() for v in vals)
     copy_w = max(v for vals in w.values() for v in vals)
@@ -230,7 +248,8 @@ def summarize_pmc(fetch_csv, write_csv):
         "copy_write_kib": round(copy_w, 1),
         "fetch_factor": round(fetch_factor, 4),
         "write_factor": round(write_factor, 4),
-        "algorithmic_bytes_per_launch": 2 * packed_weight_bytes(17408, 5120),
+        "launches_per_step": launches_per_step,
+        "algorithmic_bytes_per_launch": STEP_BYTES_64 // launches_per_step,
         "bytes_per_launch": int(round(fetch_bytes + write_bytes)),
     }
     with open(TRAFFIC_FILE, "w") as fo:
@@ -241,7 +260,7 @@ def summarize_pmc(fetch_csv, write_csv):
 def main():
     args = parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], int(args.summarize_pmc[2]))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -285,27 +304,33 @@ def main():
         gbs = step_bytes / (ms * 1e-3) / 1e9
         by_rows[str(r)] = {
             "ms_per_step": round(ms, 4),
+            "launches_per_step": seqs[r].launches,
             "GB_per_s": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "gate_up_pair_us": round(pair_ms * 1e3, 3),
             "gate_up_pair_GB_per_s": round(pair_bytes / (pair_ms * 1e-3) / 1e9, 1),
         }
-        log("rows=%d: %.4f ms/step, %.1f GB/s (%.1f%% of 8 TB/s); gate/up pair %.2f us" % (
-            r, ms, gbs, 100 * gbs / HBM_PEAK_GBS, pair_ms * 1e3))
+        log("rows=%d: %.4f ms/step in %d launches, %.1f GB/s (%.1f%% of 8 TB/s); stand-alone gate/up pair "
+            "%.2f us" % (r, ms, seqs[r].launches, gbs, 100 * gbs / HBM_PEAK_GBS, pair_ms * 1e3))
 
     head = by_rows[str(rows_list[0])]
-    pair_s = head["gate_up_pair_us"] * 1e-6
-    achieved = pair_bytes / pair_s / 1e9
+    # The dominant kernel is the shared launch that runs the step's calls
+    # (every byte of the step is read by it): bytes and duration per launch.
+    launches = head["launches_per_step"]
+    launch_bytes = step_bytes / launches
+    launch_us = head["ms_per_step"] * 1e3 / launches
+    achieved = launch_bytes / (launch_us * 1e-6) / 1e9
     roofline = {
         "bound": "hbm",
-        "kernel": "stream_kernel<%d, 2> (gate/up pair 2x[17408x5120] + SiLU*mul)" % rows_list[0],
+        "kernel": "seq_kernel<%d, true> (shared launch of %d consecutive decode-step calls: qkv, o, "
+                  "gate/up pair + SiLU*mul, down)" % (rows_list[0], round(4 * args.layers / launches)),
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": load_traffic(pair_bytes),
-        "bytes_per_launch": pair_bytes,
-        "avg_launch_us": head["gate_up_pair_us"],
+        "traffic": load_traffic() if args.layers == 64 and rows_list[0] == 1 else None,
+        "bytes_per_launch": round(launch_bytes),
+        "avg_launch_us": round(launch_us, 2),
     }
 
     cpu = None
@@ -333,7 +358,8 @@ def main():
             "layers": args.layers,
             "rows": rows_list[0],
             "packed_weight_bytes_per_step": step_bytes,
-            "launches_per_step": 4 * args.layers,
+            "calls_per_step": 4 * args.layers,
+            "launches_per_step": head["launches_per_step"],
         },
         "pct_hbm_peak": head["pct_hbm_peak"],
         "by_rows": by_rows,

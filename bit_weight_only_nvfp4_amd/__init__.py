@@ -9,7 +9,7 @@ Entry points (same names as the C ABI):
   nvfp4_packed_bytes, nvfp4_pack, nvfp4_unpack, nvfp4_dequant,
   nvfp4_quantize_workspace_bytes, nvfp4_quantize,
   nvfp4_workspace_bytes, nvfp4_gemv, nvfp4_gemv_dual_silu,
-  nvfp4_sequence_workspace_bytes, nvfp4_gemv_sequence,
+  nvfp4_sequence_workspace_bytes, nvfp4_gemv_sequence, nvfp4_sequence_launches,
   nvfp4_abi_version, nvfp4_strerror, nvfp4_last_error.
 """
 from __future__ import annotations
@@ -32,14 +32,14 @@ NVFP4_OUT_F32 = 1
 STATUS = {
     0: "NVFP4_OK", -1: "NVFP4_E_NULL", -2: "NVFP4_E_SHAPE", -3: "NVFP4_E_ROWS", -4: "NVFP4_E_ALIGN",
     -5: "NVFP4_E_DTYPE", -6: "NVFP4_E_WORKSPACE", -7: "NVFP4_E_LAYOUT", -8: "NVFP4_E_DEVICE",
-    -9: "NVFP4_E_HIP",
+    -9: "NVFP4_E_HIP", -10: "NVFP4_E_OVERLAP",
 }
 
 EXPORTS = (
     "nvfp4_abi_version", "nvfp4_strerror", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
     "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
-    "nvfp4_gemv_sequence",
+    "nvfp4_gemv_sequence", "nvfp4_sequence_launches",
 )
 
 
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "nvfp4_gemv": ([wp, vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp], ctypes.c_int),
             "nvfp4_gemv_dual_silu": ([wp, wp, vp, ctypes.c_int, vp, ctypes.c_int, vp, sz, vp], ctypes.c_int),
             "nvfp4_sequence_workspace_bytes": ([ctypes.POINTER(nvfp4_call), ctypes.c_int], sz),
+            "nvfp4_sequence_launches": ([ctypes.POINTER(nvfp4_call), ctypes.c_int], ctypes.c_int),
             "nvfp4_gemv_sequence": ([ctypes.POINTER(nvfp4_call), ctypes.c_int, vp, sz,
                                      ctypes.POINTER(ctypes.c_void_p), vp], ctypes.c_int),
         }
@@ -317,10 +318,13 @@ class Sequence:
             c.out_dtype = _OUT[y.dtype]
             self._keep.append((w, up, x, y))
         self.workspace_bytes = int(lib().nvfp4_sequence_workspace_bytes(self._arr, self.n))
+        # kernel launches of one launch() without events
+        self.launches = int(lib().nvfp4_sequence_launches(self._arr, self.n))
 
     def launch(self, workspace: torch.Tensor | None = None, events=None, stream=None):
         """Enqueue every call on ``stream`` (default: the current stream).
-        ``events``: None or a list of 2*n raw hipEvent_t handles (or None)."""
+        ``events``: None or a list of 2*n raw hipEvent_t handles (or None); with
+        events, every call gets a kernel launch of its own."""
         dev = self._keep[0][2].device if self._keep else torch.device("cuda")
         if workspace is None:
             workspace = _workspace(dev, self.workspace_bytes)
@@ -337,6 +341,10 @@ class Sequence:
 
 def nvfp4_sequence_workspace_bytes(calls) -> int:
     return Sequence(calls).workspace_bytes
+
+
+def nvfp4_sequence_launches(calls) -> int:
+    return Sequence(calls).launches
 
 
 def nvfp4_gemv_sequence(calls, workspace: torch.Tensor | None = None, events=None) -> None:

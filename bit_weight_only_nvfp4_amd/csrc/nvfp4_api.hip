@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "nvfp4_internal.h"
 
@@ -79,8 +80,7 @@ int check_weight(const char *fn, const char *name, const nvfp4_weight *w) {
     return NVFP4_OK;
 }
 
-int check_gemv_args(const char *fn, const void *x, int rows, const void *y, int out_dtype, int64_t n,
-                    int64_t k, int dual, const void *workspace, size_t workspace_bytes) {
+int check_gemv_args(const char *fn, const void *x, int rows, const void *y, int out_dtype) {
     if (!x) return fail(NVFP4_E_NULL, "%s: x is NULL", fn);
     if (!y) return fail(NVFP4_E_NULL, "%s: y is NULL", fn);
     if (rows < 1 || rows > NVFP4_MAX_ROWS)
@@ -90,16 +90,84 @@ int check_gemv_args(const char *fn, const void *x, int rows, const void *y, int 
     if (!aligned(x, 16)) return fail(NVFP4_E_ALIGN, "%s: x is not 16-byte aligned", fn);
     if (!aligned(y, out_dtype == NVFP4_OUT_F32 ? 4 : 2))
         return fail(NVFP4_E_ALIGN, "%s: y is not aligned to its element size", fn);
-    const StreamPlan pl = make_stream_plan(n, k, rows, dual);
-    const size_t need = pl.counter_bytes + pl.partial_bytes;
-    if (need > 0) {
-        if (!workspace)
-            return fail(NVFP4_E_WORKSPACE, "%s: workspace is NULL but %zu bytes are needed", fn, need);
-        if (workspace_bytes < need)
-            return fail(NVFP4_E_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
-        if (!aligned(workspace, 16)) return fail(NVFP4_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    return NVFP4_OK;
+}
+
+int check_workspace(const char *fn, const void *workspace, size_t workspace_bytes, size_t need) {
+    if (need == 0) return NVFP4_OK;
+    if (!workspace) return fail(NVFP4_E_WORKSPACE, "%s: workspace is NULL but %zu bytes are needed", fn, need);
+    if (workspace_bytes < need)
+        return fail(NVFP4_E_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if (!aligned(workspace, 16)) return fail(NVFP4_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    return NVFP4_OK;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+size_t x_bytes(const StreamCall &c) { return (size_t)c.plan.rows * c.plan.k * 2; }
+size_t y_bytes(const StreamCall &c) { return (size_t)c.plan.rows * c.plan.n * (c.out_f32 ? 4 : 2); }
+size_t w_bytes(const StreamCall &c) { return nvfp4_packed_bytes(c.plan.n, c.plan.k); }
+
+// A call's outputs may not overlap its own activations, the workspace or any
+// weight of the launch (weights are read ahead across calls).
+int check_overlaps(const char *fn, const StreamCall *calls, int ncalls, const void *workspace, size_t ws_bytes) {
+    for (int i = 0; i < ncalls; ++i) {
+        const StreamCall &c = calls[i];
+        if (overlap(c.y, y_bytes(c), c.x, x_bytes(c)))
+            return fail(NVFP4_E_OVERLAP, "%s: call %d: y overlaps its x", fn, i);
+        if (overlap(c.y, y_bytes(c), workspace, ws_bytes))
+            return fail(NVFP4_E_OVERLAP, "%s: call %d: y overlaps the workspace", fn, i);
+        for (int j = 0; j < ncalls; ++j) {
+            const StreamCall &o = calls[j];
+            if (overlap(c.y, y_bytes(c), o.w0, w_bytes(o)) || (o.w1 && overlap(c.y, y_bytes(c), o.w1, w_bytes(o))))
+                return fail(NVFP4_E_OVERLAP, "%s: call %d: y overlaps the weight of call %d", fn, i, j);
+        }
     }
     return NVFP4_OK;
+}
+
+StreamCall make_call(const nvfp4_weight *w, const nvfp4_weight *up, const void *x, int rows, void *y,
+                     int out_dtype) {
+    StreamCall c{};
+    c.plan = make_stream_plan(w->n, w->k, rows, up != nullptr);
+    c.w0 = w->data;
+    c.w1 = up ? up->data : nullptr;
+    c.x = x;
+    c.y = y;
+    c.out_f32 = out_dtype == NVFP4_OUT_F32;
+    return c;
+}
+
+// Validate one projection or pair call (everything but the workspace).
+int check_call(const char *fn, const nvfp4_weight *w, const nvfp4_weight *up, const void *x, int rows,
+               const void *y, int out_dtype) {
+    int st = check_weight(fn, up ? "gate" : "w", w);
+    if (st) return st;
+    if (up) {
+        st = check_weight(fn, "up", up);
+        if (st) return st;
+        if (w->n != up->n || w->k != up->k)
+            return fail(NVFP4_E_SHAPE, "%s: gate is %lldx%lld but up is %lldx%lld", fn, (long long)w->n,
+                        (long long)w->k, (long long)up->n, (long long)up->k);
+    }
+    return check_gemv_args(fn, x, rows, y, out_dtype);
+}
+
+int run_one(const char *fn, const nvfp4_weight *w, const nvfp4_weight *up, const void *x, int rows, void *y,
+            int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_call(fn, w, up, x, rows, y, out_dtype);
+    if (st) return st;
+    const StreamCall c = make_call(w, up, x, rows, y, out_dtype);
+    st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(&c, 1));
+    if (st) return st;
+    st = check_overlaps(fn, &c, 1, workspace, workspace_bytes);
+    if (st) return st;
+    st = check_device(fn);
+    if (st) return st;
+    return hip_status(fn, launch_sequence(&c, 1, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -120,6 +188,7 @@ const char *nvfp4_strerror(int status) {
         case NVFP4_E_LAYOUT: return "packed weight layout mismatch";
         case NVFP4_E_DEVICE: return "unsupported device";
         case NVFP4_E_HIP: return "HIP runtime error";
+        case NVFP4_E_OVERLAP: return "an output overlaps an input or the workspace";
         default: return "unknown status";
     }
 }
@@ -212,53 +281,47 @@ int nvfp4_quantize(const float *W, int64_t n, int64_t k, void *packed, size_t pa
 
 size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual) {
     if (!valid_shape(n, k) || rows < 1 || rows > NVFP4_MAX_ROWS) return 0;
-    const StreamPlan pl = make_stream_plan(n, k, rows, dual != 0);
-    return pl.counter_bytes + pl.partial_bytes;
+    StreamCall c{};
+    c.plan = make_stream_plan(n, k, rows, dual != 0);
+    return sequence_workspace_bytes(&c, 1);
 }
 
 int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype, void *workspace,
                size_t workspace_bytes, void *stream) {
-    static const char *fn = "nvfp4_gemv";
-    int st = check_weight(fn, "w", w);
-    if (st) return st;
-    st = check_gemv_args(fn, x, rows, y, out_dtype, w->n, w->k, 0, workspace, workspace_bytes);
-    if (st) return st;
-    st = check_device(fn);
-    if (st) return st;
-    const StreamPlan pl = make_stream_plan(w->n, w->k, rows, 0);
-    return hip_status(fn, launch_stream(pl, w->data, nullptr, x, y, out_dtype == NVFP4_OUT_F32, workspace,
-                                        static_cast<hipStream_t>(stream)));
+    return run_one("nvfp4_gemv", w, nullptr, x, rows, y, out_dtype, workspace, workspace_bytes, stream);
 }
 
 int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const void *x, int rows, void *y,
                          int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
-    static const char *fn = "nvfp4_gemv_dual_silu";
-    int st = check_weight(fn, "gate", gate);
-    if (st) return st;
-    st = check_weight(fn, "up", up);
-    if (st) return st;
-    if (gate->n != up->n || gate->k != up->k)
-        return fail(NVFP4_E_SHAPE, "%s: gate is %lldx%lld but up is %lldx%lld", fn, (long long)gate->n,
-                    (long long)gate->k, (long long)up->n, (long long)up->k);
-    st = check_gemv_args(fn, x, rows, y, out_dtype, gate->n, gate->k, 1, workspace, workspace_bytes);
-    if (st) return st;
-    st = check_device(fn);
-    if (st) return st;
-    const StreamPlan pl = make_stream_plan(gate->n, gate->k, rows, 1);
-    return hip_status(fn, launch_stream(pl, gate->data, up->data, x, y, out_dtype == NVFP4_OUT_F32, workspace,
-                                        static_cast<hipStream_t>(stream)));
+    if (!up) return fail(NVFP4_E_NULL, "nvfp4_gemv_dual_silu: up is NULL");
+    return run_one("nvfp4_gemv_dual_silu", gate, up, x, rows, y, out_dtype, workspace, workspace_bytes, stream);
 }
 
 size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls) {
-    if (!calls || ncalls < 0) return 0;
-    size_t need = 0;
+    if (!calls || ncalls <= 0) return 0;
+    std::vector<StreamCall> sc;
+    sc.reserve(ncalls);
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
         if (!c.w || !valid_shape(c.w->n, c.w->k) || c.rows < 1 || c.rows > NVFP4_MAX_ROWS) continue;
-        const size_t b = nvfp4_workspace_bytes(c.w->n, c.w->k, c.rows, c.up != nullptr);
-        if (b > need) need = b;
+        StreamCall s{};
+        s.plan = make_stream_plan(c.w->n, c.w->k, c.rows, c.up != nullptr);
+        sc.push_back(s);
     }
-    return need;
+    return sequence_workspace_bytes(sc.data(), (int)sc.size());
+}
+
+int nvfp4_sequence_launches(const nvfp4_call *calls, int ncalls) {
+    if (!calls || ncalls <= 0) return 0;
+    std::vector<StreamCall> sc;
+    sc.reserve(ncalls);
+    for (int i = 0; i < ncalls; ++i) {
+        const nvfp4_call &c = calls[i];
+        StreamCall s{};
+        s.plan.rows = c.rows;
+        sc.push_back(s);
+    }
+    return sequence_launches(sc.data(), ncalls);
 }
 
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
@@ -268,37 +331,32 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
     if (ncalls == 0) return ok();
     if (!calls) return fail(NVFP4_E_NULL, "%s: calls is NULL", fn);
     char name[64];
+    std::vector<StreamCall> sc((size_t)ncalls);
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
         snprintf(name, sizeof name, "%s call %d", fn, i);
-        int st = check_weight(name, c.up ? "gate" : "w", c.w);
+        int st = check_call(name, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
         if (st) return st;
-        if (c.up) {
-            st = check_weight(name, "up", c.up);
-            if (st) return st;
-            if (c.up->n != c.w->n || c.up->k != c.w->k)
-                return fail(NVFP4_E_SHAPE, "%s: gate is %lldx%lld but up is %lldx%lld", name, (long long)c.w->n,
-                            (long long)c.w->k, (long long)c.up->n, (long long)c.up->k);
-        }
-        st = check_gemv_args(name, c.x, c.rows, c.y, c.out_dtype, c.w->n, c.w->k, c.up != nullptr, workspace,
-                             workspace_bytes);
-        if (st) return st;
+        sc[i] = make_call(c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
     }
-    int st = check_device(fn);
+    int st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(sc.data(), ncalls));
+    if (st) return st;
+    st = check_overlaps(fn, sc.data(), ncalls, workspace, workspace_bytes);
+    if (st) return st;
+    st = check_device(fn);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!events) return hip_status(fn, launch_sequence(sc.data(), ncalls, workspace, s));
+    // per-call timing: one launch per call, each between its two events
     for (int i = 0; i < ncalls; ++i) {
-        const nvfp4_call &c = calls[i];
-        if (events && events[2 * i]) {
+        if (events[2 * i]) {
             hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[2 * i]), s);
             if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: hipEventRecord before call %d: %s", fn, i,
                                              hipGetErrorString(e));
         }
-        const StreamPlan pl = make_stream_plan(c.w->n, c.w->k, c.rows, c.up != nullptr);
-        hipError_t e = launch_stream(pl, c.w->data, c.up ? c.up->data : nullptr, c.x, c.y,
-                                     c.out_dtype == NVFP4_OUT_F32, workspace, s);
+        hipError_t e = launch_sequence(&sc[i], 1, workspace, s);
         if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: launch of call %d failed: %s", fn, i, hipGetErrorString(e));
-        if (events && events[2 * i + 1]) {
+        if (events[2 * i + 1]) {
             e = hipEventRecord(static_cast<hipEvent_t>(events[2 * i + 1]), s);
             if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: hipEventRecord after call %d: %s", fn, i,
                                              hipGetErrorString(e));

@@ -44,15 +44,23 @@ __host__ __device__ inline int scale_byte_offset(int f, int gt) {
     return kScaleOffset + (((gt & 3) << 4) + (f & 15)) * 16 + (gt >> 2) * 4 + (f >> 4);
 }
 
-// Split-K arrival counters live in a fixed region at the front of every
-// projection workspace, one per strip, for up to kMaxStrips strips (n <= 2^20).
-// The region does not depend on the call's shape, so partial sums of one call
-// can never land where another call's counters are: a zero-filled workspace
-// stays valid for calls of any shape, since every call returns its counters
-// to zero.
+// Projection workspace layout.  Fixed regions that do not depend on the
+// call's shape, so partial sums of one call can never land where another
+// call's counters are: a zero-filled workspace stays valid for calls of any
+// shape, since every launch returns its counters to zero.
+//   [0, 32 KiB): split-K arrival counters, one per 128-byte line for each of
+//                up to 256 shared strips (a call has fewer shared strips
+//                than workgroups);
+//   [32 KiB, 64 KiB): one 128-byte line per workgroup of a multi-call launch:
+//                word 0 = the last call it may go past;
+//   [64 KiB, 65 KiB): word 0 = set when a wait between calls timed out,
+//                word 32 = arrivals between calls, word 64 = workgroups
+//                done with the launch (one 128-byte line each);
+//   [65 KiB, ...): fp32 partial sums of the call running.
 constexpr int64_t kMaxN = (int64_t)1 << 20;
-constexpr int64_t kMaxStrips = kMaxN / kStripN;                 // 16384
-constexpr size_t kCounterRegionBytes = (size_t)kMaxStrips * 4;  // 64 KiB
+constexpr size_t kSyncOffset = 32 * 1024;
+constexpr size_t kFlagOffset = 64 * 1024;
+constexpr size_t kPartialOffset = 65 * 1024;
 
 // Bytes 32..255 of the header are always zero (pack and quantize write them);
 // kernels use them as a 16-byte source of zeros.
@@ -116,34 +124,49 @@ constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workg
 constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
 constexpr int kMaxWavesPerWg = 8;
 // Up to 4 activation rows a wave needs at most 256 registers, so two waves
-// share each SIMD (8 per workgroup) and hide each other's latencies; more rows
-// need up to 512 registers: one wave per SIMD.
+// share each SIMD (8 per workgroup): wave 0 is then a control wave (it reduces
+// and writes the results and keeps the order between calls, and has no weight
+// loads in flight), the other 7 stream the weights.  More rows need up to 512
+// registers: one wave per SIMD, all 4 streaming, wave 0 also writing.
 constexpr int kWideRowsMax = 4;
 __host__ __device__ constexpr int max_waves_for_rows(int rows) { return rows <= kWideRowsMax ? 8 : 4; }
-#ifndef NVFP4_STREAM_WAVES_SINGLE
-#define NVFP4_STREAM_WAVES_SINGLE 8
-#endif
-#ifndef NVFP4_STREAM_WAVES_PAIR
-#define NVFP4_STREAM_WAVES_PAIR 8
-#endif
-constexpr int kStreamWavesSingle = NVFP4_STREAM_WAVES_SINGLE;
-constexpr int kStreamWavesPair = NVFP4_STREAM_WAVES_PAIR;
+__host__ __device__ constexpr bool control_wave_for_rows(int rows) { return rows <= kWideRowsMax; }
+__host__ __device__ constexpr int streaming_waves_for_rows(int rows) {
+    return max_waves_for_rows(rows) - (control_wave_for_rows(rows) ? 1 : 0);
+}
 
 struct StreamPlan {
     int64_t n, k;
     int rows, nmat;
     int strips, supers;       // S, T
     int G, F, R;              // workgroups, owned strips per workgroup, shared strips
-    int waves;                // waves per workgroup
+    int waves;                // streaming waves per workgroup (plus the control wave, rows <= 4)
     int max_pieces;           // most pieces any shared strip is cut into
-    size_t counter_bytes;     // arrival counters (0 if no strip is cut)
-    size_t partial_bytes;     // fp32 partial sums [R][max_pieces][nmat][rows][64]
+    size_t partial_bytes;     // fp32 partial sums [R][max_pieces][nmat][rows][64] (0 if no strip is cut)
     size_t lds_bytes;
 };
 
+// One projection call of a launch: its plan and operands (w1 = nullptr for a
+// single projection).
+struct StreamCall {
+    StreamPlan plan;
+    const void *w0, *w1, *x;
+    void *y;
+    int out_f32;
+};
+
 StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual);
-hipError_t launch_stream(const StreamPlan &plan, const void *w0, const void *w1, const void *x, void *y,
-                         int out_f32, void *workspace, hipStream_t stream);
+size_t stream_lds_bytes(int rows, int waves);
+// Workspace bytes for these calls run by launch_sequence (one call: what
+// nvfp4_gemv needs; several: the completion counts too).
+size_t sequence_workspace_bytes(const StreamCall *calls, int ncalls);
+// Whether several calls can share one launch on this device (cooperative launch).
+bool cooperative_ok();
+// Run the calls in order on `stream`: runs of calls with the same row count
+// share one launch when cooperative launches are available.
+hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace, hipStream_t stream);
+// Launches launch_sequence makes for these calls.
+int sequence_launches(const StreamCall *calls, int ncalls);
 
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
                        int64_t n, int64_t k, void *packed, hipStream_t stream);

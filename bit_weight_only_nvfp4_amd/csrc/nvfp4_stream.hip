@@ -4,30 +4,40 @@
 // and the gate/up pair o = silu(g) * u (the w4a16_gemv / w4a16_gemv_dual kernel
 // family of the Qwen3.8-27B-NVFP4 blueprint page, "Kernels" table).
 //
-// Decode GEMVs are bound by the HBM weight stream, so the launch is shaped for
-// the stream rather than for the arithmetic:
-//   * at most one workgroup per CU (G <= 256), all resident at once: no second
-//     dispatch round and no per-workgroup start-up in the middle of the stream;
+// One launch runs an ordered list of projection calls (one call for
+// nvfp4_gemv, a decode step's projections for nvfp4_gemv_sequence).  Decode
+// GEMVs are bound by the HBM weight stream, so the launch is shaped for the
+// stream rather than for the arithmetic:
+//   * at most one workgroup per CU (G <= 256), all resident at once (a
+//     cooperative launch when there are several calls);
 //   * every wave runs a two-deep pipeline over its super-tiles (64 features x
 //     256 k): the codes, scales and activation window of super-tile i+1 are in
 //     flight while super-tile i is computed.  The activation window travels
 //     with its weights, so it is never stuck behind other waves' weight loads;
+//   * the pipeline runs across calls: while a call's last tiles are computed
+//     and its results written, the first super-tile of the next call is
+//     already in flight;
 //   * a workgroup owns whole strips of 64 features where it can (no split-K,
 //     no cross-workgroup traffic); the remaining units of work are cut into
-//     balanced pieces of strips ("stream-K").  A workgroup processes its pieces
-//     first, so their publish / last-arrival handshake overlaps the rest of the
-//     stream, and finishes with the strips it owns outright;
+//     balanced pieces of strips ("stream-K");
 //   * pieces of a strip are summed in piece order by the last to arrive (an
 //     arrival counter), so results are bitwise deterministic with no float
-//     atomics.  Partials and counters are accessed only with device-scope
-//     atomics (sc1), ordered by explicit waits -- no cache-wide flushes.
+//     atomics, and identical whether a call runs alone or in a sequence;
+//   * calls run in order: a call starts computing only after every workgroup
+//     has finished the previous one (a completion count per launch), so a call
+//     may read an earlier call's output as its activations.
+// Everything one workgroup writes to global memory -- outputs, partial sums,
+// counters -- is written by its wave 0 with device-coherent (sc1) accesses, and
+// wave 0 is the only wave with no loads in flight across a call boundary, so it
+// can wait for its own writes to complete before it counts the call done
+// without waiting for the other waves' next weight loads.  Activations are read
+// with device-coherent loads as well.  No cache-wide flushes.
 //
-// Work units: strip s in [0, S) x super-tile u in [0, T).  G workgroups; the
-// first G*F strips are owned, F per workgroup; the R = S - G*F remaining
-// strips form R*T shared units split into G contiguous ranges
+// Work units of a call: strip s in [0, S) x super-tile u in [0, T).  G
+// workgroups; the first G*F strips are owned, F per workgroup; the R = S - G*F
+// remaining strips form R*T shared units split into G contiguous ranges
 // [g*RT/G, (g+1)*RT/G), cut at strip boundaries into pieces.
 #include <atomic>
-#include <type_traits>
 
 #include "nvfp4_core.h"
 
@@ -35,18 +45,41 @@ namespace nvfp4 {
 namespace {
 using namespace core;
 
-struct StreamArgs {
+// One call of a launch.
+struct CallDesc {
     const uint8_t *w0;    // packed weight (gate of the pair)
-    const uint8_t *w1;    // packed up weight (pair only)
-    const uint16_t *x;    // [ROWS][k] bf16
-    void *y;              // [ROWS][n]
-    float *partial;       // [R][max_pieces][NMAT][ROWS][64]
-    unsigned *counters;   // [R]
+    const uint8_t *w1;    // packed up weight of a pair; w0 otherwise
+    const uint16_t *x;    // [rows][k] bf16
+    void *y;              // [rows][n]
     int n, k, T;
-    int G, F, R;
+    int G, F, R;          // workgroups taking part, owned strips each, shared strips
     int max_pieces;
-    int out_f32;
+    int waves;            // waves taking part
+    int flags;            // kPair | kOutF32 | kReloadX
+    int pad;
 };
+constexpr int kPair = 1, kOutF32 = 2;
+// x is written by the call before this one in the same launch: the activations
+// of a super-tile fetched before the call started are fetched again.
+constexpr int kReloadX = 4;
+constexpr int kSeqMax = 40;   // calls per launch (the kernel arguments stay below 4 KB)
+
+struct SeqArgs {
+    CallDesc call[kSeqMax];
+    float *partial;       // [R][max_pieces][nmat][rows][64] of the call running
+    unsigned *counters;   // arrival count of shared strip sh at word 32 sh (one 128-byte line each)
+    unsigned *sync;       // word 32 g: the last call workgroup g may go past (one 128-byte line each)
+    unsigned *flags;      // word 0: a wait between calls timed out; 32: arrivals; 64: workgroups exited
+    int ncalls;
+    int G;                // workgroups of the launch
+};
+static_assert(sizeof(SeqArgs) <= 3072, "kernel arguments must stay small");
+static_assert(sizeof(CallDesc) % 4 == 0, "call descriptors are copied as words");
+
+constexpr int kSC1 = 16;                          // cache policy: device-coherent access
+constexpr int kDroppedOffset = 0x7fffffff;        // past any buffer: loads read 0, stores are dropped
+constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit data format
+constexpr uint64_t kWaitTicks = 20000000;         // 0.2 s of the 100 MHz real-time clock
 
 // Workgroup whose shared range [floor(g*U/G), floor((g+1)*U/G)) holds shared
 // unit v: the largest g with g*U < (v+1)*G, i.e. ((v+1)*G - 1) / U.
@@ -63,6 +96,10 @@ __device__ __forceinline__ uint4 load_nt(const uint8_t *p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
 // One super-tile of one matrix in registers: its 8 KB of codes as 8 wave-wide
 // 1 KB loads (lane l: bytes 16 l of each KB), the scale entry of the lane and
 // this lane's chunks of the activation window.
@@ -74,80 +111,99 @@ struct Tile {
     uint4 xv[XR];
 };
 
-// Issue the loads of super-tile u of strip s of matrix w (with its activation
-// window when WITH_X).  With real == false the same loads read an always-valid
-// location (the weight's first super-tile, the header's zero bytes), so the
-// number of loads in flight never depends on control flow and the compiler can
-// count them exactly; those results are never used.
+// Where a super-tile's loads read from.  A dummy (real == false) reads the
+// packed header's zero bytes and no activations, so the number of loads in
+// flight never depends on control flow and the compiler can count them
+// exactly; its contents are never used, or used with zero scales.
+struct TileSrc {
+    const uint8_t *base;            // the super-tile, or the zero bytes
+    __amdgpu_buffer_rsrc_t xr;      // the call's activations
+    int kbase, k;
+    bool real;                      // weights: the super-tile's, else the zero bytes
+    bool xreal;                     // activations: the window's, else zeros
+};
+
+// This lane's chunks of the activation window: chunk c = lane + 64 i is row
+// c / 32, k = kbase + 8 (c % 32) .. + 7.  Chunks past the activations read
+// zeros (out-of-range buffer loads): always issued, never masked afterwards.
+template <int ROWS>
+__device__ __forceinline__ void load_x(const TileSrc &t, int lane, uint4 (&xv)[Tile<ROWS>::XR]) {
+#pragma unroll
+    for (int i = 0; i < Tile<ROWS>::XR; ++i) {
+        const int c = lane + 64 * i;
+        const int r = c >> 5, kk = (c & 31) * 8;
+        const bool in = t.xreal && r < ROWS && t.kbase + kk < t.k;
+        const int off = in ? (r * t.k + t.kbase + kk) * 2 : kDroppedOffset;
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(t.xr, off, 0, kSC1);
+        xv[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+}
+
 template <int ROWS, bool WITH_X>
-__device__ __forceinline__ void load_tile(const StreamArgs &a, const uint8_t *w, int s, int u, bool real,
-                                          int lane, Tile<ROWS> &b) {
-    const size_t off = real ? ((size_t)s * a.T + u) * kSuperBytes : 0;
-    const uint8_t *base = w + kHeaderBytes + off;
+__device__ __forceinline__ void load_tile(const TileSrc &t, const uint8_t *zero, int lane, Tile<ROWS> &b) {
     // the activation window first: it is consumed first (staged into LDS)
     // and, issued first, it can be waited for while the codes are in flight
     if (WITH_X) {
-        const int kbase = u * kSuperK;
-#pragma unroll
-        for (int i = 0; i < Tile<ROWS>::XR; ++i) {
-            const int c = lane + 64 * i;
-            const int r = c >> 5, kk = (c & 31) * 8;
-            const bool in = real && r < ROWS && kbase + kk < a.k;
-            // chunks past the activations read 16 zero bytes from the packed
-            // header's padding instead: always issued, never masked afterwards
-            // (both addresses are formed, then one is selected: no branch)
-            const uint8_t *xp = reinterpret_cast<const uint8_t *>(a.x + (size_t)min(r, ROWS - 1) * a.k + kbase + kk);
-            const uint8_t *src = in ? xp : a.w0 + kHeaderZeroOffset;
-            b.xv[i] = *reinterpret_cast<const uint4 *>(src);
-        }
+        load_x<ROWS>(t, lane, b.xv);
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int l = 0; l < kCodeChunks / 2; ++l) b.wc[l] = load_nt(base + l * 2 * kCodeChunkBytes + lane * 16);
-    b.ws = load_nt(base + kScaleOffset + lane * 16);
+    for (int l = 0; l < kCodeChunks / 2; ++l)
+        b.wc[l] = load_nt(t.real ? t.base + l * 2 * kCodeChunkBytes + lane * 16 : zero);
+    b.ws = load_nt(t.real ? t.base + kScaleOffset + lane * 16 : zero);
     // keep the whole tile's loads ahead of what follows (the scheduler would
     // otherwise sink them into the previous tile's arithmetic, after its wait)
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Buffer resource over the outputs: stores at an offset past its size are
-// dropped by the hardware, which masks the lanes past the last feature without
-// a branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t output_rsrc(const StreamArgs &a, int rows) {
-    const int bytes = rows * a.n * (a.out_f32 ? 4 : 2);
-    return __builtin_amdgcn_make_buffer_rsrc(a.y, (short)0, bytes, 0x00020000);
+__device__ __forceinline__ TileSrc pick(bool first, const TileSrc &a, const TileSrc &b) {
+    TileSrc t;
+    t.base = first ? a.base : b.base;
+    t.xr = first ? a.xr : b.xr;
+    t.kbase = first ? a.kbase : b.kbase;
+    t.k = first ? a.k : b.k;
+    t.real = first ? a.real : b.real;
+    t.xreal = first ? a.xreal : b.xreal;
+    return t;
 }
 
-constexpr int kDroppedOffset = 0x7fffffff;
+// Buffer resource over a call's outputs: stores at an offset past its size
+// are dropped by the hardware, which masks the lanes past the last feature
+// without a branch.
+template <int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t output_rsrc(const CallDesc &d) {
+    return rsrc(d.y, (uint32_t)(ROWS * d.n * ((d.flags & kOutF32) ? 4 : 2)));
+}
 
-// Apply the tensor scales (sg[m] of matrix m) and the SiLU product, and store
-// row r of a strip's outputs.
-template <int ROWS, int NMAT>
-__device__ __forceinline__ void epilogue(const StreamArgs &a, __amdgpu_buffer_rsrc_t yr, const float *red,
-                                         const float (&sg)[NMAT], int s, int r, int lane) {
+template <int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const CallDesc &d) {
+    return rsrc(d.x, (uint32_t)(ROWS * d.k * 2));
+}
+
+// Apply the tensor scales and the SiLU product (pair) to the strip sums g, u
+// of row r and store the row's outputs of strip s.
+template <int ROWS>
+__device__ __forceinline__ void epilogue(const CallDesc &d, __amdgpu_buffer_rsrc_t yr, float g, float u,
+                                         const float (&sg)[2], int s, int r, int lane) {
     const int f = s * kStripN + lane;
-    float out;
-    if (NMAT == 1) {
-        out = red[r * kStripN + lane] * sg[0];
-    } else {
-        const float g = red[r * kStripN + lane] * sg[0];
-        const float u = red[(ROWS + r) * kStripN + lane] * sg[NMAT - 1];
-        out = g / (1.0f + expf(-g)) * u;
-    }
-    const int at = r * a.n + f;
-    if (a.out_f32)
+    const float gs = g * sg[0];
+    const float out = (d.flags & kPair) ? gs / (1.0f + expf(-gs)) * (u * sg[1]) : gs;
+    const int at = r * d.n + f;
+    if (d.flags & kOutF32)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), yr,
-                                              f < a.n ? at * 4 : kDroppedOffset, 0, 0);
+                                              f < d.n ? at * 4 : kDroppedOffset, 0, kSC1);
     else
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(out), yr, f < a.n ? at * 2 : kDroppedOffset, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(out), yr, f < d.n ? at * 2 : kDroppedOffset, 0,
+                                              kSC1);
 }
 
-// The work of workgroup g as one sequence of super-tiles, in segments: first
-// its shared range [su0, su1) of the R*T shared units, cut at strip
-// boundaries (nsh segments), then its F owned strips.  Every quantity here
-// derives from kernel arguments and the workgroup index only, so the compiler
-// keeps it, and every branch on it, on the scalar unit.
+// The work of workgroup g in one call as one sequence of super-tiles, in
+// segments: first its F owned strips, then its shared range [su0, su1) of the
+// R*T shared units, cut at strip boundaries (nsh segments).  Every quantity
+// here derives from kernel arguments and the workgroup index only, so the
+// compiler keeps it, and every branch on it, on the scalar unit.
 struct Geometry {
-    int g, su0, su1, fs, nsh, nseg, total;
+    int su0, su1, fs, nsh, nseg, total;
     // A shared range never exceeds one strip's T super-tiles, so it touches at
     // most two shared strips: fs, whose pieces may start in an earlier
     // workgroup (this one is piece `piece0` of `np0`), and fs + 1, which
@@ -155,22 +211,31 @@ struct Geometry {
     int piece0, np0, np1;
 };
 
-__device__ __forceinline__ Geometry make_geometry(const StreamArgs &a) {
+// Owner of shared unit v, in 32-bit arithmetic: v < U = R*T < 2^24 (R < 256,
+// T <= 2^16) and G <= 256, so (v + 1) * G < 2^32.
+__device__ __forceinline__ int owner_wg32(uint32_t v, uint32_t U, uint32_t G) {
+    return (int)(((v + 1u) * G - 1u) / U);
+}
+
+__device__ __forceinline__ Geometry make_geometry(const CallDesc &d, int g) {
     Geometry q;
-    q.g = blockIdx.x;
-    const long long U = (long long)a.R * a.T;
-    q.su0 = (int)((long long)q.g * U / a.G);
-    q.su1 = (int)((long long)(q.g + 1) * U / a.G);
-    q.fs = q.su1 > q.su0 ? q.su0 / a.T : 0;
-    q.nsh = q.su1 > q.su0 ? (q.su1 - 1) / a.T - q.fs + 1 : 0;
-    q.nseg = q.nsh + a.F;
-    q.total = (q.su1 - q.su0) + a.F * a.T;
+    q.su0 = q.su1 = q.fs = q.nsh = q.nseg = q.total = 0;
     q.piece0 = q.np0 = q.np1 = 1;
+    if (g >= d.G) return q;   // not taking part in this call
+    // g * U and (g + 1) * U stay below 256 * 2^24 = 2^32
+    const uint32_t U = (uint32_t)d.R * (uint32_t)d.T, G = (uint32_t)d.G, T = (uint32_t)d.T;
+    q.su0 = (int)((uint32_t)g * U / G);
+    q.su1 = (int)((uint32_t)(g + 1) * U / G);
+    q.fs = q.su1 > q.su0 ? (int)((uint32_t)q.su0 / T) : 0;
+    q.nsh = q.su1 > q.su0 ? (int)((uint32_t)(q.su1 - 1) / T) - q.fs + 1 : 0;
+    q.nseg = d.F + q.nsh;
+    q.total = d.F * d.T + (q.su1 - q.su0);
     if (q.nsh > 0) {
-        const int first = owner_wg((long long)q.fs * a.T, U, a.G);
-        q.piece0 = q.g - first;
-        q.np0 = owner_wg((long long)(q.fs + 1) * a.T - 1, U, a.G) - first + 1;
-        q.np1 = owner_wg((long long)(q.fs + 2) * a.T - 1, U, a.G) - q.g + 1;
+        const int first = owner_wg32((uint32_t)q.fs * T, U, G);
+        q.piece0 = g - first;
+        q.np0 = owner_wg32((uint32_t)(q.fs + 1) * T - 1u, U, G) - first + 1;
+        // strip fs + 1 (used only when this range reaches it, i.e. fs + 1 < R)
+        q.np1 = owner_wg32(min((uint32_t)(q.fs + 2) * T - 1u, U - 1u), U, G) - g + 1;
     }
     return q;
 }
@@ -180,291 +245,469 @@ struct Cursor {
     int k, start, end, strip, u0;
 };
 
-// Segment order within a workgroup's sequence: its shared pieces before or
-// after its owned strips.
-#ifndef NVFP4_SHARED_FIRST
-#define NVFP4_SHARED_FIRST 0
-#endif
-constexpr bool kSharedFirst = NVFP4_SHARED_FIRST != 0;
-
 // Shared-strip index of segment k, or -1 for an owned strip.
-__device__ __forceinline__ int segment_shared(const StreamArgs &a, const Geometry &q, int k) {
-    if (kSharedFirst) return k < q.nsh ? q.fs + k : -1;
-    return k >= a.F ? q.fs + (k - a.F) : -1;
+__device__ __forceinline__ int segment_shared(const CallDesc &d, const Geometry &q, int k) {
+    return k >= d.F ? q.fs + (k - d.F) : -1;
 }
 
-// Index among the workgroup's owned strips of an owned segment k.
-__device__ __forceinline__ int segment_owned(const Geometry &q, int k) {
-    return kSharedFirst ? k - q.nsh : k;
-}
-
-__device__ __forceinline__ Cursor cursor_at(const StreamArgs &a, const Geometry &q, int k) {
-    const int sh = segment_shared(a, q, k);
-    const int f = segment_owned(q, k);
-    const int shared_base = kSharedFirst ? 0 : a.F * a.T;
-    const int owned_base = kSharedFirst ? q.su1 - q.su0 : 0;
-    const int v0 = max(q.su0, sh * a.T), v1 = min(q.su1, (sh + 1) * a.T);
+__device__ __forceinline__ Cursor cursor_at(const CallDesc &d, const Geometry &q, int g, int k) {
+    const int sh = segment_shared(d, q, k);
+    const int v0 = max(q.su0, sh * d.T), v1 = min(q.su1, (sh + 1) * d.T);
+    const int shared_base = d.F * d.T;
     Cursor c;
     c.k = k;
     const bool live = k < q.nseg, shared = sh >= 0;
-    c.start = !live ? 0x7fffffff : shared ? shared_base + v0 - q.su0 : owned_base + f * a.T;
-    c.end = !live ? 0x7fffffff : shared ? shared_base + v1 - q.su0 : owned_base + (f + 1) * a.T;
-    c.strip = shared ? a.G * a.F + sh : q.g * a.F + f;
-    c.u0 = shared ? v0 - sh * a.T : 0;
+    c.start = !live ? 0x7fffffff : shared ? shared_base + v0 - q.su0 : k * d.T;
+    c.end = !live ? 0x7fffffff : shared ? shared_base + v1 - q.su0 : (k + 1) * d.T;
+    c.strip = shared ? d.G * d.F + sh : g * d.F + k;
+    c.u0 = shared ? v0 - sh * d.T : 0;
     return c;
 }
 
-// Close segment k: reduce the waves' accumulators in wave order, then either
-// write the strip's outputs, or store this piece of a shared strip in the
-// partials and mark it in pub[] (strip fs or fs + 1).  Arrivals are counted,
-// and the last piece's workgroup sums the pieces, once the tile loop is over.
-// Every wave calls this for every segment, in order, and leaves with its
-// accumulators cleared.  Rows r = wave, wave + nwaves, ... are this wave's.
+// Close segment k: reduce the waves' accumulators in wave order; then wave 0
+// either writes the strip's outputs, or stores this piece of a shared strip
+// in the partials and marks it in pub[] (strip fs or fs + 1).  Arrivals are
+// counted, and the last piece's workgroup sums the pieces, once the call's
+// tiles are done.  Every wave calls this for every segment, in order, and
+// leaves with its accumulators cleared.
 //
 // This runs inside the tile loop, so its loops are fully unrolled with
 // wave-uniform guards: a rolled loop or a divergent branch there makes the
 // compiler assume that tile loads may still be in flight at the top of the
 // tile loop, and wait for them.
-template <int ROWS, int NMAT>
-__device__ __forceinline__ void finish_segment(const StreamArgs &a, const Geometry &q, int k, float *red,
-                                               const float (&sg)[NMAT], __amdgpu_buffer_rsrc_t yr,
-                                               int wave, int nwaves, int lane, float (&acc)[NMAT][4][ROWS],
-                                               int (&pub)[2]) {
+template <int ROWS>
+__device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc &d, const Geometry &q, int g,
+                                               int k, float *red, const float (&sg)[2],
+                                               __amdgpu_buffer_rsrc_t yr, int wave, int nwc, int lane,
+                                               float (&acc)[2][4][ROWS], int (&pub)[2]) {
+    const bool pair = d.flags & kPair;
     __syncthreads();   // the previous segment's reads of `red` are done
+    // a pair's accumulators are its gate and up sums; a single projection's
+    // are two halves of its sum (even and odd tiles of the wave)
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int r = 0; r < ROWS; ++r) {
+        float g4[4], u4[4];
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) {
+            g4[fb] = pair ? acc[0][fb][r] : acc[0][fb][r] + acc[1][fb][r];
+            u4[fb] = acc[1][fb][r];
+            acc[0][fb][r] = 0.0f;
+            acc[1][fb][r] = 0.0f;
+        }
+        red[((wave * 2 + 0) * ROWS + r) * kStripN + lane] = core::strip_total(g4, lane);
+        if (pair) red[((wave * 2 + 1) * ROWS + r) * kStripN + lane] = core::strip_total(u4, lane);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float v[2][ROWS];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            const float a4[4] = {acc[m][0][r], acc[m][1][r], acc[m][2][r], acc[m][3][r]};
-            red[((wave * NMAT + m) * ROWS + r) * kStripN + lane] = core::strip_total(a4, lane);
+            float t = 0.0f;
+            if (m == 0 || pair) {
+                // the streaming waves w0, ..., w0 + nwc - 1, in order
+                constexpr int w0 = control_wave_for_rows(ROWS) ? 1 : 0;
+                t = red[((w0 * 2 + m) * ROWS + r) * kStripN + lane];
 #pragma unroll
-            for (int fb = 0; fb < 4; ++fb) acc[m][fb][r] = 0.0f;
-        }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < ROWS; ++t) {
-        const int r = wave + t * nwaves;
-        if (r < ROWS) {
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                float v = red[(m * ROWS + r) * kStripN + lane];
-#pragma unroll
-                for (int w = 1; w < kMaxWavesPerWg; ++w)
-                    if (w < nwaves) v += red[((w * NMAT + m) * ROWS + r) * kStripN + lane];
-                red[(m * ROWS + r) * kStripN + lane] = v;
+                for (int w = w0 + 1; w < kMaxWavesPerWg; ++w)
+                    if (w < w0 + nwc) t += red[((w * 2 + m) * ROWS + r) * kStripN + lane];
             }
+            v[m][r] = t;
         }
-    }
-    const int sh = segment_shared(a, q, k);
+    const int sh = segment_shared(d, q, k);
     const bool head = sh == q.fs;
     const int np = head ? q.np0 : q.np1;
     if (sh >= 0 && np > 1) {
-        const size_t slot = ((size_t)sh * a.max_pieces + (head ? q.piece0 : 0)) * NMAT;
+        const int nmat = pair ? 2 : 1;
+        const size_t slot = ((size_t)sh * d.max_pieces + (head ? q.piece0 : 0)) * nmat;
 #pragma unroll
-        for (int t = 0; t < ROWS; ++t) {
-            const int r = wave + t * nwaves;
-            if (r < ROWS) {
+        for (int m = 0; m < 2; ++m)
+            if (m == 0 || pair)
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-                    __hip_atomic_store(&a.partial[((slot + m) * ROWS + r) * kStripN + lane],
-                                       red[(m * ROWS + r) * kStripN + lane], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        pub[head ? 0 : 1] = 1;   // its arrival is counted after the tile loop
+                for (int r = 0; r < ROWS; ++r)
+                    __hip_atomic_store(&a.partial[((slot + m) * ROWS + r) * kStripN + lane], v[m][r],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pub[head ? 0 : 1] = 1;   // its arrival is counted after the call's tiles
         return;
     }
-    const int strip = sh >= 0 ? a.G * a.F + sh : q.g * a.F + segment_owned(q, k);
+    const int strip = sh >= 0 ? d.G * d.F + sh : g * d.F + k;
 #pragma unroll
-    for (int t = 0; t < ROWS; ++t) {
-        const int r = wave + t * nwaves;
-        if (r < ROWS) epilogue<ROWS, NMAT>(a, yr, red, sg, strip, r, lane);
-    }
+    for (int r = 0; r < ROWS; ++r) epilogue<ROWS>(d, yr, v[0][r], v[1][r], sg, strip, r, lane);
 }
 
-// Sum the pieces of shared strip sh in piece order and write its outputs
-// (done by the workgroup whose piece arrived last), then clear its counter.
-template <int ROWS, int NMAT>
-__device__ __forceinline__ void final_sum(const StreamArgs &a, int sh, int np, float *red, const float (&sg)[NMAT],
-                                          __amdgpu_buffer_rsrc_t yr, int wave, int nwaves, int lane) {
-    __syncthreads();   // earlier reads of `red` are done
+// Wave 0: sum the pieces of shared strip sh in piece order and write its outputs.
+template <int ROWS>
+__device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, int sh, int np,
+                                          const float (&sg)[2], __amdgpu_buffer_rsrc_t yr, int lane) {
+    const bool pair = d.flags & kPair;
+    const int nmat = pair ? 2 : 1;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     constexpr int QB = 8;   // partial loads in flight per matrix before the in-order adds
-    for (int r = wave; r < ROWS; r += nwaves) {
-        float tq[NMAT];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) tq[m] = 0.0f;
+    for (int r = 0; r < ROWS; ++r) {
+        float tq[2] = {0.0f, 0.0f};
         for (int q0 = 0; q0 < np; q0 += QB) {
-            float pv[NMAT][QB];
+            float pv[2][QB];
 #pragma unroll
             for (int j = 0; j < QB; ++j) {
                 const int pq = min(q0 + j, np - 1);
-                const size_t qs = ((size_t)sh * a.max_pieces + pq) * NMAT;
+                const size_t qs = ((size_t)sh * d.max_pieces + pq) * nmat;
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-                    pv[m][j] = __hip_atomic_load(&a.partial[((qs + m) * ROWS + r) * kStripN + lane],
+                for (int m = 0; m < 2; ++m)
+                    pv[m][j] = __hip_atomic_load(&a.partial[((qs + (pair ? m : 0)) * ROWS + r) * kStripN + lane],
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
 #pragma unroll
             for (int j = 0; j < QB; ++j)
                 if (q0 + j < np)
 #pragma unroll
-                    for (int m = 0; m < NMAT; ++m) tq[m] += pv[m][j];
+                    for (int m = 0; m < 2; ++m) tq[m] += pv[m][j];
         }
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) red[(m * ROWS + r) * kStripN + lane] = tq[m];
-        epilogue<ROWS, NMAT>(a, yr, red, sg, a.G * a.F + sh, r, lane);
+        epilogue<ROWS>(d, yr, tq[0], tq[1], sg, d.G * d.F + sh, r, lane);
     }
-    if (wave == 0) __hip_atomic_store(&a.counters[sh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int ROWS, int NMAT>
-__global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void stream_kernel(StreamArgs a) {
+// Wave 0: wait until every earlier write of this wave has completed.  All of
+// them are device-coherent, so completion makes them visible to every CU.
+__device__ __forceinline__ void wait_own_writes() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Counter accesses of wave 0, made by its lane 0 alone (device-scope
+// atomics), with the result broadcast to the wave.  They sit outside the tile
+// loop, where the divergent branch costs nothing.
+__device__ __forceinline__ unsigned lane0_add(unsigned *p, int lane) {
+    unsigned old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (unsigned)__builtin_amdgcn_readfirstlane((int)old);
+}
+
+__device__ __forceinline__ unsigned lane0_load(unsigned *p, int lane) {
+    unsigned v = 0;
+    if (lane == 0) v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (unsigned)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ void lane0_store(unsigned *p, unsigned v, int lane) {
+    if (lane == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 0: count this workgroup's piece of shared strip sh; the workgroup
+// whose count completes it sums the strip and clears the counter.
+template <int ROWS>
+__device__ __forceinline__ void arrive_piece(const SeqArgs &a, const CallDesc &d, int sh, int np,
+                                             const float (&sg)[2], __amdgpu_buffer_rsrc_t yr, int lane) {
+    unsigned *cnt = a.counters + sh * 32;
+    if (lane0_add(cnt, lane) == (unsigned)(np - 1)) {
+        lane0_store(cnt, 0u, lane);
+        final_sum<ROWS>(a, d, sh, np, sg, yr, lane);
+    }
+}
+
+// Wave 0: the wait between calls (epoch e = calls finished so far).  Each
+// workgroup counts itself in one arrival counter once its writes of the call
+// are complete; the workgroup whose count completes epoch e stores e in every
+// workgroup's release word, each in a 128-byte line of its own that only its
+// workgroup polls.  A wait that exceeds kWaitTicks sets a flag and goes on: it
+// never hangs.
+__device__ __forceinline__ void arrive_call(const SeqArgs &a, int g, unsigned e, int lane) {
+    wait_own_writes();
+    if (lane0_add(a.flags + 32, lane) + 1u == e * (unsigned)a.G) {
+#pragma unroll
+        for (int i = 0; i < kMaxWorkgroups / 64; ++i) {
+            const int w = lane + 64 * i;
+            if (w < a.G) __hip_atomic_store(a.sync + w * 32, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+__device__ __forceinline__ void wait_release(const SeqArgs &a, int g, unsigned e, int lane) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool late = false;
+    while (lane0_load(a.sync + g * 32, lane) < e && !late) {
+        __builtin_amdgcn_s_sleep(1);
+        late = __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks;
+    }
+    if (late) lane0_store(a.flags, 1u, lane);
+}
+
+// SEQ: several calls per launch (the cross-call pipeline and the completion
+// counts); without it the launch runs call 0 alone.
+template <int ROWS, bool SEQ>
+__global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ unsigned s_last[2];
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index is uniform across the wave; saying so keeps every loop and
     // branch below on the scalar unit (no exec-masked control flow around loads)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nwaves = blockDim.x >> 6;
+    const int nwb = blockDim.x >> 6;
+    const int g = blockIdx.x;
+    const int sw = control_wave_for_rows(ROWS) ? wave - 1 : wave;   // streaming-wave index, -1: control wave
     using XS = core::XStage<ROWS>;
     static_assert(XS::BYTES == 2304 * ((ROWS + 3) / 4) + 32, "host LDS sizing assumes this staging size");
     uint8_t *xs = smem + (size_t)wave * XS::BYTES;   // this wave's staged activations
-    float *red = reinterpret_cast<float *>(smem + (size_t)nwaves * XS::BYTES);
+    float *red = reinterpret_cast<float *>(smem + (size_t)nwb * XS::BYTES);
     if (lane < 8) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
-    const Geometry q = make_geometry(a);
-    // tensor scales, loaded before any tile so that no later wait is for them
-    float sg[NMAT];
-    sg[0] = *reinterpret_cast<const float *>(a.w0);
-    if (NMAT == 2) sg[NMAT - 1] = *reinterpret_cast<const float *>(a.w1);
-    const __amdgpu_buffer_rsrc_t yr = output_rsrc(a, ROWS);
 
-    // Wave w takes positions w, w + nwaves, ... of the workgroup's sequence,
-    // through all its segments, two deep: the loads of the next super-tile are
-    // in flight while one is computed and while a segment is closed.
-    const int nw = wave < q.total ? (q.total - wave + nwaves - 1) / nwaves : 0;
-    float acc[NMAT][4][ROWS];
+    float acc[2][4][ROWS];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
             for (int r = 0; r < ROWS; ++r) acc[m][fb][r] = 0.0f;
-    int pub[2] = {0, 0};   // pieces of shared strips fs, fs + 1 stored here
-    Cursor lc, cc;   // load cursor (runs ahead) and the segment being accumulated
-    lc = cursor_at(a, q, 0);
-    cc = lc;
+    // The call table, copied into LDS once: reading a call's descriptor from
+    // the kernel arguments at the start of every call costs a cache miss each
+    // time; from LDS it is a few cycles.  The words are wave-uniform.
+    __shared__ CallDesc s_calls[SEQ ? kSeqMax : 1];
+    constexpr int kDescWords = sizeof(CallDesc) / 4;
+    if (SEQ) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.call);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(s_calls);
+        for (int i = tid; i < a.ncalls * kDescWords; i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+    }
+    auto desc = [&](int c) {
+        if (!SEQ) return a.call[0];
+        CallDesc v;
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(&s_calls[c]);
+        uint32_t *o = reinterpret_cast<uint32_t *>(&v);
+#pragma unroll
+        for (int i = 0; i < kDescWords; ++i) o[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)p[i]);
+        return v;
+    };
+
+    // Everything a wave needs to start call k: its descriptor and geometry,
+    // the wave's number of positions, and the sources of its first two items
+    // (the wave's stream of super-tiles in a call, item t: of a single
+    // projection, position sw + t * waves, with its activation window; of a
+    // pair, position sw + (t / 2) * waves, gate (t even, with the window) or
+    // up (t odd); items past the wave's last are dummies).  Prepared one call
+    // ahead, before the wait between calls, so none of it is on the path from
+    // one call's end to the next one's first tile.
+    struct Prep {
+        CallDesc d;
+        Geometry q;
+        int nw;          // this wave's positions
+        bool fetch;      // its first two items are fetched during the call before
+        TileSrc s0, s1;
+    };
+    const int ncalls = SEQ ? a.ncalls : 1;
+    auto prepare = [&](int k) {
+        Prep p;
+        const bool live = k < ncalls;
+        p.d = desc(live ? k : ncalls - 1);
+        const CallDesc &d = p.d;
+        p.q = make_geometry(d, live ? g : kMaxWorkgroups);
+        const Geometry &q = p.q;
+        p.nw = sw >= 0 && sw < d.waves && sw < q.total ? (q.total - sw + d.waves - 1) / d.waves : 0;
+        // wave 0 fetches its own items only once the call has started: it must
+        // have no loads in flight while it waits for its writes
+        p.fetch = wave != 0 && p.nw > 0;
+        const bool pair = d.flags & kPair;
+        Cursor cu = cursor_at(d, q, g, 0);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc<ROWS>(d);
+        auto src_at = [&](const uint8_t *w, int i, bool real, bool xreal) {
+            if (real)
+                while (i >= cu.end) cu = cursor_at(d, q, g, cu.k + 1);
+            TileSrc t;
+            const int u = cu.u0 + (i - cu.start);
+            t.base = w + kHeaderBytes + ((size_t)cu.strip * d.T + u) * kSuperBytes;
+            t.xr = xr;
+            t.kbase = u * kSuperK;
+            t.k = d.k;
+            t.real = real;
+            t.xreal = xreal;
+            return t;
+        };
+        p.s0 = src_at(d.w0, sw, p.fetch, p.fetch);
+        const bool r1 = p.fetch && (pair || p.nw > 1);
+        p.s1 = src_at(pair ? d.w1 : d.w0, pair ? sw : sw + d.waves, r1, r1 && !pair);
+        return p;
+    };
+
     Tile<ROWS> b0, b1;
-    // issue the loads of matrix w at position i (dummy loads past the wave's last tile)
-    auto load_pos = [&](const uint8_t *w, int i, bool real, Tile<ROWS> &b, auto with_x) {
-        if (real)
-            while (i >= lc.end) lc = cursor_at(a, q, lc.k + 1);
-        load_tile<ROWS, decltype(with_x)::value>(a, w, lc.strip, lc.u0 + (i - lc.start), real, lane, b);
-    };
-    // close every segment that ends before position i
-    auto close_before = [&](int i) {
-        while (i >= cc.end) {
-            finish_segment<ROWS, NMAT>(a, q, cc.k, red, sg, yr, wave, nwaves, lane, acc, pub);
-            cc = cursor_at(a, q, cc.k + 1);
+    bool pre = false;   // b0, b1 hold this call's first two super-tiles, fetched during the previous call
+    Prep cur = prepare(0);
+    Prep nxt = prepare(1);
+    for (int c = 0; c < ncalls; ++c) {
+        const CallDesc d = cur.d;
+        const Geometry q = cur.q;
+        const int nw = cur.nw;
+        const bool has_next = SEQ && c + 1 < ncalls;
+        const bool pair = d.flags & kPair;
+        const int nwc = d.waves;
+        const uint8_t *zero = d.w0 + kHeaderZeroOffset;
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc<ROWS>(d);
+        const __amdgpu_buffer_rsrc_t yr = output_rsrc<ROWS>(d);
+        // Tensor scales, from the packed headers: only wave 0 writes results.
+        // The other waves must not load them: a scalar load in flight makes the
+        // wave's next LDS wait also wait for it (one counter counts both).
+        float sg[2] = {0.0f, 0.0f};
+        if (wave == 0) {
+            sg[0] = *reinterpret_cast<const float *>(d.w0);
+            sg[1] = *reinterpret_cast<const float *>(d.w1);
         }
-    };
-    using WithX = std::true_type;
-    using NoX = std::false_type;
-    if (NMAT == 1) {
-        // Two positions per iteration.  A tile's activations are staged into
-        // LDS (their registers freed) before the next tile's loads are issued;
-        // its codes are consumed after.  The wave's tile count is padded to
-        // even with one dummy tile whose scales are zeroed, so both tiles of
-        // every iteration are consumed and the loop has one exit: on the way
-        // back to its head the only loads in flight are those of the next
-        // tile, and no wait is needed before reusing registers.
-        if (nw > 0) {
-            load_pos(a.w0, wave, true, b0, WithX{});
-            for (int j = 0; j < nw; j += 2) {
-                const int i0 = wave + j * nwaves, i1 = i0 + nwaves;
-                const bool r1 = j + 1 < nw, r2 = j + 2 < nw;
-                core::stage_x<ROWS>(b0.xv, xs, lane);
-                load_pos(a.w0, i1, r1, b1, WithX{});
-                close_before(i0);
-                core::core_mx<ROWS>(b0.wc, b0.ws, xs, lane, acc[0]);
-                core::stage_x<ROWS>(b1.xv, xs, lane);
-                load_pos(a.w0, i1 + nwaves, r2, b0, WithX{});
-                if (!r1) b1.ws = make_uint4(0, 0, 0, 0);
-                close_before(i1);   // past the last tile this closes every segment left
-                core::core_mx<ROWS>(b1.wc, b1.ws, xs, lane, acc[0]);
+        // the next call's first two items, fetched while this call ends
+        const bool nreal = nxt.fetch;
+        const TileSrc n0 = nxt.s0, n1 = nxt.s1;
+
+        int pub[2] = {0, 0};   // pieces of shared strips fs, fs + 1 stored here
+        Cursor lc = cursor_at(d, q, g, 0), cc = lc;   // load cursor (runs ahead), segment being accumulated
+        auto item = [&](int t) {
+            const bool up = pair && (t & 1);
+            const int pos = sw + (pair ? t >> 1 : t) * nwc;
+            const bool real = (pair ? t >> 1 : t) < nw;
+            if (real)
+                while (pos >= lc.end) lc = cursor_at(d, q, g, lc.k + 1);
+            TileSrc s;
+            const int u = lc.u0 + (pos - lc.start);
+            s.base = real ? (up ? d.w1 : d.w0) + kHeaderBytes + ((size_t)lc.strip * d.T + u) * kSuperBytes : zero;
+            s.xr = xr;
+            s.kbase = u * kSuperK;
+            s.k = d.k;
+            s.real = real;
+            s.xreal = real && !up;
+            return s;
+        };
+        // close every segment that ends before position i
+        auto close_before = [&](int i) {
+            while (i >= cc.end) {
+                finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, nwc, lane, acc, pub);
+                cc = cursor_at(d, q, g, cc.k + 1);
             }
+        };
+        if (nw > 0) {
+            if (!pre) {
+                load_tile<ROWS, true>(item(0), zero, lane, b0);
+                load_tile<ROWS, true>(item(1), zero, lane, b1);
+            } else if (d.flags & kReloadX) {
+                load_x<ROWS>(item(0), lane, b0.xv);
+                load_x<ROWS>(item(1), lane, b1.xv);
+            }
+            // Items 2j (b0) and 2j + 1 (b1) per iteration, both in flight at the
+            // top; each buffer is refilled with the item two ahead as soon as it
+            // has been consumed, and past the call's last items with the next
+            // call's first two.  A single projection's odd count ends with a
+            // dummy tile whose scales are zeroed.  The loop has one exit, and no
+            // wait at its head other than for the data it consumes.
+            const int iters = pair ? nw : (nw + 1) >> 1;
+            for (int j = 0; j < iters; ++j) {
+                const int t = 2 * j;
+                const int p0 = sw + (pair ? j : t) * nwc, p1 = pair ? p0 : p0 + nwc;
+                const bool r1 = pair || t + 1 < nw;            // b1 holds a real tile
+                const bool more = pair ? j + 1 < nw : t + 2 < nw;   // another iteration follows
+                core::stage_x<ROWS>(b0.xv, xs, lane);
+                close_before(p0);
+                core::core_mx<ROWS>(b0.wc, b0.ws, xs, lane, acc[0]);
+                load_tile<ROWS, true>(pick(more, item(t + 2), n0), zero, lane, b0);
+                if (!pair) core::stage_x<ROWS>(b1.xv, xs, lane);
+                close_before(p1);   // past the last tile this closes every segment left
+                const uint4 ws1 = r1 ? b1.ws : make_uint4(0u, 0u, 0u, 0u);
+                core::core_mx<ROWS>(b1.wc, ws1, xs, lane, acc[1]);
+                load_tile<ROWS, true>(pick(more, item(t + 3), n1), zero, lane, b1);
+            }
+        } else if (nreal) {
+            load_tile<ROWS, true>(n0, zero, lane, b0);
+            load_tile<ROWS, true>(n1, zero, lane, b1);
         }
-    } else {
-        // One position per iteration: the gate super-tile (with the activation
-        // window, staged once) then the up super-tile of the same position,
-        // each in flight while the other is computed.
-        if (nw > 0) {
-            load_pos(a.w0, wave, true, b0, WithX{});
-            for (int j = 0; j < nw; ++j) {
-                const int i0 = wave + j * nwaves;
-                core::stage_x<ROWS>(b0.xv, xs, lane);
-                load_pos(a.w1, i0, true, b1, NoX{});
-                close_before(i0);
-                core::core_mx<ROWS>(b0.wc, b0.ws, xs, lane, acc[0]);
-                load_pos(a.w0, i0 + nwaves, j + 1 < nw, b0, WithX{});
-                core::core_mx<ROWS>(b1.wc, b1.ws, xs, lane, acc[NMAT - 1]);
+        pre = nreal;
+        while (cc.k < q.nseg) {
+            finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, nwc, lane, acc, pub);
+            cc = cursor_at(d, q, g, cc.k + 1);
+        }
+        if (wave == 0) {
+            if (pub[0] | pub[1]) {
+                wait_own_writes();   // the partials are visible before they are counted
+                if (pub[0]) arrive_piece<ROWS>(a, d, q.fs, q.np0, sg, yr, lane);
+                if (pub[1]) arrive_piece<ROWS>(a, d, q.fs + 1, q.np1, sg, yr, lane);
             }
+            if (has_next) arrive_call(a, g, (unsigned)(c + 1), lane);
+        }
+        if (has_next) {
+            // the call after next, prepared while the workgroups finish this one
+            cur = nxt;
+            nxt = prepare(c + 2);
+            if (wave == 0) wait_release(a, g, (unsigned)(c + 1), lane);
+            __syncthreads();   // the next call starts in every wave
         }
     }
-    while (cc.k < q.nseg) {
-        finish_segment<ROWS, NMAT>(a, q, cc.k, red, sg, yr, wave, nwaves, lane, acc, pub);
-        cc = cursor_at(a, q, cc.k + 1);
-    }
-    if (pub[0] | pub[1]) {
-        // Every wave's partial stores have completed (they are in the
-        // device-coherent level) before the arrivals are counted.
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __syncthreads();
-        if (tid == 0) {
-            s_last[0] = pub[0] && __hip_atomic_fetch_add(&a.counters[q.fs], 1u, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(q.np0 - 1);
-            s_last[1] = pub[1] && __hip_atomic_fetch_add(&a.counters[q.fs + 1], 1u, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(q.np1 - 1);
+    if (SEQ && wave == 0) {
+        // Back to zero for the next launch: this workgroup's release word (no
+        // release is stored after the last wait), and, by the last workgroup
+        // out, the arrival and exit counts.
+        wait_own_writes();
+        lane0_store(a.sync + g * 32, 0u, lane);
+        if (lane0_add(a.flags + 64, lane) == (unsigned)(a.G - 1)) {
+            lane0_store(a.flags + 32, 0u, lane);
+            lane0_store(a.flags + 64, 0u, lane);
         }
-        __syncthreads();
-        if (s_last[0]) final_sum<ROWS, NMAT>(a, q.fs, q.np0, red, sg, yr, wave, nwaves, lane);
-        if (s_last[1]) final_sum<ROWS, NMAT>(a, q.fs + 1, q.np1, red, sg, yr, wave, nwaves, lane);
     }
 }
 
-template <int ROWS, int NMAT>
-hipError_t launch_stream_rows(const StreamPlan &pl, const StreamArgs &args, hipStream_t stream) {
-    const void *fn = reinterpret_cast<const void *>(&stream_kernel<ROWS, NMAT>);
+template <int ROWS, bool SEQ>
+hipError_t launch_kernel(const SeqArgs &args, int waves, size_t lds, hipStream_t stream) {
+    const void *fn = reinterpret_cast<const void *>(&seq_kernel<ROWS, SEQ>);
     // dynamic LDS beyond the default limit needs the attribute, set once per instantiation
     static std::atomic<int> lds_set{0};
     if (lds_set.load(std::memory_order_acquire) == 0) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 152 * 1024);
         if (e != hipSuccess) return e;
         lds_set.store(1, std::memory_order_release);
     }
-    StreamArgs a = args;
+    SeqArgs a = args;
     void *kargs[] = {&a};
-    return hipLaunchKernel(fn, dim3((unsigned)pl.G), dim3((unsigned)(64 * pl.waves)), kargs, pl.lds_bytes, stream);
+    const dim3 grid((unsigned)a.G), block((unsigned)(64 * waves));
+    // workgroups that wait for each other must all be resident: a cooperative launch
+    if (SEQ) return hipLaunchCooperativeKernel(fn, grid, block, kargs, (unsigned)lds, stream);
+    return hipLaunchKernel(fn, grid, block, kargs, lds, stream);
 }
 
-template <int NMAT>
-hipError_t launch_stream_nmat(const StreamPlan &pl, const StreamArgs &a, hipStream_t stream) {
-    switch (pl.rows) {
-        case 1: return launch_stream_rows<1, NMAT>(pl, a, stream);
-        case 2: return launch_stream_rows<2, NMAT>(pl, a, stream);
-        case 3: return launch_stream_rows<3, NMAT>(pl, a, stream);
-        case 4: return launch_stream_rows<4, NMAT>(pl, a, stream);
-        case 5: return launch_stream_rows<5, NMAT>(pl, a, stream);
-        case 6: return launch_stream_rows<6, NMAT>(pl, a, stream);
-        case 7: return launch_stream_rows<7, NMAT>(pl, a, stream);
-        case 8: return launch_stream_rows<8, NMAT>(pl, a, stream);
+template <int ROWS>
+hipError_t launch_rows(const SeqArgs &a, int waves, size_t lds, hipStream_t s) {
+    return a.ncalls > 1 ? launch_kernel<ROWS, true>(a, waves, lds, s) : launch_kernel<ROWS, false>(a, waves, lds, s);
+}
+
+hipError_t launch_args(int rows, const SeqArgs &a, int waves, size_t lds, hipStream_t s) {
+    switch (rows) {
+        case 1: return launch_rows<1>(a, waves, lds, s);
+        case 2: return launch_rows<2>(a, waves, lds, s);
+        case 3: return launch_rows<3>(a, waves, lds, s);
+        case 4: return launch_rows<4>(a, waves, lds, s);
+        case 5: return launch_rows<5>(a, waves, lds, s);
+        case 6: return launch_rows<6>(a, waves, lds, s);
+        case 7: return launch_rows<7>(a, waves, lds, s);
+        case 8: return launch_rows<8>(a, waves, lds, s);
         default: return hipErrorInvalidValue;
     }
 }
 
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
 }  // namespace
+
+// Whether this device runs launches whose workgroups wait for each other.
+bool cooperative_ok() {
+    static std::atomic<int> state{-1};
+    int s = state.load(std::memory_order_acquire);
+    if (s < 0) {
+        int dev = 0, coop = 0, cus = 0;
+        s = hipGetDevice(&dev) == hipSuccess &&
+                    hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                    coop != 0 && cus >= kMaxWorkgroups
+                ? 1
+                : 0;
+        state.store(s, std::memory_order_release);
+    }
+    return s == 1;
+}
 
 StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
     StreamPlan pl{};
@@ -489,12 +732,10 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
         pl.F = 0;
     }
     pl.R = S - pl.G * pl.F;
-    // Waves per workgroup: each keeps about two super-tiles in flight, so this
-    // sets the bytes in flight per CU (about 18 KB per wave for one matrix, 36 KB
-    // for the pair) -- enough to cover the memory latency at full bandwidth,
-    // and few enough that the first tiles arrive early.
-    int waves = pl.nmat == 1 ? kStreamWavesSingle : kStreamWavesPair;
-    if (waves > max_waves_for_rows(rows)) waves = max_waves_for_rows(rows);
+    // Streaming waves per workgroup: each keeps two super-tiles in flight
+    // (18 KB), so this sets the bytes in flight per CU -- enough to cover the
+    // memory latency at full bandwidth.
+    int waves = streaming_waves_for_rows(rows);
     const long long per_wg = pl.F * (long long)T + (pl.R ? ((long long)pl.R * T + pl.G - 1) / pl.G : 0);
     if (waves > per_wg) waves = (int)per_wg;
     if (waves < 1) waves = 1;
@@ -507,37 +748,91 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
             if (np > pl.max_pieces) pl.max_pieces = np;
         }
     }
-    if (pl.max_pieces > 1) {
-        pl.counter_bytes = kCounterRegionBytes;
-        pl.partial_bytes = (size_t)pl.R * pl.max_pieces * pl.nmat * rows * kStripN * sizeof(float);
-    }
-    const size_t lds_x = (size_t)pl.waves * (2304 * ((rows + 3) / 4) + 32);   // core::XStage<rows>::BYTES
-    const size_t lds_red = (size_t)pl.waves * pl.nmat * rows * kStripN * sizeof(float);
-    // at least ~81 KB so that no CU ever holds two of these workgroups
-    pl.lds_bytes = lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;
+    if (pl.max_pieces > 1) pl.partial_bytes = (size_t)pl.R * pl.max_pieces * pl.nmat * rows * kStripN * sizeof(float);
+    pl.lds_bytes = stream_lds_bytes(rows, pl.waves + (control_wave_for_rows(rows) ? 1 : 0));
     return pl;
 }
 
-hipError_t launch_stream(const StreamPlan &pl, const void *w0, const void *w1, const void *x, void *y, int out_f32,
-                         void *workspace, hipStream_t stream) {
-    StreamArgs a{};
-    a.w0 = static_cast<const uint8_t *>(w0);
-    a.w1 = static_cast<const uint8_t *>(w1);
-    a.x = static_cast<const uint16_t *>(x);
-    a.y = y;
-    a.counters = static_cast<unsigned *>(workspace);
-    a.partial = pl.max_pieces > 1
-                    ? reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.counter_bytes)
-                    : nullptr;
-    a.n = (int)pl.n;
-    a.k = (int)pl.k;
-    a.T = pl.supers;
-    a.G = pl.G;
-    a.F = pl.F;
-    a.R = pl.R;
-    a.max_pieces = pl.max_pieces;
-    a.out_f32 = out_f32;
-    return pl.nmat == 2 ? launch_stream_nmat<2>(pl, a, stream) : launch_stream_nmat<1>(pl, a, stream);
+size_t stream_lds_bytes(int rows, int waves) {
+    const size_t lds_x = (size_t)waves * (2304 * ((rows + 3) / 4) + 32);   // core::XStage<rows>::BYTES
+    const size_t lds_red = (size_t)waves * 2 * rows * kStripN * sizeof(float);
+    // at least ~81 KB so that no CU ever holds two of these workgroups
+    return lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;
+}
+
+size_t sequence_workspace_bytes(const StreamCall *calls, int ncalls) {
+    size_t partial = 0;
+    for (int i = 0; i < ncalls; ++i)
+        if (calls[i].plan.partial_bytes > partial) partial = calls[i].plan.partial_bytes;
+    // several calls in one launch keep their waits in the sync region
+    if (ncalls > 1 || partial > 0) return kPartialOffset + partial;
+    return 0;
+}
+
+namespace {
+// End of the launch that starts at call i0: a run of calls with the same row
+// count, cut into launches of at most kSeqMax calls, as equal as possible.
+int launch_end(const StreamCall *calls, int ncalls, int i0, bool shared) {
+    if (!shared) return i0 + 1;
+    int run = i0 + 1;
+    while (run < ncalls && calls[run].plan.rows == calls[i0].plan.rows) ++run;
+    const int left = run - i0, parts = (left + kSeqMax - 1) / kSeqMax;
+    return i0 + (left + parts - 1) / parts;
+}
+}  // namespace
+
+int sequence_launches(const StreamCall *calls, int ncalls) {
+    const bool shared = ncalls > 1 && cooperative_ok();
+    int n = 0;
+    for (int i0 = 0; i0 < ncalls; i0 = launch_end(calls, ncalls, i0, shared)) ++n;
+    return n;
+}
+
+hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace, hipStream_t stream) {
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const bool shared = ncalls > 1 && cooperative_ok();
+    for (int i0 = 0; i0 < ncalls;) {
+        const int i1 = launch_end(calls, ncalls, i0, shared);
+        const int rows = calls[i0].plan.rows;
+        SeqArgs a{};
+        a.ncalls = i1 - i0;
+        a.counters = reinterpret_cast<unsigned *>(ws);
+        a.sync = ws ? reinterpret_cast<unsigned *>(ws + kSyncOffset) : nullptr;
+        a.flags = ws ? reinterpret_cast<unsigned *>(ws + kFlagOffset) : nullptr;
+        a.partial = ws ? reinterpret_cast<float *>(ws + kPartialOffset) : nullptr;
+        int G = 1, waves = 1;
+        for (int i = i0; i < i1; ++i) {
+            const StreamCall &sc = calls[i];
+            const StreamPlan &pl = sc.plan;
+            CallDesc &d = a.call[i - i0];
+            d.w0 = static_cast<const uint8_t *>(sc.w0);
+            d.w1 = static_cast<const uint8_t *>(sc.w1 ? sc.w1 : sc.w0);
+            d.x = static_cast<const uint16_t *>(sc.x);
+            d.y = sc.y;
+            d.n = (int)pl.n;
+            d.k = (int)pl.k;
+            d.T = pl.supers;
+            d.G = pl.G;
+            d.F = pl.F;
+            d.R = pl.R;
+            d.max_pieces = pl.max_pieces;
+            d.waves = pl.waves;
+            d.flags = (pl.nmat == 2 ? kPair : 0) | (sc.out_f32 ? kOutF32 : 0);
+            if (i > i0) {
+                const StreamCall &p = calls[i - 1];
+                const size_t ybytes = (size_t)p.plan.rows * p.plan.n * (p.out_f32 ? 4 : 2);
+                if (ranges_overlap(sc.x, (size_t)rows * pl.k * 2, p.y, ybytes)) d.flags |= kReloadX;
+            }
+            if (pl.G > G) G = pl.G;
+            const int block = pl.waves + (control_wave_for_rows(rows) ? 1 : 0);
+            if (block > waves) waves = block;
+        }
+        a.G = G;
+        hipError_t e = launch_args(rows, a, waves, stream_lds_bytes(rows, waves), stream);
+        if (e != hipSuccess) return e;
+        i0 = i1;
+    }
+    return hipSuccess;
 }
 
 }  // namespace nvfp4

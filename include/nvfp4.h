@@ -74,7 +74,8 @@ enum {
     NVFP4_E_WORKSPACE = -6, /* workspace missing or smaller than required      */
     NVFP4_E_LAYOUT = -7,    /* nvfp4_weight magic/version/size mismatch        */
     NVFP4_E_DEVICE = -8,    /* no HIP device, or not gfx950                    */
-    NVFP4_E_HIP = -9        /* a HIP runtime call or launch failed             */
+    NVFP4_E_HIP = -9,       /* a HIP runtime call or launch failed             */
+    NVFP4_E_OVERLAP = -10   /* an output overlaps an input or the workspace    */
 };
 
 enum { NVFP4_OUT_BF16 = 0, NVFP4_OUT_F32 = 1 };
@@ -135,20 +136,21 @@ int nvfp4_quantize(const float *W, int64_t n, int64_t k, void *packed, size_t pa
                    void *workspace, size_t workspace_bytes, nvfp4_weight *out, void *stream);
 
 /* Workspace needed by nvfp4_gemv (dual = 0) or nvfp4_gemv_dual_silu (dual = 1)
- * for this shape and row count: split-K partial sums plus per-strip arrival
- * counters.  0 means none.  Deterministic in (n, k, rows, dual). */
+ * for this shape and row count: split-K partial sums plus arrival counters.
+ * 0 means none.  Deterministic in (n, k, rows, dual). */
 size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual);
 
 /* y[r][j] = s_g * sum_k (code * scale)[j][k] * x[r][k]  for r < rows, j < n.
  * x: device bf16 [rows][k], 16-byte aligned.  y: device [rows][n], bf16
  * (NVFP4_OUT_BF16, round to nearest even) or fp32 (NVFP4_OUT_F32), aligned
- * to its element size; y must not overlap x, the weight or the workspace.
- * fp32 accumulation; results are bitwise deterministic run to run.
+ * to its element size; y must not overlap x, the weight or the workspace
+ * (NVFP4_E_OVERLAP).  fp32 accumulation; results are bitwise deterministic
+ * run to run.
  * workspace: >= nvfp4_workspace_bytes(n, k, rows, 0) bytes, 16-byte aligned,
- * ZERO-FILLED before its first use.  Its first 64 KiB hold per-strip arrival
- * counters at fixed positions and every call returns them to zero, so one
- * workspace serves any sequence of calls of any shape on one stream; calls
- * that may run concurrently need distinct workspaces. */
+ * ZERO-FILLED before its first use.  Its first 65 KiB hold counters at fixed
+ * positions and every call returns them to zero, so one workspace serves any
+ * sequence of calls of any shape on one stream; calls that may run
+ * concurrently need distinct workspaces. */
 int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype,
                void *workspace, size_t workspace_bytes, void *stream);
 
@@ -172,23 +174,33 @@ typedef struct nvfp4_call {
     int out_dtype;           /* NVFP4_OUT_BF16 or NVFP4_OUT_F32                    */
 } nvfp4_call;
 
-/* Workspace for nvfp4_gemv_sequence: the largest any of its calls needs. */
+/* Workspace for nvfp4_gemv_sequence: the largest partial sums any of its
+ * calls needs, plus the counters (65 KiB) when ncalls > 1. */
 size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
 
 /* Enqueue a whole decode step's projections with one host call: every call is
  * validated first (nothing is launched if any is invalid; the message names
- * the failing call's index), then the calls are launched in order on `stream`,
- * each exactly as nvfp4_gemv / nvfp4_gemv_dual_silu would, sharing the one
- * workspace (same-stream order makes that safe).  The pages drive a decode step
- * of several hundred launches as one captured graph (kern README, "decode"
- * programs; the NVFP4 blueprint's 755 launches per step); this is the
- * graph-free equivalent, and it is itself capturable.  A call may read the y
- * of an earlier call as its x.
- * events: NULL, or 2*ncalls hipEvent_t handles (entries may be NULL);
- * events[2i] is recorded on `stream` right before call i and events[2i+1]
- * right after it, for per-launch device timing. */
+ * the failing call's index), then the calls run in order on `stream`, each
+ * computing exactly what nvfp4_gemv / nvfp4_gemv_dual_silu would (bit for
+ * bit), sharing the one workspace.  The pages drive a decode step of several
+ * hundred launches as one captured graph (kern README, "decode" programs; the
+ * NVFP4 blueprint's 755 launches per step); here runs of up to 40 consecutive
+ * calls with the same row count share one cooperative launch whose
+ * workgroups finish each call before any starts computing the next (the next
+ * call's first weight tiles are fetched meanwhile), so a call may read the y
+ * of an earlier call as its x.  No call's y may overlap any call's weight,
+ * its own x or the workspace (NVFP4_E_OVERLAP).
+ * events: NULL, or 2*ncalls hipEvent_t handles (entries may be NULL); with
+ * events every call gets a launch of its own, events[2i] is recorded on
+ * `stream` right before call i and events[2i+1] right after it, for
+ * per-launch device timing. */
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
                         void *const *events, void *stream);
+
+/* Number of kernel launches nvfp4_gemv_sequence makes for these calls without
+ * events on the current device (one per call where shared launches are not
+ * available); 0 if ncalls <= 0 or calls is NULL. */
+int nvfp4_sequence_launches(const nvfp4_call *calls, int ncalls);
 
 #ifdef __cplusplus
 }

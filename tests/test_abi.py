@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(nv):
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     L = ctypes.CDLL(nv.LIB_PATH)
     for name in names:
         assert hasattr(L, name), name
@@ -70,7 +70,10 @@ def test_workspace_bytes(nv):
     assert nv.nvfp4_quantize_workspace_bytes(256, 20) == 0
 
 
-FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
+FAKE = 0x10000      # 64 KiB-aligned addresses that are never dereferenced:
+XF = 0x1000000      # weights at FAKE, activations at XF, outputs at YF,
+YF = 0x2000000      # workspaces at WF (16 MiB apart: no two overlap)
+WF = 0x3000000
 
 
 def _weight(nv, n=256, k=512, magic=None, layout=None, data=FAKE):
@@ -81,7 +84,7 @@ def _weight(nv, n=256, k=512, magic=None, layout=None, data=FAKE):
     return w
 
 
-def _gemv(nv, w, x=FAKE, rows=1, y=FAKE, dtype=0, ws=None, wsb=0):
+def _gemv(nv, w, x=XF, rows=1, y=YF, dtype=0, ws=None, wsb=0):
     return nv.lib().nvfp4_gemv(ctypes.byref(w) if w is not None else None, x, rows, y, dtype, ws, wsb, None)
 
 
@@ -100,14 +103,38 @@ def test_gemv_argument_errors(nv):
     assert _gemv(nv, _weight(nv), rows=0) == E["NVFP4_E_ROWS"]
     assert _gemv(nv, _weight(nv), rows=9) == E["NVFP4_E_ROWS"]
     assert _gemv(nv, _weight(nv), dtype=2) == E["NVFP4_E_DTYPE"]
-    assert _gemv(nv, _weight(nv), x=FAKE + 2) == E["NVFP4_E_ALIGN"]
-    assert _gemv(nv, _weight(nv), y=FAKE + 1) == E["NVFP4_E_ALIGN"]
-    assert _gemv(nv, _weight(nv), y=FAKE + 2, dtype=1) == E["NVFP4_E_ALIGN"]
+    assert _gemv(nv, _weight(nv), x=XF + 2) == E["NVFP4_E_ALIGN"]
+    assert _gemv(nv, _weight(nv), y=YF + 1) == E["NVFP4_E_ALIGN"]
+    assert _gemv(nv, _weight(nv), y=YF + 2, dtype=1) == E["NVFP4_E_ALIGN"]
     big = _weight(nv, n=5120, k=17408)
     need = nv.nvfp4_workspace_bytes(5120, 17408, 1)
     assert _gemv(nv, big) == E["NVFP4_E_WORKSPACE"]
-    assert _gemv(nv, big, ws=FAKE, wsb=need - 1) == E["NVFP4_E_WORKSPACE"]
-    assert _gemv(nv, big, ws=FAKE + 4, wsb=need) == E["NVFP4_E_ALIGN"]
+    assert _gemv(nv, big, ws=WF, wsb=need - 1) == E["NVFP4_E_WORKSPACE"]
+    assert _gemv(nv, big, ws=WF + 4, wsb=need) == E["NVFP4_E_ALIGN"]
+
+
+def test_overlap_errors(nv):
+    """An output may not overlap its activations, the weight or the workspace;
+    in a sequence, no output may overlap any call's weight."""
+    E = {v: k for k, v in nv.STATUS.items()}
+    L = nv.lib()
+    w = _weight(nv)                                   # 256 x 512: bytes [FAKE, FAKE + 73984)
+    assert _gemv(nv, w, y=XF) == E["NVFP4_E_OVERLAP"]
+    assert _gemv(nv, w, x=YF + 256) == E["NVFP4_E_OVERLAP"]          # y = [YF, YF + 512)
+    assert _gemv(nv, w, y=FAKE + 73984 - 2) == E["NVFP4_E_OVERLAP"]
+    big = _weight(nv, n=5120, k=17408)
+    need = nv.nvfp4_workspace_bytes(5120, 17408, 1)
+    assert _gemv(nv, big, y=WF + need - 2, ws=WF, wsb=need) == E["NVFP4_E_OVERLAP"]
+    assert "workspace" in nv.nvfp4_last_error()
+    arr = (nv.nvfp4_call * 3)()
+    ws = [_weight(nv, 256, 512, data=FAKE + i * 0x100000) for i in range(3)]
+    for i, c in enumerate(arr):
+        c.w = ctypes.pointer(ws[i])
+        c.x, c.y, c.rows, c.out_dtype = XF, YF + i * 0x10000, 1, 0
+    arr[0].y = FAKE + 2 * 0x100000 + 4096                # into call 2's weight
+    sneed = L.nvfp4_sequence_workspace_bytes(arr, 3)
+    assert L.nvfp4_gemv_sequence(arr, 3, WF, sneed, None, None) == E["NVFP4_E_OVERLAP"]
+    assert "call 0" in nv.nvfp4_last_error() and "call 2" in nv.nvfp4_last_error()
 
 
 def test_dual_and_pack_argument_errors(nv):
@@ -142,7 +169,7 @@ def test_sequence_argument_errors(nv):
     bad = _weight(nv, 256, 512, magic=1)
     for c in arr:
         c.w = ctypes.pointer(good)
-        c.x, c.y, c.rows, c.out_dtype = FAKE, FAKE, 1, 0
+        c.x, c.y, c.rows, c.out_dtype = XF, YF, 1, 0
     assert L.nvfp4_gemv_sequence(arr, 0, None, 0, None, None) == 0       # nothing to do
     arr[2].w = ctypes.pointer(bad)
     assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_LAYOUT"]
@@ -159,8 +186,15 @@ def test_sequence_argument_errors(nv):
     big = _weight(nv, 5120, 17408)
     arr[1].w = ctypes.pointer(big)
     need = L.nvfp4_sequence_workspace_bytes(arr, 3)
+    # the largest partial sums (rows 8 of the 5120 x 17408 call) plus the counters
     assert need == nv.nvfp4_workspace_bytes(5120, 17408, 8)
-    assert L.nvfp4_gemv_sequence(arr, 3, FAKE, need - 16, None, None) == E["NVFP4_E_WORKSPACE"]
+    assert L.nvfp4_gemv_sequence(arr, 3, WF, need - 16, None, None) == E["NVFP4_E_WORKSPACE"]
+    # several calls always need the counters, split-K or not
+    arr[1].w = ctypes.pointer(good)
+    assert L.nvfp4_sequence_workspace_bytes(arr, 3) == 65 * 1024
+    assert L.nvfp4_sequence_workspace_bytes(arr, 1) == 0
+    assert L.nvfp4_sequence_launches(arr, 0) == 0 and L.nvfp4_sequence_launches(None, 3) == 0
+    assert 1 <= L.nvfp4_sequence_launches(arr, 3) <= 3
     assert L.nvfp4_gemv_sequence(None, 3, None, 0, None, None) == E["NVFP4_E_NULL"]
 
 

@@ -386,19 +386,23 @@ def test_sweep_layer_sampled(nv):
 # ---- sequence executor -------------------------------------------------------------
 
 def test_sequence_matches_individual_calls(nv):
-    """A small decode step (qkv, o, gate/up pair, down fed by the pair) through
-    nvfp4_gemv_sequence equals the same calls made one by one, bit for bit, and
-    event handles are recorded around the requested calls."""
+    """A small decode step (qkv, o, gate/up pair, down fed by the pair) for 11
+    layers -- 44 calls, so two launches of the shared-launch executor -- through
+    nvfp4_gemv_sequence equals the same calls made one by one, bit for bit;
+    with event handles every call gets a launch of its own, and the events are
+    recorded around the requested calls.  Afterwards the workspace's counters
+    are back to zero."""
     shapes = {"qkv": (384, 512), "o": (128, 768), "gate": (512, 512), "up": (512, 512), "down": (128, 512)}
     rng = np.random.default_rng(3)
     layers = []
-    for li in range(3):
+    for li in range(11):
         lm = {}
         for name, (n, k) in shapes.items():
             W = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
             lm[name] = _pack(nv, oracle.quantize(W))
         layers.append(lm)
     for rows in (1, 3, 8):
+        print("sequence of 44 small calls, rows=%d" % rows, flush=True)
         x512 = _x_dev(workloads.draw_x(rng, rows, 512))
         x768 = _x_dev(workloads.draw_x(rng, rows, 768))
         outs = [torch.empty((rows, n), dtype=torch.bfloat16 if i % 2 else torch.float32, device="cuda")
@@ -409,7 +413,14 @@ def test_sequence_matches_individual_calls(nv):
             calls += [(lm["qkv"], None, x512, outs[0]), (lm["o"], None, x768, outs[1]),
                       (lm["gate"], lm["up"], x512, pair16), (lm["down"], None, pair16, outs[3])]
         seq = nv.Sequence(calls)
-        ws = torch.zeros(max(seq.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        assert seq.n == 44
+        ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device="cuda")
+        seq.launch(ws)
+        torch.cuda.synchronize()
+        fused = [o.clone() for o in (outs[0], outs[1], pair16, outs[3])]
+        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+        for o in (outs[0], outs[1], pair16, outs[3]):
+            o.zero_()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for e in ev:
             e.record()
@@ -417,7 +428,7 @@ def test_sequence_matches_individual_calls(nv):
         handles[2 * 2], handles[2 * 2 + 1] = ev[0].cuda_event, ev[1].cuda_event
         seq.launch(ws, events=handles)
         torch.cuda.synchronize()
-        got = [o.clone() for o in (outs[0], outs[1], pair16, outs[3])]
+        timed = [o.clone() for o in (outs[0], outs[1], pair16, outs[3])]
         assert ev[0].elapsed_time(ev[1]) >= 0.0
         # one by one
         for lm in layers:
@@ -426,5 +437,81 @@ def test_sequence_matches_individual_calls(nv):
             nv.nvfp4_gemv_dual_silu(lm["gate"], lm["up"], x512, out=pair16, workspace=ws)
             nv.nvfp4_gemv(lm["down"], pair16, out=outs[3], out_dtype=outs[3].dtype, workspace=ws)
         torch.cuda.synchronize()
-        for a, b in zip(got, (outs[0], outs[1], pair16, outs[3])):
+        for a, t, b in zip(fused, timed, (outs[0], outs[1], pair16, outs[3])):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rows
+            assert torch.equal(t.view(torch.uint8), b.view(torch.uint8)), rows
+        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+
+
+def test_sequence_mixed_rows(nv):
+    """Calls with different row counts in one sequence (one launch per run of
+    equal row counts) equal the calls made one by one."""
+    rng = np.random.default_rng(5)
+    w = [_pack(nv, oracle.quantize(rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)))
+         for n, k in ((200, 784), (130, 2064), (640, 1024))]
+    xs = {(r, k): _x_dev(workloads.draw_x(rng, r, k)) for r in (1, 2, 5) for k in (784, 2064, 1024)}
+    plan = [(0, 1), (1, 1), (2, 2), (0, 2), (1, 5), (2, 5), (0, 1)]
+    ks = (784, 2064, 1024)
+    ns = (200, 130, 640)
+    outs = [torch.empty((r, ns[i]), dtype=torch.float32, device="cuda") for i, r in plan]
+    seq = nv.Sequence([(w[i], None, xs[(r, ks[i])], outs[j]) for j, (i, r) in enumerate(plan)])
+    ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device="cuda")
+    seq.launch(ws)
+    torch.cuda.synchronize()
+    for j, (i, r) in enumerate(plan):
+        alone = nv.nvfp4_gemv(w[i], xs[(r, ks[i])], out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(alone.view(torch.int32), outs[j].view(torch.int32)), (j, i, r)
+    assert not bool(ws[:65 * 1024].any())
+
+
+def test_sequence_full_size_decode_step(nv):
+    """Two full-size decode-step layers through one sequence (a shared launch
+    per row count, the weight pipeline running across calls): the last layer's
+    qkv, o and gate/up outputs match the oracle on sampled features; its down
+    projection, fed by the pair's output inside the same launch, equals a
+    launch of its own on that output bit for bit; the counters are back to zero."""
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(78)
+    layers = []
+    for layer in range(2):
+        lm = {}
+        for pi, (name, n, k) in enumerate(workloads.LAYER_PROJECTIONS):
+            Wd = workloads.draw_weights_device(n, k, workloads.sweep_seed(layer, pi), dev)
+            qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+            pw = nv.nvfp4_quantize(Wd, workspace=qws)
+            lm[name] = (pw, oracle.quantize(Wd.cpu().numpy()) if layer == 1 else None)
+            del Wd
+        layers.append(lm)
+    last = layers[1]
+    for rows in (1, 8):
+        print("full-size sequence, rows=%d" % rows, flush=True)
+        xa = workloads.draw_x_device(rows, 5120, 500 + rows, dev)
+        xo = workloads.draw_x_device(rows, 6144, 600 + rows, dev)
+        y_qkv = torch.empty((rows, 12288), dtype=torch.float32, device=dev)
+        y_o = torch.empty((rows, 5120), dtype=torch.float32, device=dev)
+        o32 = torch.empty((rows, 17408), dtype=torch.float32, device=dev)
+        o_gu = torch.empty((rows, 17408), dtype=torch.bfloat16, device=dev)
+        y_down = torch.empty((rows, 5120), dtype=torch.float32, device=dev)
+        calls = []
+        for lm in layers:
+            calls += [(lm["qkv"][0], None, xa, y_qkv), (lm["o"][0], None, xo, y_o),
+                      (lm["gate"][0], lm["up"][0], xa, o32), (lm["gate"][0], lm["up"][0], xa, o_gu),
+                      (lm["down"][0], None, o_gu, y_down)]
+        seq = nv.Sequence(calls)
+        ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device=dev)
+        seq.launch(ws)
+        torch.cuda.synchronize()
+        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+        alone = nv.nvfp4_gemv(last["down"][0], o_gu, out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(alone.view(torch.int32), y_down.view(torch.int32))
+        xab, xob = _bits(xa), _bits(xo)
+        for name, y, xb in (("qkv", y_qkv, xab), ("o", y_o, xob)):
+            sel = np.sort(rng.choice(y.shape[1], 256, replace=False))
+            ref, absd, ref16 = oracle.gemv(*last[name][1], xb, sel=sel)
+            check.check_gemv(y.cpu().numpy()[:, sel], None, ref, absd, ref16,
+                             label="sequence %s r%d" % (name, rows))
+        sel = np.sort(rng.choice(17408, 256, replace=False))
+        d = oracle.gemv_dual_silu(last["gate"][1], last["up"][1], xab, sel=sel)
+        check.check_dual(o32.cpu().numpy()[:, sel], _bits(o_gu)[:, sel], d, label="sequence gate/up r%d" % rows)
