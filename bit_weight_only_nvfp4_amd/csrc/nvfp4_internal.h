@@ -124,23 +124,16 @@ constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workg
 constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
 constexpr int kMaxWavesPerWg = 8;
 // Up to 4 activation rows a wave needs at most 256 registers, so two waves
-// share each SIMD (8 per workgroup): wave 0 is then a control wave (it reduces
-// and writes the results and keeps the order between calls, and has no weight
-// loads in flight), the other 7 stream the weights.  More rows need up to 512
-// registers: one wave per SIMD, all 4 streaming, wave 0 also writing.
+// share each SIMD (8 per workgroup); more rows need up to 512: one per SIMD.
 constexpr int kWideRowsMax = 4;
 __host__ __device__ constexpr int max_waves_for_rows(int rows) { return rows <= kWideRowsMax ? 8 : 4; }
-__host__ __device__ constexpr bool control_wave_for_rows(int rows) { return rows <= kWideRowsMax; }
-__host__ __device__ constexpr int streaming_waves_for_rows(int rows) {
-    return max_waves_for_rows(rows) - (control_wave_for_rows(rows) ? 1 : 0);
-}
 
 struct StreamPlan {
     int64_t n, k;
     int rows, nmat;
     int strips, supers;       // S, T
     int G, F, R;              // workgroups, owned strips per workgroup, shared strips
-    int waves;                // streaming waves per workgroup (plus the control wave, rows <= 4)
+    int waves;                // waves per workgroup taking part in the call
     int max_pieces;           // most pieces any shared strip is cut into
     size_t partial_bytes;     // fp32 partial sums [R][max_pieces][nmat][rows][64] (0 if no strip is cut)
     size_t lds_bytes;

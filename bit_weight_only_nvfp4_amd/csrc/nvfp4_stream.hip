@@ -89,10 +89,15 @@ __host__ __device__ __forceinline__ int owner_wg(long long v, long long U, int G
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+typedef const __attribute__((address_space(1))) u32x4_t *global_u32x4_ptr;
+
 // Streamed-once weight bytes: nontemporal loads keep them from displacing the
-// activations and partials in the caches.
+// activations and partials in the caches.  The pointer is declared global:
+// where the compiler cannot prove it (a pointer carried across calls), it
+// would otherwise emit a flat load, which also counts against the LDS wait
+// counter and makes every later LDS wait wait for the weights.
 __device__ __forceinline__ uint4 load_nt(const uint8_t *p) {
-    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    const u32x4_t t = __builtin_nontemporal_load((global_u32x4_ptr)(p));
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
@@ -278,10 +283,11 @@ __device__ __forceinline__ Cursor cursor_at(const CallDesc &d, const Geometry &q
 template <int ROWS>
 __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc &d, const Geometry &q, int g,
                                                int k, float *red, const float (&sg)[2],
-                                               __amdgpu_buffer_rsrc_t yr, int wave, int nwc, int lane,
+                                               __amdgpu_buffer_rsrc_t yr, int wave, int sw, int nwc, int lane,
                                                float (&acc)[2][4][ROWS], int (&pub)[2]) {
     const bool pair = d.flags & kPair;
     __syncthreads();   // the previous segment's reads of `red` are done
+    // slots in position order (sw): the sums below run in that order
     // a pair's accumulators are its gate and up sums; a single projection's
     // are two halves of its sum (even and odd tiles of the wave)
 #pragma unroll
@@ -294,8 +300,8 @@ __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc 
             acc[0][fb][r] = 0.0f;
             acc[1][fb][r] = 0.0f;
         }
-        red[((wave * 2 + 0) * ROWS + r) * kStripN + lane] = core::strip_total(g4, lane);
-        if (pair) red[((wave * 2 + 1) * ROWS + r) * kStripN + lane] = core::strip_total(u4, lane);
+        red[((sw * 2 + 0) * ROWS + r) * kStripN + lane] = core::strip_total(g4, lane);
+        if (pair) red[((sw * 2 + 1) * ROWS + r) * kStripN + lane] = core::strip_total(u4, lane);
     }
     __syncthreads();
     if (wave != 0) return;
@@ -306,12 +312,10 @@ __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc 
         for (int r = 0; r < ROWS; ++r) {
             float t = 0.0f;
             if (m == 0 || pair) {
-                // the streaming waves w0, ..., w0 + nwc - 1, in order
-                constexpr int w0 = control_wave_for_rows(ROWS) ? 1 : 0;
-                t = red[((w0 * 2 + m) * ROWS + r) * kStripN + lane];
+                t = red[(m * ROWS + r) * kStripN + lane];
 #pragma unroll
-                for (int w = w0 + 1; w < kMaxWavesPerWg; ++w)
-                    if (w < w0 + nwc) t += red[((w * 2 + m) * ROWS + r) * kStripN + lane];
+                for (int w = 1; w < kMaxWavesPerWg; ++w)
+                    if (w < nwc) t += red[((w * 2 + m) * ROWS + r) * kStripN + lane];
             }
             v[m][r] = t;
         }
@@ -445,7 +449,10 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nwb = blockDim.x >> 6;
     const int g = blockIdx.x;
-    const int sw = control_wave_for_rows(ROWS) ? wave - 1 : wave;   // streaming-wave index, -1: control wave
+    // Position order of the waves: wave 0 comes last, so it gets the fewest
+    // super-tiles -- it also reduces and writes every result, and it starts
+    // each call late (it fetches nothing ahead across calls).
+    const int sw = wave == 0 ? nwb - 1 : wave - 1;
     using XS = core::XStage<ROWS>;
     static_assert(XS::BYTES == 2304 * ((ROWS + 3) / 4) + 32, "host LDS sizing assumes this staging size");
     uint8_t *xs = smem + (size_t)wave * XS::BYTES;   // this wave's staged activations
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         const CallDesc &d = p.d;
         p.q = make_geometry(d, live ? g : kMaxWorkgroups);
         const Geometry &q = p.q;
-        p.nw = sw >= 0 && sw < d.waves && sw < q.total ? (q.total - sw + d.waves - 1) / d.waves : 0;
+        p.nw = sw < d.waves && sw < q.total ? (q.total - sw + d.waves - 1) / d.waves : 0;
         // wave 0 fetches its own items only once the call has started: it must
         // have no loads in flight while it waits for its writes
         p.fetch = wave != 0 && p.nw > 0;
@@ -548,8 +555,9 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         // wave's next LDS wait also wait for it (one counter counts both).
         float sg[2] = {0.0f, 0.0f};
         if (wave == 0) {
-            sg[0] = *reinterpret_cast<const float *>(d.w0);
-            sg[1] = *reinterpret_cast<const float *>(d.w1);
+            typedef const __attribute__((address_space(1))) float *global_float_ptr;
+            sg[0] = *(global_float_ptr)(d.w0);
+            sg[1] = *(global_float_ptr)(d.w1);
         }
         // the next call's first two items, fetched while this call ends
         const bool nreal = nxt.fetch;
@@ -576,7 +584,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         // close every segment that ends before position i
         auto close_before = [&](int i) {
             while (i >= cc.end) {
-                finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, nwc, lane, acc, pub);
+                finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
                 cc = cursor_at(d, q, g, cc.k + 1);
             }
         };
@@ -616,7 +624,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         }
         pre = nreal;
         while (cc.k < q.nseg) {
-            finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, nwc, lane, acc, pub);
+            finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
         }
         if (wave == 0) {
@@ -732,10 +740,10 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
         pl.F = 0;
     }
     pl.R = S - pl.G * pl.F;
-    // Streaming waves per workgroup: each keeps two super-tiles in flight
-    // (18 KB), so this sets the bytes in flight per CU -- enough to cover the
-    // memory latency at full bandwidth.
-    int waves = streaming_waves_for_rows(rows);
+    // Waves per workgroup: each keeps two super-tiles in flight (18 KB), so
+    // this sets the bytes in flight per CU -- enough to cover the memory
+    // latency at full bandwidth.
+    int waves = max_waves_for_rows(rows);
     const long long per_wg = pl.F * (long long)T + (pl.R ? ((long long)pl.R * T + pl.G - 1) / pl.G : 0);
     if (waves > per_wg) waves = (int)per_wg;
     if (waves < 1) waves = 1;
@@ -749,7 +757,7 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
         }
     }
     if (pl.max_pieces > 1) pl.partial_bytes = (size_t)pl.R * pl.max_pieces * pl.nmat * rows * kStripN * sizeof(float);
-    pl.lds_bytes = stream_lds_bytes(rows, pl.waves + (control_wave_for_rows(rows) ? 1 : 0));
+    pl.lds_bytes = stream_lds_bytes(rows, pl.waves);
     return pl;
 }
 
@@ -824,8 +832,7 @@ hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace,
                 if (ranges_overlap(sc.x, (size_t)rows * pl.k * 2, p.y, ybytes)) d.flags |= kReloadX;
             }
             if (pl.G > G) G = pl.G;
-            const int block = pl.waves + (control_wave_for_rows(rows) ? 1 : 0);
-            if (block > waves) waves = block;
+            if (pl.waves > waves) waves = pl.waves;
         }
         a.G = G;
         hipError_t e = launch_args(rows, a, waves, stream_lds_bytes(rows, waves), stream);
