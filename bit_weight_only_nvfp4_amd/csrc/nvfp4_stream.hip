@@ -450,8 +450,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     const int nwb = blockDim.x >> 6;
     const int g = blockIdx.x;
     // Position order of the waves: wave 0 comes last, so it gets the fewest
-    // super-tiles -- it also reduces and writes every result, and it starts
-    // each call late (it fetches nothing ahead across calls).
+    // super-tiles -- it also reduces and writes every result.
     const int sw = wave == 0 ? nwb - 1 : wave - 1;
     using XS = core::XStage<ROWS>;
     static_assert(XS::BYTES == 2304 * ((ROWS + 3) / 4) + 32, "host LDS sizing assumes this staging size");
@@ -511,9 +510,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         p.q = make_geometry(d, live ? g : kMaxWorkgroups);
         const Geometry &q = p.q;
         p.nw = sw < d.waves && sw < q.total ? (q.total - sw + d.waves - 1) / d.waves : 0;
-        // wave 0 fetches its own items only once the call has started: it must
-        // have no loads in flight while it waits for its writes
-        p.fetch = wave != 0 && p.nw > 0;
+        p.fetch = p.nw > 0;
         const bool pair = d.flags & kPair;
         Cursor cu = cursor_at(d, q, g, 0);
         const __amdgpu_buffer_rsrc_t xr = x_rsrc<ROWS>(d);
@@ -559,9 +556,12 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             sg[0] = *(global_float_ptr)(d.w0);
             sg[1] = *(global_float_ptr)(d.w1);
         }
-        // the next call's first two items, fetched while this call ends
-        const bool nreal = nxt.fetch;
-        const TileSrc n0 = nxt.s0, n1 = nxt.s1;
+        // The next call's first two items, fetched while this call ends.  Wave
+        // 0 fetches its own only once it has counted this call done: it writes
+        // every result, and waits for its writes to complete first.
+        const bool nreal = nxt.fetch && wave != 0;
+        TileSrc n0 = nxt.s0, n1 = nxt.s1;
+        if (wave == 0) n0.real = n0.xreal = n1.real = n1.xreal = false;
 
         int pub[2] = {0, 0};   // pieces of shared strips fs, fs + 1 stored here
         Cursor lc = cursor_at(d, q, g, 0), cc = lc;   // load cursor (runs ahead), segment being accumulated
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             load_tile<ROWS, true>(n0, zero, lane, b0);
             load_tile<ROWS, true>(n1, zero, lane, b1);
         }
-        pre = nreal;
+        pre = nxt.fetch;
         while (cc.k < q.nseg) {
             finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
@@ -636,6 +636,11 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             if (has_next) arrive_call(a, g, (unsigned)(c + 1), lane);
         }
         if (has_next) {
+            if (wave == 0 && nxt.fetch) {
+                // its writes are complete: its loads in flight delay only its polls
+                load_tile<ROWS, true>(nxt.s0, zero, lane, b0);
+                load_tile<ROWS, true>(nxt.s1, zero, lane, b1);
+            }
             // the call after next, prepared while the workgroups finish this one
             cur = nxt;
             nxt = prepare(c + 2);
@@ -745,6 +750,12 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
     // latency at full bandwidth.
     int waves = max_waves_for_rows(rows);
     const long long per_wg = pl.F * (long long)T + (pl.R ? ((long long)pl.R * T + pl.G - 1) / pl.G : 0);
+    // When the others can take everything two at a time, wave 0 takes no
+    // position: in a sequence each wave's first two super-tiles arrive ahead
+    // of the call, except wave 0's (it writes the results and cannot have
+    // loads in flight while it waits for them), so a position of its own would
+    // be the last to arrive.
+    if (per_wg <= 2 * (waves - 1)) waves -= 1;
     if (waves > per_wg) waves = (int)per_wg;
     if (waves < 1) waves = 1;
     pl.waves = waves;
