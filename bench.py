@@ -229,9 +229,9 @@ def summarize_pmc(fetch_csv, write_csv, launches_per_step):
         return sum(vals) / len(vals), len(vals), keys[0]
 
     pair = lambda k: STEP_KERNEL_TAG in k
-    # the torch copy of --copy-calibration: the only dispatch whose counters exceed 0.9 GiB
-    copy_f = max(v for vals in f.values() for v in vals)
-    copy_w = max(v for vals in w.values() for v in vals)
+    # the 1 GiB device copy of --copy-calibration (the runtime's copy kernel)
+    copy_f = max(v for k, vals in f.items() if "copyBuffer" in k for v in vals)
+    copy_w = max(v for k, vals in w.items() if "copyBuffer" in k for v in vals)
     fetch_factor = COPY_BYTES / (copy_f * 1024.0)
     write_factor = COPY_BYTES / (copy_w * 1024.0)
     pf, n_f, name = pick(f, pair)
