@@ -123,10 +123,19 @@ constexpr int kMaxWorkgroups = 256;      // one per CU on MI355X
 constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workgroup
 constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
 constexpr int kMaxWavesPerWg = 8;
-// Up to 4 activation rows a wave needs at most 256 registers, so two waves
-// share each SIMD (8 per workgroup); more rows need up to 512: one per SIMD.
-constexpr int kWideRowsMax = 4;
-__host__ __device__ constexpr int max_waves_for_rows(int rows) { return rows <= kWideRowsMax ? 8 : 4; }
+// Waves per workgroup and super-tiles each wave keeps in flight (NB, even,
+// so that a pair's gate and up super-tiles of one position are always in
+// flight together).  The super-tiles in flight live in registers.  Two waves
+// per SIMD with two super-tiles each fit in 256 registers at every row count
+// (about 145 at 1 row, 245 at 8), and measured faster than either one wave
+// per SIMD with six in flight or three waves per SIMD with two: the calls of
+// a decode step are short (a few super-tiles per wave), and what a call
+// costs beyond its bytes is latency at its start and end, which more bytes
+// in flight do not shorten.  A wave can have at most 63 vector-memory loads
+// outstanding (a super-tile takes 9 plus one per 64 lanes of activations),
+// which would bound NB at 6 (1-2 rows) or 4 (up to 8 rows).
+__host__ __device__ constexpr int max_waves_for_rows(int rows) { return 8; }
+__host__ __device__ constexpr int pipe_depth_for_rows(int rows) { return 2; }
 
 struct StreamPlan {
     int64_t n, k;

@@ -10,12 +10,13 @@
 // stream rather than for the arithmetic:
 //   * at most one workgroup per CU (G <= 256), all resident at once (a
 //     cooperative launch when there are several calls);
-//   * every wave runs a two-deep pipeline over its super-tiles (64 features x
-//     256 k): the codes, scales and activation window of super-tile i+1 are in
-//     flight while super-tile i is computed.  The activation window travels
-//     with its weights, so it is never stuck behind other waves' weight loads;
+//   * two waves per SIMD, each running a pipeline of NB = 2 super-tiles (64
+//     features x 256 k) in registers: the codes, scales and activation window
+//     of super-tile i+1 are in flight while super-tile i is computed.  The
+//     activation window travels with its weights, so it is never stuck
+//     behind other waves' weight loads;
 //   * the pipeline runs across calls: while a call's last tiles are computed
-//     and its results written, the first super-tile of the next call is
+//     and its results written, the first NB super-tiles of the next call are
 //     already in flight;
 //   * a workgroup owns whole strips of 64 features where it can (no split-K,
 //     no cross-workgroup traffic); the remaining units of work are cut into
@@ -372,6 +373,11 @@ __device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, i
     }
 }
 
+// Wait until every load and store of this wave issued so far has completed.
+__device__ __forceinline__ void wait_all_loads() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited for
+}
+
 // Wave 0: wait until every earlier write of this wave has completed.  All of
 // them are device-coherent, so completion makes them visible to every CU.
 __device__ __forceinline__ void wait_own_writes() {
@@ -487,19 +493,21 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     };
 
     // Everything a wave needs to start call k: its descriptor and geometry,
-    // the wave's number of positions, and the sources of its first two items
+    // the wave's number of positions, and the sources of its first NB items
     // (the wave's stream of super-tiles in a call, item t: of a single
     // projection, position sw + t * waves, with its activation window; of a
     // pair, position sw + (t / 2) * waves, gate (t even, with the window) or
     // up (t odd); items past the wave's last are dummies).  Prepared one call
     // ahead, before the wait between calls, so none of it is on the path from
     // one call's end to the next one's first tile.
+    constexpr int NB = pipe_depth_for_rows(ROWS);
+    static_assert(NB % 2 == 0, "a pair's gate and up super-tiles share a buffer pair");
     struct Prep {
         CallDesc d;
         Geometry q;
         int nw;          // this wave's positions
-        bool fetch;      // its first two items are fetched during the call before
-        TileSrc s0, s1;
+        bool fetch;      // its first NB items are fetched during the call before
+        float sg[2];     // tensor scales (wave 0 only)
     };
     const int ncalls = SEQ ? a.ncalls : 1;
     auto prepare = [&](int k) {
@@ -511,32 +519,53 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         const Geometry &q = p.q;
         p.nw = sw < d.waves && sw < q.total ? (q.total - sw + d.waves - 1) / d.waves : 0;
         p.fetch = p.nw > 0;
-        const bool pair = d.flags & kPair;
-        Cursor cu = cursor_at(d, q, g, 0);
-        const __amdgpu_buffer_rsrc_t xr = x_rsrc<ROWS>(d);
-        auto src_at = [&](const uint8_t *w, int i, bool real, bool xreal) {
-            if (real)
-                while (i >= cu.end) cu = cursor_at(d, q, g, cu.k + 1);
-            TileSrc t;
-            const int u = cu.u0 + (i - cu.start);
-            t.base = w + kHeaderBytes + ((size_t)cu.strip * d.T + u) * kSuperBytes;
-            t.xr = xr;
-            t.kbase = u * kSuperK;
-            t.k = d.k;
-            t.real = real;
-            t.xreal = xreal;
-            return t;
-        };
-        p.s0 = src_at(d.w0, sw, p.fetch, p.fetch);
-        const bool r1 = p.fetch && (pair || p.nw > 1);
-        p.s1 = src_at(pair ? d.w1 : d.w0, pair ? sw : sw + d.waves, r1, r1 && !pair);
+        // Tensor scales from the packed headers, for wave 0, which writes every
+        // result.  Scalar loads, issued a call ahead: a value loaded into a
+        // vector register and used in a loop that stores makes the compiler
+        // wait for every load in flight before entering that loop (which the
+        // segment-closing loops are), and the scalar counter is only waited on
+        // by the next LDS access, long after these have landed.
+        p.sg[0] = p.sg[1] = 0.0f;
+        if (wave == 0) {
+            typedef const __attribute__((address_space(4))) float *const_float_ptr;
+            p.sg[0] = *(const_float_ptr)(uintptr_t)d.w0;
+            p.sg[1] = *(const_float_ptr)(uintptr_t)d.w1;
+        }
         return p;
     };
+    // Item t of prepared call p, for a first fetch (t < NB); `cu` is a cursor
+    // over p's segments that only moves forward, so t must not decrease
+    // between uses of one cursor.  `mine` false makes it a dummy.
+    auto first_item = [&](const Prep &p, Cursor &cu, int t, bool mine) {
+        const CallDesc &d = p.d;
+        const bool pair = d.flags & kPair;
+        const bool real = mine && p.fetch && t < (pair ? 2 * p.nw : p.nw), up = pair && (t & 1);
+        const int i = sw + (pair ? t >> 1 : t) * d.waves;
+        if (real)
+            while (i >= cu.end) cu = cursor_at(d, p.q, g, cu.k + 1);
+        TileSrc s;
+        const int u = cu.u0 + (i - cu.start);
+        s.base = (up ? d.w1 : d.w0) + kHeaderBytes + ((size_t)cu.strip * d.T + u) * kSuperBytes;
+        s.xr = x_rsrc<ROWS>(d);
+        s.kbase = u * kSuperK;
+        s.k = d.k;
+        s.real = real;
+        s.xreal = real && !up;
+        return s;
+    };
 
-    Tile<ROWS> b0, b1;
-    bool pre = false;   // b0, b1 hold this call's first two super-tiles, fetched during the previous call
+    // b[] holds the first NB items of the call about to start: call 0's are
+    // fetched here, every later call's during the call before it (items of a
+    // wave with no positions are dummies, never used)
+    Tile<ROWS> b[NB];
     Prep cur = prepare(0);
     Prep nxt = prepare(1);
+    {
+        Cursor c0 = cursor_at(cur.d, cur.q, g, 0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            load_tile<ROWS, true>(first_item(cur, c0, i, true), cur.d.w0 + kHeaderZeroOffset, lane, b[i]);
+    }
     for (int c = 0; c < ncalls; ++c) {
         const CallDesc d = cur.d;
         const Geometry q = cur.q;
@@ -547,21 +576,12 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         const uint8_t *zero = d.w0 + kHeaderZeroOffset;
         const __amdgpu_buffer_rsrc_t xr = x_rsrc<ROWS>(d);
         const __amdgpu_buffer_rsrc_t yr = output_rsrc<ROWS>(d);
-        // Tensor scales, from the packed headers: only wave 0 writes results.
-        // The other waves must not load them: a scalar load in flight makes the
-        // wave's next LDS wait also wait for it (one counter counts both).
-        float sg[2] = {0.0f, 0.0f};
-        if (wave == 0) {
-            typedef const __attribute__((address_space(1))) float *global_float_ptr;
-            sg[0] = *(global_float_ptr)(d.w0);
-            sg[1] = *(global_float_ptr)(d.w1);
-        }
-        // The next call's first two items, fetched while this call ends.  Wave
+        const float sg[2] = {cur.sg[0], cur.sg[1]};
+        // The next call's first NB items, fetched while this call ends.  Wave
         // 0 fetches its own only once it has counted this call done: it writes
         // every result, and waits for its writes to complete first.
         const bool nreal = nxt.fetch && wave != 0;
-        TileSrc n0 = nxt.s0, n1 = nxt.s1;
-        if (wave == 0) n0.real = n0.xreal = n1.real = n1.xreal = false;
+        const Cursor nc0 = cursor_at(nxt.d, nxt.q, g, 0);
 
         int pub[2] = {0, 0};   // pieces of shared strips fs, fs + 1 stored here
         Cursor lc = cursor_at(d, q, g, 0), cc = lc;   // load cursor (runs ahead), segment being accumulated
@@ -588,41 +608,48 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
                 cc = cursor_at(d, q, g, cc.k + 1);
             }
         };
-        if (nw > 0) {
-            if (!pre) {
-                load_tile<ROWS, true>(item(0), zero, lane, b0);
-                load_tile<ROWS, true>(item(1), zero, lane, b1);
-            } else if (d.flags & kReloadX) {
-                load_x<ROWS>(item(0), lane, b0.xv);
-                load_x<ROWS>(item(1), lane, b1.xv);
-            }
-            // Items 2j (b0) and 2j + 1 (b1) per iteration, both in flight at the
-            // top; each buffer is refilled with the item two ahead as soon as it
-            // has been consumed, and past the call's last items with the next
-            // call's first two.  A single projection's odd count ends with a
-            // dummy tile whose scales are zeroed.  The loop has one exit, and no
-            // wait at its head other than for the data it consumes.
-            const int iters = pair ? nw : (nw + 1) >> 1;
-            for (int j = 0; j < iters; ++j) {
-                const int t = 2 * j;
-                const int p0 = sw + (pair ? j : t) * nwc, p1 = pair ? p0 : p0 + nwc;
-                const bool r1 = pair || t + 1 < nw;            // b1 holds a real tile
-                const bool more = pair ? j + 1 < nw : t + 2 < nw;   // another iteration follows
-                core::stage_x<ROWS>(b0.xv, xs, lane);
-                close_before(p0);
-                core::core_mx<ROWS>(b0.wc, b0.ws, xs, lane, acc[0]);
-                load_tile<ROWS, true>(pick(more, item(t + 2), n0), zero, lane, b0);
-                if (!pair) core::stage_x<ROWS>(b1.xv, xs, lane);
-                close_before(p1);   // past the last tile this closes every segment left
-                const uint4 ws1 = r1 ? b1.ws : make_uint4(0u, 0u, 0u, 0u);
-                core::core_mx<ROWS>(b1.wc, ws1, xs, lane, acc[1]);
-                load_tile<ROWS, true>(pick(more, item(t + 3), n1), zero, lane, b1);
-            }
-        } else if (nreal) {
-            load_tile<ROWS, true>(n0, zero, lane, b0);
-            load_tile<ROWS, true>(n1, zero, lane, b1);
+        if (nw > 0 && (d.flags & kReloadX)) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                if (!pair || !(i & 1)) load_x<ROWS>(item(i), lane, b[i].xv);
         }
-        pre = nxt.fetch;
+        // Items NB j + i (buffer i) per iteration, all NB in flight at the top;
+        // each buffer is refilled with the item NB ahead as soon as it has been
+        // consumed, and past the call's last items with the next call's first
+        // NB.  Items past the wave's last are dummies whose scales are zeroed.
+        // A wave with no positions that fetches for the next call runs one
+        // iteration that only fetches, so that the buffers are written in one
+        // place only -- a second place costs registers at the merge.  The loop has one exit,
+        // and no wait at its head other than for the data it consumes.
+        const int nitems = pair ? 2 * nw : nw;
+        const int iters = nw > 0 ? (nitems + NB - 1) / NB : nreal ? 1 : 0;
+        // Every load issued before the loop has completed here (the first
+        // items arrived during the wait between calls; reloaded activation
+        // windows are cache hits).  Saying so costs little and lets the
+        // compiler count the loop's own loads exactly: otherwise its wait at
+        // the loop head merges the state of the way in, where the first items'
+        // loads are the most recent, and it waits for nearly every load in
+        // flight at the top of every iteration.
+        if (iters > 0) wait_all_loads();
+        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < iters; ++j) {
+            const int t = NB * j;
+            const bool more = j + 1 < iters;   // another iteration follows
+            Cursor nc = nc0;   // over the next call's first items
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int ti = t + i;
+                // a pair's up super-tile uses the window its gate staged; a wave
+                // without positions computes nothing (its buffers may hold
+                // anything, even non-finite activations of an earlier call)
+                if (nw > 0 && (!pair || !(i & 1))) core::stage_x<ROWS>(b[i].xv, xs, lane);
+                // past the last item this closes every segment left
+                close_before(sw + (pair ? ti >> 1 : ti) * nwc);
+                if (nw > 0) core::core_mx<ROWS>(b[i].wc, ti < nitems ? b[i].ws : zero4, xs, lane, acc[i & 1]);
+                load_tile<ROWS, true>(pick(more, item(ti + NB), first_item(nxt, nc, i, wave != 0)), zero, lane,
+                                      b[i]);
+            }
+        }
         while (cc.k < q.nseg) {
             finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
@@ -638,8 +665,9 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         if (has_next) {
             if (wave == 0 && nxt.fetch) {
                 // its writes are complete: its loads in flight delay only its polls
-                load_tile<ROWS, true>(nxt.s0, zero, lane, b0);
-                load_tile<ROWS, true>(nxt.s1, zero, lane, b1);
+                Cursor nc = nc0;
+#pragma unroll
+                for (int i = 0; i < NB; ++i) load_tile<ROWS, true>(first_item(nxt, nc, i, true), zero, lane, b[i]);
             }
             // the call after next, prepared while the workgroups finish this one
             cur = nxt;
@@ -745,17 +773,18 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
         pl.F = 0;
     }
     pl.R = S - pl.G * pl.F;
-    // Waves per workgroup: each keeps two super-tiles in flight (18 KB), so
-    // this sets the bytes in flight per CU -- enough to cover the memory
-    // latency at full bandwidth.
+    // Waves per workgroup: each keeps pipe_depth_for_rows(rows) super-tiles
+    // (9 KB each) in flight, so this sets the bytes in flight per CU -- enough
+    // to cover the memory latency at full bandwidth.
     int waves = max_waves_for_rows(rows);
     const long long per_wg = pl.F * (long long)T + (pl.R ? ((long long)pl.R * T + pl.G - 1) / pl.G : 0);
-    // When the others can take everything two at a time, wave 0 takes no
-    // position: in a sequence each wave's first two super-tiles arrive ahead
-    // of the call, except wave 0's (it writes the results and cannot have
-    // loads in flight while it waits for them), so a position of its own would
-    // be the last to arrive.
-    if (per_wg <= 2 * (waves - 1)) waves -= 1;
+    // When the others can take everything in their first fetch, wave 0 takes
+    // no position: in a sequence each wave's first items arrive ahead of the
+    // call, except wave 0's (it writes the results and cannot have loads in
+    // flight while it waits for them), so a position of its own would be the
+    // last to arrive.
+    const int ahead = pipe_depth_for_rows(rows) / pl.nmat;   // positions of a wave's first fetch
+    if (per_wg <= (long long)ahead * (waves - 1)) waves -= 1;
     if (waves > per_wg) waves = (int)per_wg;
     if (waves < 1) waves = 1;
     pl.waves = waves;
