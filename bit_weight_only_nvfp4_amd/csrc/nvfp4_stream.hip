@@ -341,36 +341,43 @@ __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc 
     for (int r = 0; r < ROWS; ++r) epilogue<ROWS>(d, yr, v[0][r], v[1][r], sg, strip, r, lane);
 }
 
-// Wave 0: sum the pieces of shared strip sh in piece order and write its outputs.
+// Wave 0: sum the pieces of shared strip sh in piece order and write its
+// outputs.  The pieces are loaded QB at a time for every row at once, so a
+// strip costs one round trip to memory per QB pieces whatever the row count
+// (one per row, each behind the previous row's stores, is up to 8 at 8 rows).
 template <int ROWS>
 __device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, int sh, int np,
                                           const float (&sg)[2], __amdgpu_buffer_rsrc_t yr, int lane) {
     const bool pair = d.flags & kPair;
     const int nmat = pair ? 2 : 1;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    constexpr int QB = 8;   // partial loads in flight per matrix before the in-order adds
+    constexpr int QB = ROWS <= 2 ? 8 : ROWS <= 4 ? 4 : 2;   // pieces per round: at most 32 values per lane
+    float tq[ROWS][2];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        float tq[2] = {0.0f, 0.0f};
-        for (int q0 = 0; q0 < np; q0 += QB) {
-            float pv[2][QB];
+    for (int r = 0; r < ROWS; ++r) tq[r][0] = tq[r][1] = 0.0f;
+    for (int q0 = 0; q0 < np; q0 += QB) {
+        float pv[ROWS][2][QB];
 #pragma unroll
-            for (int j = 0; j < QB; ++j) {
-                const int pq = min(q0 + j, np - 1);
-                const size_t qs = ((size_t)sh * d.max_pieces + pq) * nmat;
+        for (int j = 0; j < QB; ++j) {
+            const int pq = min(q0 + j, np - 1);
+            const size_t qs = ((size_t)sh * d.max_pieces + pq) * nmat;
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    pv[m][j] = __hip_atomic_load(&a.partial[((qs + (pair ? m : 0)) * ROWS + r) * kStripN + lane],
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int j = 0; j < QB; ++j)
-                if (q0 + j < np)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) tq[m] += pv[m][j];
+                for (int r = 0; r < ROWS; ++r)
+                    pv[r][m][j] = __hip_atomic_load(&a.partial[((qs + (pair ? m : 0)) * ROWS + r) * kStripN + lane],
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        epilogue<ROWS>(d, yr, tq[0], tq[1], sg, d.G * d.F + sh, r, lane);
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+            if (q0 + j < np)
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) tq[r][m] += pv[r][m][j];
     }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) epilogue<ROWS>(d, yr, tq[r][0], tq[r][1], sg, d.G * d.F + sh, r, lane);
 }
 
 // Wait until every load and store of this wave issued so far has completed.
