@@ -127,13 +127,15 @@ constexpr int kMaxWavesPerWg = 8;
 // so that a pair's gate and up super-tiles of one position are always in
 // flight together).  The super-tiles in flight live in registers.  Two waves
 // per SIMD with two super-tiles each fit in 256 registers at every row count
-// (about 145 at 1 row, 245 at 8), and measured faster than either one wave
-// per SIMD with six in flight or three waves per SIMD with two: the calls of
-// a decode step are short (a few super-tiles per wave), and what a call
-// costs beyond its bytes is latency at its start and end, which more bytes
-// in flight do not shorten.  A wave can have at most 63 vector-memory loads
-// outstanding (a super-tile takes 9 plus one per 64 lanes of activations),
-// which would bound NB at 6 (1-2 rows) or 4 (up to 8 rows).
+// (about 145 at 1 row, 245 at 8).  Measured against it on the decode-step
+// sweep: one wave per SIMD with six in flight and three waves per SIMD with
+// two were 6-15% slower at 1-2 rows, and four in flight at two waves per SIMD
+// (1-2 rows, 225-252 registers) within 1% either way.  The calls of a decode
+// step are short (a few super-tiles per wave), and what a call costs beyond
+// its bytes is latency at its start and end, which more bytes in flight do
+// not shorten.  A wave can have at most 63 vector-memory loads outstanding (a
+// super-tile takes 9 plus one per 64 lanes of activations), which bounds NB
+// at 6 (1-2 rows) or 4 (up to 8 rows).
 __host__ __device__ constexpr int max_waves_for_rows(int rows) { return 8; }
 __host__ __device__ constexpr int pipe_depth_for_rows(int rows) { return 2; }
 

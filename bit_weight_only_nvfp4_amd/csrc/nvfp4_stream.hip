@@ -623,11 +623,11 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         // Items NB j + i (buffer i) per iteration, all NB in flight at the top;
         // each buffer is refilled with the item NB ahead as soon as it has been
         // consumed, and past the call's last items with the next call's first
-        // NB.  Items past the wave's last are dummies whose scales are zeroed.
-        // A wave with no positions that fetches for the next call runs one
+        // NB.  A wave with no positions that fetches for the next call runs one
         // iteration that only fetches, so that the buffers are written in one
-        // place only -- a second place costs registers at the merge.  The loop has one exit,
-        // and no wait at its head other than for the data it consumes.
+        // place only -- a second place costs registers at the merge.  The loop
+        // has one exit, and no wait at its head other than for the data it
+        // consumes.
         const int nitems = pair ? 2 * nw : nw;
         const int iters = nw > 0 ? (nitems + NB - 1) / NB : nreal ? 1 : 0;
         // Every load issued before the loop has completed here (the first
@@ -638,7 +638,6 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         // loads are the most recent, and it waits for nearly every load in
         // flight at the top of every iteration.
         if (iters > 0) wait_all_loads();
-        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
         for (int j = 0; j < iters; ++j) {
             const int t = NB * j;
             const bool more = j + 1 < iters;   // another iteration follows
@@ -646,13 +645,14 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int ti = t + i;
-                // a pair's up super-tile uses the window its gate staged; a wave
-                // without positions computes nothing (its buffers may hold
-                // anything, even non-finite activations of an earlier call)
-                if (nw > 0 && (!pair || !(i & 1))) core::stage_x<ROWS>(b[i].xv, xs, lane);
+                // Items past the wave's last are fetched (the loads in flight
+                // must not depend on control flow) but not computed; a pair's
+                // up super-tile uses the window its gate staged.
+                const bool live = ti < nitems;
+                if (live && (!pair || !(i & 1))) core::stage_x<ROWS>(b[i].xv, xs, lane);
                 // past the last item this closes every segment left
                 close_before(sw + (pair ? ti >> 1 : ti) * nwc);
-                if (nw > 0) core::core_mx<ROWS>(b[i].wc, ti < nitems ? b[i].ws : zero4, xs, lane, acc[i & 1]);
+                if (live) core::core_mx<ROWS>(b[i].wc, b[i].ws, xs, lane, acc[i & 1]);
                 load_tile<ROWS, true>(pick(more, item(ti + NB), first_item(nxt, nc, i, wave != 0)), zero, lane,
                                       b[i]);
             }
