@@ -428,17 +428,19 @@ __device__ __forceinline__ void arrive_piece(const SeqArgs &a, const CallDesc &d
 // workgroup counts itself in one arrival counter once its writes of the call
 // are complete; the workgroup whose count completes epoch e stores e in every
 // workgroup's release word, each in a 128-byte line of its own that only its
-// workgroup polls.  A wait that exceeds kWaitTicks sets a flag and goes on: it
-// never hangs.
-__device__ __forceinline__ void arrive_call(const SeqArgs &a, int g, unsigned e, int lane) {
+// workgroup polls, and goes on without waiting (returns true).  A wait that
+// exceeds kWaitTicks sets a flag and goes on: it never hangs.
+__device__ __forceinline__ bool arrive_call(const SeqArgs &a, int g, unsigned e, int lane) {
     wait_own_writes();
-    if (lane0_add(a.flags + 32, lane) + 1u == e * (unsigned)a.G) {
+    const bool last = lane0_add(a.flags + 32, lane) + 1u == e * (unsigned)a.G;
+    if (last) {
 #pragma unroll
         for (int i = 0; i < kMaxWorkgroups / 64; ++i) {
             const int w = lane + 64 * i;
             if (w < a.G) __hip_atomic_store(a.sync + w * 32, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    return last;
 }
 
 __device__ __forceinline__ void wait_release(const SeqArgs &a, int g, unsigned e, int lane) {
@@ -586,11 +588,19 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         const float sg[2] = {cur.sg[0], cur.sg[1]};
         // The next call's first NB items, fetched while this call ends.  Wave
         // 0 fetches its own only once it has counted this call done: it writes
-        // every result, and waits for its writes to complete first.
-        const bool nreal = nxt.fetch && wave != 0;
+        // every result, and waits for its writes to complete first.  At 1-2
+        // rows every wave waits until then (kLateFetch): the end of a call is a
+        // chain of dependent round trips to memory (partial sums, counts, the
+        // final sums, outputs, the wait), each slowed by any burst of loads in
+        // flight, and the calls are short enough that the chain, not the
+        // stream, sets their length (measured 1-2% faster on a decode step; at
+        // 4-8 rows, with more arithmetic per byte, 4-6% slower).
+        constexpr bool kLateFetch = ROWS <= 2;
+        const bool nreal = !kLateFetch && nxt.fetch && wave != 0;
         const Cursor nc0 = cursor_at(nxt.d, nxt.q, g, 0);
 
         int pub[2] = {0, 0};   // pieces of shared strips fs, fs + 1 stored here
+        bool released = false;   // this workgroup completed the call's epoch (wave 0)
         Cursor lc = cursor_at(d, q, g, 0), cc = lc;   // load cursor (runs ahead), segment being accumulated
         auto item = [&](int t) {
             const bool up = pair && (t & 1);
@@ -653,8 +663,8 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
                 // past the last item this closes every segment left
                 close_before(sw + (pair ? ti >> 1 : ti) * nwc);
                 if (live) core::core_mx<ROWS>(b[i].wc, b[i].ws, xs, lane, acc[i & 1]);
-                load_tile<ROWS, true>(pick(more, item(ti + NB), first_item(nxt, nc, i, wave != 0)), zero, lane,
-                                      b[i]);
+                const TileSrc next_call = first_item(nxt, nc, i, !kLateFetch && wave != 0);
+                load_tile<ROWS, true>(pick(more, item(ti + NB), next_call), zero, lane, b[i]);
             }
         }
         while (cc.k < q.nseg) {
@@ -667,11 +677,12 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
                 if (pub[0]) arrive_piece<ROWS>(a, d, q.fs, q.np0, sg, yr, lane);
                 if (pub[1]) arrive_piece<ROWS>(a, d, q.fs + 1, q.np1, sg, yr, lane);
             }
-            if (has_next) arrive_call(a, g, (unsigned)(c + 1), lane);
+            if (has_next) released = arrive_call(a, g, (unsigned)(c + 1), lane);
         }
         if (has_next) {
-            if (wave == 0 && nxt.fetch) {
-                // its writes are complete: its loads in flight delay only its polls
+            if (kLateFetch) __syncthreads();   // wave 0 has counted the call done
+            if ((kLateFetch || wave == 0) && nxt.fetch) {
+                // wave 0's writes are complete: its loads in flight delay only its polls
                 Cursor nc = nc0;
 #pragma unroll
                 for (int i = 0; i < NB; ++i) load_tile<ROWS, true>(first_item(nxt, nc, i, true), zero, lane, b[i]);
@@ -679,7 +690,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             // the call after next, prepared while the workgroups finish this one
             cur = nxt;
             nxt = prepare(c + 2);
-            if (wave == 0) wait_release(a, g, (unsigned)(c + 1), lane);
+            if (wave == 0 && !released) wait_release(a, g, (unsigned)(c + 1), lane);
             __syncthreads();   // the next call starts in every wave
         }
     }
