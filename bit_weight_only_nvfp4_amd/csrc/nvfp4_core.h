@@ -1,8 +1,11 @@
 // nvfp4_core.h -- per-super-tile compute of the gfx950 NVFP4 projection on the
-// block-scaled matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4, fp8 x fp4).
+// matrix cores, on one of two paths: block-scaled fp8 x fp4 products
+// (v_mfma_scale_f32_16x16x128_f8f6f4: stage_x, core_mx; up to 4 activation
+// rows) or fp16 products of dequantized weights (v_mfma_f32_16x16x32_f16:
+// stage_x16, core_f16; 5-8 rows), described before each.
 //
-// The E2M1 codes are the fp4 B operand exactly as stored: no per-weight
-// conversion.  One product covers 16 features x 64 k and 16 "slots" (rows of
+// fp8 x fp4 path: the E2M1 codes are the fp4 B operand exactly as stored (no
+// per-weight conversion).  One product covers 16 features x 64 k and 16 "slots" (rows of
 // A): slot 4 G + R is activation row 4 rq + R restricted to group G (16 k) of
 // the 64-k block.  Each activation value is split exactly into an fp8 E4M3
 // high part and an fp8 low part (x = hi + lo for all values within 13 binades
@@ -161,6 +164,145 @@ __device__ __forceinline__ void core_mx(const uint4 (&wc)[kCodeChunks / 2], cons
         // one k block at a time: bounds the products in flight (registers)
         if (ROWS > 4) __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// ---------------------------------------------------------------------------
+// fp16 path (v_mfma_f32_16x16x32_f16).  Each code times its E4M3 group scale
+// is exact in fp16 (at most 6 significant bits, magnitudes 2^-10 .. 2688), and
+// so is each activation times one power of two per (row, super-tile) for the
+// values within 31 binades of that row's largest in the super-tile (the rest,
+// below 2^-31 of it, round to the nearest 2^-24 step of the scaled values).
+// The products are then ordinary fp16 x fp16 -> fp32 matrix products with no
+// masked rows: A rows are the activation rows, B the dequantized weights.
+//
+// Operand lane layouts of the 16x16x32 product (measured on gfx950): A: lane
+// 16 q + i holds row i, k = 8 q .. 8 q + 7; B: lane 16 q + n holds column n,
+// k = 8 q .. 8 q + 7; D: lane 16 q + n holds rows 4 q .. 4 q + 3 of column n.
+// Any assignment of actual k to the products' k slots is a valid product as
+// long as A and B use the same one; here lane group q of the products of k
+// pair p (64-k blocks 2 p, 2 p + 1) and step s covers k = K(q) + 8 s + e with
+// K(q) = 64 (2 p + q / 2) + 32 (q % 2): exactly the 32 codes the lane holds
+// after one v_permlane32_swap of two of its code registers.
+
+// LDS image of one super-tile's activations for the fp16 path, per wave.
+template <int ROWS>
+struct XStage16 {
+    static constexpr int XR = (ROWS * 32 + 63) / 64;   // 16-byte activation chunks per lane
+    static constexpr int ROW_BYTES = 528;              // 256 fp16 + 16 (rows start 4 banks apart)
+    static constexpr int ZERO_OFF = ROWS * ROW_BYTES;  // 16 zero bytes: the A rows past ROWS
+    static constexpr int SCALE_OFF = ZERO_OFF + 16;    // per row: the float undoing its scale
+    static constexpr int WS_OFF = SCALE_OFF + 32;      // the lanes' 16-byte group-scale entries
+    static constexpr int BYTES = WS_OFF + 1024;
+};
+
+// Stage the super-tile's activations as fp16, each row scaled by 2^(14 - E)
+// where its largest |x| in the super-tile is below 2^(E+1).  Chunk c = lane +
+// 64 i holds row c / 32, k = 8 (c % 32) .. + 7: the 32 lanes of a half-wave
+// hold one row.
+template <int ROWS>
+__device__ __forceinline__ void stage_x16(const uint4 (&xv)[XStage16<ROWS>::XR], uint8_t *xs, int lane) {
+    using S = XStage16<ROWS>;
+#pragma unroll
+    for (int i = 0; i < S::XR; ++i) {
+        const int c = lane + 64 * i;
+        const int r = c >> 5, kk = (c & 31) * 8;
+        const uint32_t d[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        uint32_t m = pk_max_u16(pk_max_u16(d[0] & 0x7fff7fffu, d[1] & 0x7fff7fffu),
+                                pk_max_u16(d[2] & 0x7fff7fffu, d[3] & 0x7fff7fffu));
+        m = max(m & 0xffffu, m >> 16);
+        // largest over the 32 lanes of the row: quads (lane ^ 1, lane ^ 2),
+        // half-rows and rows of 16 (mirrors), then the two rows of 16
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));   // row_half_mirror
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));   // row_mirror
+        m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+        // biased exponent of the row's largest |x|, kept where both scales are
+        // normal floats (rows of all zeros or of tiny values take the bottom)
+        const int ef = min(max((int)(m >> 7), 15), 254);
+        const float sc = __builtin_bit_cast(float, (268 - ef) << 23);    // 2^(141 - ef) = 2^(14 - E)
+        const float un = __builtin_bit_cast(float, (ef - 14) << 23);     // 2^(E - 14)
+        typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+        half8_t h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            h[2 * q] = (_Float16)(__builtin_bit_cast(float, d[q] << 16) * sc);
+            h[2 * q + 1] = (_Float16)(__builtin_bit_cast(float, d[q] & 0xffff0000u) * sc);
+        }
+        if (r < ROWS) {
+            *reinterpret_cast<half8_t *>(xs + r * S::ROW_BYTES + kk * 2) = h;
+            if ((c & 31) == 0) *reinterpret_cast<float *>(xs + S::SCALE_OFF + r * 4) = un;
+        }
+    }
+}
+
+// acc[fb][r] += this super-tile's sum for feature 16 fb + n, row r, in the
+// lanes of group r / 4 (others add nothing).  wc, ws as for core_mx.
+template <int ROWS>
+__device__ __forceinline__ void core_f16(const uint4 (&wc)[kCodeChunks / 2], const uint4 &ws, uint8_t *xs, int lane,
+                                         float (&acc)[4][ROWS]) {
+    using S = XStage16<ROWS>;
+    typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    const int q = lane >> 4, n = lane & 15;
+    // group-scale entries: lane (q, n) needs those of lanes 16 (2 (q % 2) + t) + n
+    *reinterpret_cast<uint4 *>(xs + S::WS_OFF + lane * 16) = ws;
+    f32x4_t D[4];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) D[fb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        // scales of this lane's two groups (t), for each feature block
+        half2_t sh[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int src = 16 * (2 * (q & 1) + t) + n;
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(xs + S::WS_OFF + src * 16 + 4 * (2 * p + (q >> 1)));
+            const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+            const f32x2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+            const float sv[4] = {s01.x, s01.y, s23.x, s23.y};
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) sh[t][fb] = half2_t{(_Float16)sv[fb], (_Float16)sv[fb]};
+        }
+        // codes of k pair p: feature blocks 2 h, 2 h + 1 from one swap per register
+        uint32_t cb[4][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t x[4] = {wc[4 * p + h].x, wc[4 * p + h].y, wc[4 * p + h].z, wc[4 * p + h].w};
+            const uint32_t y[4] = {wc[4 * p + 2 + h].x, wc[4 * p + 2 + h].y, wc[4 * p + 2 + h].z, wc[4 * p + 2 + h].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const auto r = __builtin_amdgcn_permlane32_swap(x[j], y[j], false, false);
+                cb[2 * h][j] = r[0];
+                cb[2 * h + 1][j] = r[1];
+            }
+        }
+        const int K = 64 * (2 * p + (q >> 1)) + 32 * (q & 1);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const half8_t A = *reinterpret_cast<const half8_t *>(
+                xs + (n < ROWS ? n * S::ROW_BYTES + (K + 8 * st) * 2 : S::ZERO_OFF));
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+                const uint32_t w = cb[fb][st];
+                const half2_t g = sh[st >> 1][fb];
+                const half2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * g;
+                const half2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * g;
+                const half2_t b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * g;
+                const half2_t b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * g;
+                const half8_t B = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+                D[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, D[fb], 0, 0, 0);
+            }
+        }
+    }
+    float un[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) un[r] = *reinterpret_cast<const float *>(xs + S::SCALE_OFF + r * 4);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+            acc[fb][r] = q == (r >> 2) ? __builtin_fmaf(D[fb][r & 3], un[r], acc[fb][r]) : acc[fb][r];
 }
 
 // Sum over the four lane groups; lane 16 g + n returns the total of feature

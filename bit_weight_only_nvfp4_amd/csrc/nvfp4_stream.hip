@@ -39,6 +39,7 @@
 // remaining strips form R*T shared units split into G contiguous ranges
 // [g*RT/G, (g+1)*RT/G), cut at strip boundaries into pieces.
 #include <atomic>
+#include <type_traits>
 
 #include "nvfp4_core.h"
 
@@ -467,11 +468,23 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     // Position order of the waves: wave 0 comes last, so it gets the fewest
     // super-tiles -- it also reduces and writes every result.
     const int sw = wave == 0 ? nwb - 1 : wave - 1;
-    using XS = core::XStage<ROWS>;
-    static_assert(XS::BYTES == 2304 * ((ROWS + 3) / 4) + 32, "host LDS sizing assumes this staging size");
+    constexpr bool kF16 = use_f16_core(ROWS);
+    using XS = std::conditional_t<kF16, core::XStage16<ROWS>, core::XStage<ROWS>>;
+    static_assert(XS::BYTES == x_stage_bytes(ROWS), "host LDS sizing assumes this staging size");
+    static_assert(XS::XR == Tile<ROWS>::XR, "one activation chunk layout");
     uint8_t *xs = smem + (size_t)wave * XS::BYTES;   // this wave's staged activations
     float *red = reinterpret_cast<float *>(smem + (size_t)nwb * XS::BYTES);
-    if (lane < 8) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
+    constexpr int kZeroWords = kF16 ? 4 : 8;   // the staging's zero bytes
+    if (lane < kZeroWords) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
+    // one staging and one product per super-tile, on the path chosen for ROWS
+    auto stage = [&](const Tile<ROWS> &t) {
+        if constexpr (kF16) core::stage_x16<ROWS>(t.xv, xs, lane);
+        else core::stage_x<ROWS>(t.xv, xs, lane);
+    };
+    auto product = [&](const Tile<ROWS> &t, float (&ac)[4][ROWS]) {
+        if constexpr (kF16) core::core_f16<ROWS>(t.wc, t.ws, xs, lane, ac);
+        else core::core_mx<ROWS>(t.wc, t.ws, xs, lane, ac);
+    };
 
     float acc[2][4][ROWS];
 #pragma unroll
@@ -659,10 +672,10 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
                 // must not depend on control flow) but not computed; a pair's
                 // up super-tile uses the window its gate staged.
                 const bool live = ti < nitems;
-                if (live && (!pair || !(i & 1))) core::stage_x<ROWS>(b[i].xv, xs, lane);
+                if (live && (!pair || !(i & 1))) stage(b[i]);
                 // past the last item this closes every segment left
                 close_before(sw + (pair ? ti >> 1 : ti) * nwc);
-                if (live) core::core_mx<ROWS>(b[i].wc, b[i].ws, xs, lane, acc[i & 1]);
+                if (live) product(b[i], acc[i & 1]);
                 const TileSrc next_call = first_item(nxt, nc, i, !kLateFetch && wave != 0);
                 load_tile<ROWS, true>(pick(more, item(ti + NB), next_call), zero, lane, b[i]);
             }
@@ -820,7 +833,7 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
 }
 
 size_t stream_lds_bytes(int rows, int waves) {
-    const size_t lds_x = (size_t)waves * (2304 * ((rows + 3) / 4) + 32);   // core::XStage<rows>::BYTES
+    const size_t lds_x = (size_t)waves * x_stage_bytes(rows);
     const size_t lds_red = (size_t)waves * 2 * rows * kStripN * sizeof(float);
     // at least ~81 KB so that no CU ever holds two of these workgroups
     return lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;
