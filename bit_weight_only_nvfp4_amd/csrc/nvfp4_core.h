@@ -166,6 +166,126 @@ __device__ __forceinline__ void core_mx(const uint4 (&wc)[kCodeChunks / 2], cons
     }
 }
 
+// One activation row (the fp8 x fp4 path mapped for it): a product covers 16
+// features x 128 k -- the codes of two 64-k blocks of one feature block after
+// one v_permlane32_swap, already the B layout above -- and its 16 slots are
+// the 8 groups of those 128 k, hi and lo part each: slot m = 2 G + part holds
+// group G (k 16 G .. 16 G + 15) of part m % 2, zero elsewhere, so a super-tile
+// takes 8 products where the general mapping takes 16 (it fills only one of
+// its 4 row slots with one row).  D rows 4 q + v of lane group q are groups
+// 2 q + v / 2: their sums are D[0] + D[1] and D[2] + D[3].
+struct XStage1 {
+    static constexpr int XR = 1;
+    // pair p (64-k blocks 2 p, 2 p + 1), slot m: 32 bytes in the A lane layout
+    // (group G < 4 in bytes 0..15, G >= 4 in bytes 16..31, the other half zero)
+    static constexpr int EXP_OFF = 2 * 16 * 32;        // pair p, slot m: E8M0 byte
+    static constexpr int ZERO_OFF = EXP_OFF + 32;      // 32 zero bytes
+    static constexpr int WS_OFF = ZERO_OFF + 32;       // the lanes' 16-byte group-scale entries
+    static constexpr int BYTES = WS_OFF + 1024;
+};
+
+// Zero the slot image once: the half of each slot entry that holds no group
+// is never written afterwards.
+__device__ __forceinline__ void init_x1(uint8_t *xs, int lane) {
+    *reinterpret_cast<uint4 *>(xs + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < 8) reinterpret_cast<uint32_t *>(xs + XStage1::ZERO_OFF)[lane] = 0u;
+}
+
+// As stage_x (same hi / lo split and exponents), into the one-row slot image.
+// Lane l < 32 holds k = 8 l .. 8 l + 7: group l / 2 of the super-tile.
+__device__ __forceinline__ void stage_x1(const uint4 (&xv)[1], uint8_t *xs, int lane) {
+    using S = XStage1;
+    const uint32_t d[4] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w};
+    uint32_t m = pk_max_u16(pk_max_u16(d[0] & 0x7fff7fffu, d[1] & 0x7fff7fffu),
+                            pk_max_u16(d[2] & 0x7fff7fffu, d[3] & 0x7fff7fffu));
+    m = max(m & 0xffffu, m >> 16);
+    m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+    const int ef = (int)(m >> 7);
+    const int ehi = max(ef, 8) - 7, elo = max(ef, 13) - 12;
+    const float shi = __builtin_bit_cast(float, ehi << 23), slo = __builtin_bit_cast(float, elo << 23);
+    i16x2_t hw0 = {0, 0}, hw1 = {0, 0};
+    hw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw0, __builtin_bit_cast(bf16x2_t, d[0]), shi, false);
+    hw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw0, __builtin_bit_cast(bf16x2_t, d[1]), shi, true);
+    hw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw1, __builtin_bit_cast(bf16x2_t, d[2]), shi, false);
+    hw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hw1, __builtin_bit_cast(bf16x2_t, d[3]), shi, true);
+    const uint32_t h0 = __builtin_bit_cast(uint32_t, hw0), h1 = __builtin_bit_cast(uint32_t, hw1);
+    const f32x2_t back[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h0, shi, false),
+                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h0, shi, true),
+                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h1, shi, false),
+                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h1, shi, true)};
+    float lo[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {   // exact: x and hi share the exponent range
+        lo[2 * q] = __builtin_bit_cast(float, d[q] << 16) - back[q].x;
+        lo[2 * q + 1] = __builtin_bit_cast(float, d[q] & 0xffff0000u) - back[q].y;
+    }
+    i16x2_t lw0 = {0, 0}, lw1 = {0, 0};
+    lw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw0, lo[0], lo[1], slo, false);
+    lw0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw0, lo[2], lo[3], slo, true);
+    lw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw1, lo[4], lo[5], slo, false);
+    lw1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw1, lo[6], lo[7], slo, true);
+    if (lane < 32) {
+        const int gt = lane >> 1, h = lane & 1, p = gt >> 3, G = gt & 7;
+        uint8_t *e = xs + p * 512 + 2 * G * 32 + (G >> 2) * 16 + h * 8;   // slot 2 G (hi); 2 G + 1 (lo) is 32 on
+        *reinterpret_cast<uint2 *>(e) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2 *>(e + 32) =
+            make_uint2(__builtin_bit_cast(uint32_t, lw0), __builtin_bit_cast(uint32_t, lw1));
+        if (h == 0)
+            *reinterpret_cast<uint16_t *>(xs + S::EXP_OFF + p * 16 + 2 * G) = (uint16_t)(ehi | (elo << 8));
+    }
+}
+
+// acc[fb] += this lane's share of one matrix's super-tile (lane group q: groups
+// 8 p + 2 q, 8 p + 2 q + 1 of each k pair p); wc, ws as for core_mx.
+__device__ __forceinline__ void core_mx1(const uint4 (&wc)[kCodeChunks / 2], const uint4 &ws, uint8_t *xs, int lane,
+                                         float (&acc)[4][1]) {
+    using S = XStage1;
+    const int q = lane >> 4, i = lane & 15;
+    *reinterpret_cast<uint4 *>(xs + S::WS_OFF + lane * 16) = ws;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        // E4M3 scales of this lane's groups 8 p + 2 q + t, from lanes 16 (2 (q % 2) + t) + n
+        float sc[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int src = 16 * (2 * (q & 1) + t) + i;
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(xs + S::WS_OFF + src * 16 + 4 * (2 * p + (q >> 1)));
+            const f32x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+            const f32x2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+            sc[t][0] = s01.x;
+            sc[t][1] = s01.y;
+            sc[t][2] = s23.x;
+            sc[t][3] = s23.y;
+        }
+        // A: slot i; data in lane group (i / 2) % 4, the E8M0 scale in lane group i / 4
+        const int G = i >> 1;
+        const i32x8_t A = *reinterpret_cast<const i32x8_t *>(xs + (q == (G & 3) ? p * 512 + i * 32 : S::ZERO_OFF));
+        const uint32_t e2 = *reinterpret_cast<const uint16_t *>(xs + S::EXP_OFF + p * 16 + (i & ~1));
+        const int sa = q == (i >> 2) ? (int)((i & 1) ? (e2 >> 8) : (e2 & 0xff)) : 127;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t x[4] = {wc[4 * p + h].x, wc[4 * p + h].y, wc[4 * p + h].z, wc[4 * p + h].w};
+            const uint32_t y[4] = {wc[4 * p + 2 + h].x, wc[4 * p + 2 + h].y, wc[4 * p + 2 + h].z, wc[4 * p + 2 + h].w};
+            i32x4_t b[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const auto r = __builtin_amdgcn_permlane32_swap(x[j], y[j], false, false);
+                b[0][j] = (int32_t)r[0];
+                b[1][j] = (int32_t)r[1];
+            }
+#pragma unroll
+            for (int o = 0; o < 2; ++o) {
+                const int fb = 2 * h + o;
+                const i32x8_t B = __builtin_shufflevector(b[o], b[o], 0, 1, 2, 3, -1, -1, -1, -1);
+                const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                const f32x4_t D = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, 127);
+                acc[fb][0] = __builtin_fmaf(D[0] + D[1], sc[0][fb], acc[fb][0]);
+                acc[fb][0] = __builtin_fmaf(D[2] + D[3], sc[1][fb], acc[fb][0]);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fp16 path (v_mfma_f32_16x16x32_f16).  Each code times its E4M3 group scale
 // is exact in fp16 (at most 6 significant bits, magnitudes 2^-10 .. 2688), and

@@ -140,7 +140,8 @@ __host__ __device__ constexpr int max_waves_for_rows(int rows) { return 8; }
 __host__ __device__ constexpr int pipe_depth_for_rows(int rows) { return 2; }
 // Super-tile arithmetic: the fp16 matrix-core path (dequantized weights, fp16
 // activations) from 5 rows on, the block-scaled fp8 x fp4 path below; and the
-// per-wave LDS bytes of its staged activations (core::XStage16 / core::XStage).
+// per-wave LDS bytes of its staged activations (core::XStage16, core::XStage1
+// at one row, core::XStage).
 // The fp8 path masks 3 of every 4 product rows and splits each activation in
 // two; the fp16 path pays instead for converting every code (about 512 vector
 // instructions per super-tile, whatever the row count).  Measured on the
@@ -150,7 +151,7 @@ __host__ __device__ constexpr int pipe_depth_for_rows(int rows) { return 2; }
 constexpr int kF16FromRows = 5;
 __host__ __device__ constexpr bool use_f16_core(int rows) { return rows >= kF16FromRows; }
 __host__ __device__ constexpr int x_stage_bytes(int rows) {
-    return use_f16_core(rows) ? rows * 528 + 16 + 32 + 1024 : 2304 * ((rows + 3) / 4) + 32;
+    return use_f16_core(rows) ? rows * 528 + 16 + 32 + 1024 : rows == 1 ? 2112 : 2304 * ((rows + 3) / 4) + 32;
 }
 
 struct StreamPlan {

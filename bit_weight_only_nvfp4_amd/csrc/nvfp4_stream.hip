@@ -468,21 +468,25 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     // Position order of the waves: wave 0 comes last, so it gets the fewest
     // super-tiles -- it also reduces and writes every result.
     const int sw = wave == 0 ? nwb - 1 : wave - 1;
-    constexpr bool kF16 = use_f16_core(ROWS);
-    using XS = std::conditional_t<kF16, core::XStage16<ROWS>, core::XStage<ROWS>>;
+    constexpr bool kF16 = use_f16_core(ROWS), kOne = !kF16 && ROWS == 1;
+    using XS = std::conditional_t<kF16, core::XStage16<ROWS>,
+                                  std::conditional_t<kOne, core::XStage1, core::XStage<ROWS>>>;
     static_assert(XS::BYTES == x_stage_bytes(ROWS), "host LDS sizing assumes this staging size");
     static_assert(XS::XR == Tile<ROWS>::XR, "one activation chunk layout");
     uint8_t *xs = smem + (size_t)wave * XS::BYTES;   // this wave's staged activations
     float *red = reinterpret_cast<float *>(smem + (size_t)nwb * XS::BYTES);
     constexpr int kZeroWords = kF16 ? 4 : 8;   // the staging's zero bytes
-    if (lane < kZeroWords) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
+    if constexpr (kOne) core::init_x1(xs, lane);
+    else if (lane < kZeroWords) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
     // one staging and one product per super-tile, on the path chosen for ROWS
     auto stage = [&](const Tile<ROWS> &t) {
         if constexpr (kF16) core::stage_x16<ROWS>(t.xv, xs, lane);
+        else if constexpr (kOne) core::stage_x1(t.xv, xs, lane);
         else core::stage_x<ROWS>(t.xv, xs, lane);
     };
     auto product = [&](const Tile<ROWS> &t, float (&ac)[4][ROWS]) {
         if constexpr (kF16) core::core_f16<ROWS>(t.wc, t.ws, xs, lane, ac);
+        else if constexpr (kOne) core::core_mx1(t.wc, t.ws, xs, lane, ac);
         else core::core_mx<ROWS>(t.wc, t.ws, xs, lane, ac);
     };
 
