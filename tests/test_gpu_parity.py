@@ -222,6 +222,30 @@ def test_dual_random_all_rows(nv, n, k):
         check.check_dual(o32, o16, d, label="dual %dx%d rows=%d" % (n, k, rows))
 
 
+def _wide_x(rng, rows, k, binades):
+    """bf16 activations sign * 2^u, u uniform over [-binades, binades]: groups
+    and super-tiles whose values span up to 2 * binades binades."""
+    u = rng.uniform(-binades, binades, size=(rows, k))
+    xv = (np.where(rng.random((rows, k)) < 0.5, -1.0, 1.0) * np.exp2(u)).astype(np.float32)
+    return workloads.bf16_bits(xv)
+
+
+@pytest.mark.parametrize("n,k", [(200, 784), (130, 4112)])
+def test_gemv_wide_range_activations_all_rows(nv, n, k):
+    """Activations spread over 2^-16 .. 2^16 inside every group: the fp8 split
+    is exact only within 13 binades of a group's largest and the fp16 staging
+    within 31 of a row's largest in a super-tile; R14/R15 still hold."""
+    rng = np.random.default_rng(31 * n + k)
+    for rows in range(1, 9):
+        c = workloads.case(n, k, rows, seed=300 * rows + n, outlier_frac=0.01)
+        q = oracle.quantize(c["W"])
+        xb = _wide_x(rng, rows, k, 16)
+        y32, y16 = _run_gemv(nv, _pack(nv, q), xb)
+        ref, absd, ref16 = oracle.gemv(*q, xb)
+        st = check.check_gemv(y32, y16, ref, absd, ref16, label="wide gemv %dx%d rows=%d" % (n, k, rows))
+        print("wide gemv %dx%d rows=%d: max err / sum|w*x| = %.3g" % (n, k, rows, st["max_err_over_absdot"]))
+
+
 def test_gemv_zero_inputs(nv):
     c = workloads.case(130, 784, 3, seed=5)
     q = oracle.quantize(c["W"])
