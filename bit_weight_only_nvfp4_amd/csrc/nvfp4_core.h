@@ -2,7 +2,7 @@
 // matrix cores, on one of two paths: block-scaled fp8 x fp4 products
 // (v_mfma_scale_f32_16x16x128_f8f6f4: stage_x, core_mx; up to 4 activation
 // rows) or fp16 products of dequantized weights (v_mfma_f32_16x16x32_f16:
-// stage_x16, core_f16; 5-8 rows), described before each.
+// stage_x16, core_f16; 5-16 rows), described before each.
 //
 // fp8 x fp4 path: the E2M1 codes are the fp4 B operand exactly as stored (no
 // per-weight conversion).  One product covers 16 features x 64 k and 16 "slots" (rows of
@@ -310,9 +310,12 @@ struct XStage16 {
     static constexpr int XR = (ROWS * 32 + 63) / 64;   // 16-byte activation chunks per lane
     static constexpr int ROW_BYTES = 528;              // 256 fp16 + 16 (rows start 4 banks apart)
     static constexpr int ZERO_OFF = ROWS * ROW_BYTES;  // 16 zero bytes: the A rows past ROWS
-    static constexpr int SCALE_OFF = ZERO_OFF + 16;    // per row: the float undoing its scale
-    static constexpr int WS_OFF = SCALE_OFF + 32;      // the lanes' 16-byte group-scale entries
+    // per product row (16): the float undoing its row's scale, zero past ROWS
+    // (zeroed with the 16 bytes before it, once per launch)
+    static constexpr int SCALE_OFF = ZERO_OFF + 16;
+    static constexpr int WS_OFF = SCALE_OFF + 64;      // the lanes' 16-byte group-scale entries
     static constexpr int BYTES = WS_OFF + 1024;
+    static constexpr int ZERO_WORDS = 20;              // zero bytes and row scales, as words
 };
 
 // Stage the super-tile's activations as fp16, each row scaled by 2^(14 - E)
@@ -356,11 +359,12 @@ __device__ __forceinline__ void stage_x16(const uint4 (&xv)[XStage16<ROWS>::XR],
     }
 }
 
-// acc[fb][r] += this super-tile's sum for feature 16 fb + n, row r, in the
-// lanes of group r / 4 (others add nothing).  wc, ws as for core_mx.
+// acc[fb][v] += this super-tile's sum for feature 16 fb + n, row 4 q + v: a
+// lane keeps only the rows its products hold (lane group q; rows past ROWS
+// stay zero).  wc, ws as for core_mx.
 template <int ROWS>
 __device__ __forceinline__ void core_f16(const uint4 (&wc)[kCodeChunks / 2], const uint4 &ws, uint8_t *xs, int lane,
-                                         float (&acc)[4][ROWS]) {
+                                         float (&acc)[4][4]) {
     using S = XStage16<ROWS>;
     typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -415,14 +419,11 @@ __device__ __forceinline__ void core_f16(const uint4 (&wc)[kCodeChunks / 2], con
             }
         }
     }
-    float un[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) un[r] = *reinterpret_cast<const float *>(xs + S::SCALE_OFF + r * 4);
+    const f32x4_t un = *reinterpret_cast<const f32x4_t *>(xs + S::SCALE_OFF + 16 * q);
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r)
-            acc[fb][r] = q == (r >> 2) ? __builtin_fmaf(D[fb][r & 3], un[r], acc[fb][r]) : acc[fb][r];
+        for (int v = 0; v < 4; ++v) acc[fb][v] = __builtin_fmaf(D[fb][v], un[v], acc[fb][v]);
 }
 
 // Sum over the four lane groups; lane 16 g + n returns the total of feature

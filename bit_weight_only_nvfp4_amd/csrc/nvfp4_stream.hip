@@ -1,6 +1,6 @@
 // nvfp4_stream.hip -- persistent streaming NVFP4 projection kernel for gfx950.
 //
-// y[r][j] = s_g * sum_k (code * scale)[j][k] * x[r][k] for 1..8 activation rows,
+// y[r][j] = s_g * sum_k (code * scale)[j][k] * x[r][k] for 1..16 activation rows,
 // and the gate/up pair o = silu(g) * u (the w4a16_gemv / w4a16_gemv_dual kernel
 // family of the Qwen3.8-27B-NVFP4 blueprint page, "Kernels" table).
 //
@@ -282,28 +282,45 @@ __device__ __forceinline__ Cursor cursor_at(const CallDesc &d, const Geometry &q
 // wave-uniform guards: a rolled loop or a divergent branch there makes the
 // compiler assume that tile loads may still be in flight at the top of the
 // tile loop, and wait for them.
-template <int ROWS>
+template <int ROWS, int AR>
 __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc &d, const Geometry &q, int g,
                                                int k, float *red, const float (&sg)[2],
                                                __amdgpu_buffer_rsrc_t yr, int wave, int sw, int nwc, int lane,
-                                               float (&acc)[2][4][ROWS], int (&pub)[2]) {
+                                               float (&acc)[2][4][AR], int (&pub)[2]) {
     const bool pair = d.flags & kPair;
+    constexpr int RR = red_rows(ROWS);   // rows per slot of `red`
     __syncthreads();   // the previous segment's reads of `red` are done
     // slots in position order (sw): the sums below run in that order
     // a pair's accumulators are its gate and up sums; a single projection's
     // are two halves of its sum (even and odd tiles of the wave)
+    if constexpr (use_f16_core(ROWS)) {
+        // lane 16 q + n holds rows 4 q + v of features 16 fb + n, already
+        // summed over k: each lane writes its own, rows past ROWS (exact
+        // zeros) included, since the slots have 16 rows on this path
+        float *base = red + (sw * 2 * RR + 4 * (lane >> 4)) * kStripN + (lane & 15);
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        float g4[4], u4[4];
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb) {
-            g4[fb] = pair ? acc[0][fb][r] : acc[0][fb][r] + acc[1][fb][r];
-            u4[fb] = acc[1][fb][r];
-            acc[0][fb][r] = 0.0f;
-            acc[1][fb][r] = 0.0f;
+            for (int fb = 0; fb < 4; ++fb) {
+                base[v * kStripN + 16 * fb] = pair ? acc[0][fb][v] : acc[0][fb][v] + acc[1][fb][v];
+                if (pair) base[(RR + v) * kStripN + 16 * fb] = acc[1][fb][v];
+                acc[0][fb][v] = 0.0f;
+                acc[1][fb][v] = 0.0f;
+            }
+    } else {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            float g4[4], u4[4];
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+                g4[fb] = pair ? acc[0][fb][r] : acc[0][fb][r] + acc[1][fb][r];
+                u4[fb] = acc[1][fb][r];
+                acc[0][fb][r] = 0.0f;
+                acc[1][fb][r] = 0.0f;
+            }
+            red[((sw * 2 + 0) * RR + r) * kStripN + lane] = core::strip_total(g4, lane);
+            if (pair) red[((sw * 2 + 1) * RR + r) * kStripN + lane] = core::strip_total(u4, lane);
         }
-        red[((sw * 2 + 0) * ROWS + r) * kStripN + lane] = core::strip_total(g4, lane);
-        if (pair) red[((sw * 2 + 1) * ROWS + r) * kStripN + lane] = core::strip_total(u4, lane);
     }
     __syncthreads();
     if (wave != 0) return;
@@ -314,10 +331,10 @@ __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc 
         for (int r = 0; r < ROWS; ++r) {
             float t = 0.0f;
             if (m == 0 || pair) {
-                t = red[(m * ROWS + r) * kStripN + lane];
+                t = red[(m * RR + r) * kStripN + lane];
 #pragma unroll
                 for (int w = 1; w < kMaxWavesPerWg; ++w)
-                    if (w < nwc) t += red[((w * 2 + m) * ROWS + r) * kStripN + lane];
+                    if (w < nwc) t += red[((w * 2 + m) * RR + r) * kStripN + lane];
             }
             v[m][r] = t;
         }
@@ -352,7 +369,7 @@ __device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, i
     const bool pair = d.flags & kPair;
     const int nmat = pair ? 2 : 1;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    constexpr int QB = ROWS <= 2 ? 8 : ROWS <= 4 ? 4 : 2;   // pieces per round: at most 32 values per lane
+    constexpr int QB = ROWS <= 2 ? 8 : ROWS <= 4 ? 4 : ROWS <= 8 ? 2 : 1;   // pieces per round: at most 32 values per lane
     float tq[ROWS][2];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) tq[r][0] = tq[r][1] = 0.0f;
@@ -475,7 +492,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     static_assert(XS::XR == Tile<ROWS>::XR, "one activation chunk layout");
     uint8_t *xs = smem + (size_t)wave * XS::BYTES;   // this wave's staged activations
     float *red = reinterpret_cast<float *>(smem + (size_t)nwb * XS::BYTES);
-    constexpr int kZeroWords = kF16 ? 4 : 8;   // the staging's zero bytes
+    constexpr int kZeroWords = kF16 ? core::XStage16<ROWS>::ZERO_WORDS : 8;   // the staging's zero bytes
     if constexpr (kOne) core::init_x1(xs, lane);
     else if (lane < kZeroWords) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
     // one staging and one product per super-tile, on the path chosen for ROWS
@@ -484,19 +501,22 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         else if constexpr (kOne) core::stage_x1(t.xv, xs, lane);
         else core::stage_x<ROWS>(t.xv, xs, lane);
     };
-    auto product = [&](const Tile<ROWS> &t, float (&ac)[4][ROWS]) {
+    // Accumulators: the fp16 path's lanes hold 4 rows each (their products'
+    // rows), the other paths every row in every lane.
+    constexpr int AR = kF16 ? 4 : ROWS;
+    auto product = [&](const Tile<ROWS> &t, float (&ac)[4][AR]) {
         if constexpr (kF16) core::core_f16<ROWS>(t.wc, t.ws, xs, lane, ac);
         else if constexpr (kOne) core::core_mx1(t.wc, t.ws, xs, lane, ac);
         else core::core_mx<ROWS>(t.wc, t.ws, xs, lane, ac);
     };
 
-    float acc[2][4][ROWS];
+    float acc[2][4][AR];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) acc[m][fb][r] = 0.0f;
+            for (int r = 0; r < AR; ++r) acc[m][fb][r] = 0.0f;
     // The call table, copied into LDS once: reading a call's descriptor from
     // the kernel arguments at the start of every call costs a cache miss each
     // time; from LDS it is a few cycles.  The words are wave-uniform.
@@ -638,7 +658,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         // close every segment that ends before position i
         auto close_before = [&](int i) {
             while (i >= cc.end) {
-                finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
+                finish_segment<ROWS, AR>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
                 cc = cursor_at(d, q, g, cc.k + 1);
             }
         };
@@ -685,7 +705,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             }
         }
         while (cc.k < q.nseg) {
-            finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
+            finish_segment<ROWS, AR>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
         }
         if (wave == 0) {
@@ -757,6 +777,14 @@ hipError_t launch_args(int rows, const SeqArgs &a, int waves, size_t lds, hipStr
         case 6: return launch_rows<6>(a, waves, lds, s);
         case 7: return launch_rows<7>(a, waves, lds, s);
         case 8: return launch_rows<8>(a, waves, lds, s);
+        case 9: return launch_rows<9>(a, waves, lds, s);
+        case 10: return launch_rows<10>(a, waves, lds, s);
+        case 11: return launch_rows<11>(a, waves, lds, s);
+        case 12: return launch_rows<12>(a, waves, lds, s);
+        case 13: return launch_rows<13>(a, waves, lds, s);
+        case 14: return launch_rows<14>(a, waves, lds, s);
+        case 15: return launch_rows<15>(a, waves, lds, s);
+        case 16: return launch_rows<16>(a, waves, lds, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -838,7 +866,7 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
 
 size_t stream_lds_bytes(int rows, int waves) {
     const size_t lds_x = (size_t)waves * x_stage_bytes(rows);
-    const size_t lds_red = (size_t)waves * 2 * rows * kStripN * sizeof(float);
+    const size_t lds_red = (size_t)waves * 2 * red_rows(rows) * kStripN * sizeof(float);
     // at least ~81 KB so that no CU ever holds two of these workgroups
     return lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;
 }

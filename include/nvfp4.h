@@ -3,7 +3,7 @@
  *
  * Weight-only 4-bit projection ("w4a16" GEMV): weights are NVFP4 -- E2M1 codes,
  * one OCP E4M3 scale per 16 consecutive weights of an output row, one FP32
- * per-tensor scale -- and activations are bf16, 1..8 rows per call.  The
+ * per-tensor scale -- and activations are bf16, 1..16 rows per call.  The
  * format and kernel family are the ones named on the Qwen3.8-27B-NVFP4
  * blueprint page: "Precision" table (weights nvfp4/g16, activations bf16) and
  * "Kernels" table (w4a16_gemv_qg / _sw / _dual / _dual_sw, with the planner
@@ -62,7 +62,7 @@ extern "C" {
 #define NVFP4_ABI_VERSION 1
 #define NVFP4_LAYOUT_MAGIC 0x34465056u /* "VPF4" */
 #define NVFP4_LAYOUT_VERSION 2u
-#define NVFP4_MAX_ROWS 8
+#define NVFP4_MAX_ROWS 16
 
 enum {
     NVFP4_OK = 0,

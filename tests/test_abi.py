@@ -101,7 +101,7 @@ def test_gemv_argument_errors(nv):
     assert _gemv(nv, _weight(nv), x=None) == E["NVFP4_E_NULL"]
     assert _gemv(nv, _weight(nv), y=None) == E["NVFP4_E_NULL"]
     assert _gemv(nv, _weight(nv), rows=0) == E["NVFP4_E_ROWS"]
-    assert _gemv(nv, _weight(nv), rows=9) == E["NVFP4_E_ROWS"]
+    assert _gemv(nv, _weight(nv), rows=17) == E["NVFP4_E_ROWS"]
     assert _gemv(nv, _weight(nv), dtype=2) == E["NVFP4_E_DTYPE"]
     assert _gemv(nv, _weight(nv), x=XF + 2) == E["NVFP4_E_ALIGN"]
     assert _gemv(nv, _weight(nv), y=YF + 1) == E["NVFP4_E_ALIGN"]
@@ -175,7 +175,7 @@ def test_sequence_argument_errors(nv):
     assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_LAYOUT"]
     assert "call 2" in nv.nvfp4_last_error()
     arr[2].w = ctypes.pointer(good)
-    arr[1].rows = 9
+    arr[1].rows = 17
     assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_ROWS"]
     assert "call 1" in nv.nvfp4_last_error()
     arr[1].rows = 8

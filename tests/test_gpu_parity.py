@@ -19,6 +19,8 @@ import oracle
 import workloads
 from oracle import check
 
+ALL_ROWS = range(1, 17)   # every activation row count the library takes
+
 pytestmark = pytest.mark.gpu
 
 
@@ -164,7 +166,7 @@ def _exact_case(rng, n, k, rows):
 def test_gemv_exact_arithmetic_all_rows(nv, n, k):
     assert k * 6 * 2 < 2 ** 17
     rng = np.random.default_rng(n + k)
-    for rows in range(1, 9):
+    for rows in ALL_ROWS:
         codes, scales, sg, xb = _exact_case(rng, n, k, rows)
         w = nv.nvfp4_pack(_dev(codes), _dev(scales), float(sg))
         y32, y16 = _run_gemv(nv, w, xb)
@@ -178,7 +180,7 @@ def test_dual_exact_arithmetic(nv, n, k):
     """gate rows give g = 192 exactly (silu(192) = 192 in fp32 and fp64), so
     o = 192 * u must match the oracle exactly."""
     rng = np.random.default_rng(7 * n + k)
-    for rows in (1, 3, 8):
+    for rows in (1, 3, 8, 13, 16):
         ucodes, uscales, sg, xb = _exact_case(rng, n, k, rows)
         xv = ((xb.astype(np.uint32) << 16).view(np.float32)).copy()
         xv[:, :16] = 1.0
@@ -203,7 +205,7 @@ SHAPES = [(256, 512), (200, 784), (64, 2048), (130, 4112), (72, 17408)]
 
 @pytest.mark.parametrize("n,k", SHAPES)
 def test_gemv_random_all_rows(nv, n, k):
-    for rows in range(1, 9):
+    for rows in ALL_ROWS:
         c = workloads.case(n, k, rows, seed=100 * rows + n, outlier_frac=0.01)
         q = oracle.quantize(c["W"])
         w = _pack(nv, q)
@@ -214,7 +216,7 @@ def test_gemv_random_all_rows(nv, n, k):
 
 @pytest.mark.parametrize("n,k", [(256, 512), (200, 784), (130, 4112)])
 def test_dual_random_all_rows(nv, n, k):
-    for rows in range(1, 9):
+    for rows in ALL_ROWS:
         c = workloads.case(n, k, rows, seed=200 * rows + n, dual=True)
         gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
         o32, o16 = _run_dual(nv, _pack(nv, gq), _pack(nv, uq), c["x"])
@@ -236,7 +238,7 @@ def test_gemv_wide_range_activations_all_rows(nv, n, k):
     is exact only within 13 binades of a group's largest and the fp16 staging
     within 31 of a row's largest in a super-tile; R14/R15 still hold."""
     rng = np.random.default_rng(31 * n + k)
-    for rows in range(1, 9):
+    for rows in ALL_ROWS:
         c = workloads.case(n, k, rows, seed=300 * rows + n, outlier_frac=0.01)
         q = oracle.quantize(c["W"])
         xb = _wide_x(rng, rows, k, 16)
@@ -260,7 +262,7 @@ def test_gemv_zero_inputs(nv):
 def test_workspace_reuse_and_mixed_calls(nv):
     """Counters are left at zero: interleaved calls of different shapes, few and
     many strips, that share one workspace stay correct."""
-    cases = [workloads.case(300, 4352, r, seed=40 + r) for r in (1, 8, 3)]
+    cases = [workloads.case(300, 4352, r, seed=40 + r) for r in (1, 8, 3, 16, 11)]
     cases.append(workloads.case(4480, 2048, 2, seed=44))
     qs = [oracle.quantize(c["W"]) for c in cases]
     need = max(nv.nvfp4_workspace_bytes(c["n"], c["k"], c["rows"]) for c in cases)
