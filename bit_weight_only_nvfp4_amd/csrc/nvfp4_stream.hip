@@ -359,31 +359,39 @@ __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc 
     for (int r = 0; r < ROWS; ++r) epilogue<ROWS>(d, yr, v[0][r], v[1][r], sg, strip, r, lane);
 }
 
-// Wave 0: sum the pieces of shared strip sh in piece order and write its
-// outputs.  The pieces are loaded QB at a time for every row at once, so a
-// strip costs one round trip to memory per QB pieces whatever the row count
-// (one per row, each behind the previous row's stores, is up to 8 at 8 rows).
-template <int ROWS>
+// Pieces of a shared strip are summed in piece order, gate and up (NM = 2) or
+// the projection alone (NM = 1), 32 values per lane in flight per round trip
+// to memory (16 at one row: measured 1% faster on the decode step there, 1%
+// slower at two rows; loads past the last piece read the last one again,
+// which measured faster than skipping them behind branches).  Pieces per
+// round trip for one wave holding every row:
+template <int ROWS, int NM>
+__host__ __device__ constexpr int final_sum_qb() {
+    return ROWS == 1 ? 16 / NM : (32 / NM) / ROWS > 0 ? (32 / NM) / ROWS : 1;
+}
+
+// Wave 0: sum the pieces of shared strip sh for every row at once, QB pieces
+// per round, and write its outputs.
+template <int ROWS, int NM>
 __device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, int sh, int np,
                                           const float (&sg)[2], __amdgpu_buffer_rsrc_t yr, int lane) {
-    const bool pair = d.flags & kPair;
-    const int nmat = pair ? 2 : 1;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    constexpr int QB = ROWS <= 2 ? 8 : ROWS <= 4 ? 4 : ROWS <= 8 ? 2 : 1;   // pieces per round: at most 32 values per lane
-    float tq[ROWS][2];
+    constexpr int QB = final_sum_qb<ROWS, NM>();
+    float tq[ROWS][NM];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) tq[r][0] = tq[r][1] = 0.0f;
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) tq[r][m] = 0.0f;
     for (int q0 = 0; q0 < np; q0 += QB) {
-        float pv[ROWS][2][QB];
+        float pv[ROWS][NM][QB];
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
-            const int pq = min(q0 + j, np - 1);
-            const size_t qs = ((size_t)sh * d.max_pieces + pq) * nmat;
+            const size_t qs = ((size_t)sh * d.max_pieces + min(q0 + j, np - 1)) * NM;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int m = 0; m < NM; ++m)
 #pragma unroll
                 for (int r = 0; r < ROWS; ++r)
-                    pv[r][m][j] = __hip_atomic_load(&a.partial[((qs + (pair ? m : 0)) * ROWS + r) * kStripN + lane],
+                    pv[r][m][j] = __hip_atomic_load(&a.partial[((qs + m) * ROWS + r) * kStripN + lane],
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
@@ -392,10 +400,44 @@ __device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, i
 #pragma unroll
                 for (int r = 0; r < ROWS; ++r)
 #pragma unroll
-                    for (int m = 0; m < 2; ++m) tq[r][m] += pv[r][m][j];
+                    for (int m = 0; m < NM; ++m) tq[r][m] += pv[r][m][j];
     }
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) epilogue<ROWS>(d, yr, tq[r][0], tq[r][1], sg, d.G * d.F + sh, r, lane);
+    for (int r = 0; r < ROWS; ++r)
+        epilogue<ROWS>(d, yr, tq[r][0], tq[r][NM - 1], sg, d.G * d.F + sh, r, lane);
+}
+
+// The same sums spread over the workgroup's waves: wave w takes rows w,
+// w + nwb, ..., each in rounds of 32 / NM pieces, into fs[m][r][lane] (LDS)
+// for wave 0 to write.  The order of every sum is the one above.
+template <int ROWS, int NM>
+__device__ __forceinline__ void sum_pieces(const SeqArgs &a, const CallDesc &d, int sh, int np, int wave, int nwb,
+                                           int lane, float *fs) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    constexpr int QB = 32 / NM;
+    for (int r = wave; r < ROWS; r += nwb) {
+        float t[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) t[m] = 0.0f;
+        for (int q0 = 0; q0 < np; q0 += QB) {
+            float pv[NM][QB];
+#pragma unroll
+            for (int j = 0; j < QB; ++j) {
+                const size_t qs = ((size_t)sh * d.max_pieces + min(q0 + j, np - 1)) * NM;
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    pv[m][j] = __hip_atomic_load(&a.partial[((qs + m) * ROWS + r) * kStripN + lane],
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int j = 0; j < QB; ++j)
+                if (q0 + j < np)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) t[m] += pv[m][j];
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) fs[(m * ROWS + r) * kStripN + lane] = t[m];
+    }
 }
 
 // Wait until every load and store of this wave issued so far has completed.
@@ -430,16 +472,14 @@ __device__ __forceinline__ void lane0_store(unsigned *p, unsigned v, int lane) {
     if (lane == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave 0: count this workgroup's piece of shared strip sh; the workgroup
-// whose count completes it sums the strip and clears the counter.
-template <int ROWS>
-__device__ __forceinline__ void arrive_piece(const SeqArgs &a, const CallDesc &d, int sh, int np,
-                                             const float (&sg)[2], __amdgpu_buffer_rsrc_t yr, int lane) {
+// Wave 0: count this workgroup's piece of shared strip sh; true for the
+// workgroup whose count completes it, which clears the counter and sums the
+// strip.
+__device__ __forceinline__ bool arrive_piece(const SeqArgs &a, int sh, int np, int lane) {
     unsigned *cnt = a.counters + sh * 32;
-    if (lane0_add(cnt, lane) == (unsigned)(np - 1)) {
-        lane0_store(cnt, 0u, lane);
-        final_sum<ROWS>(a, d, sh, np, sg, yr, lane);
-    }
+    if (lane0_add(cnt, lane) != (unsigned)(np - 1)) return false;
+    lane0_store(cnt, 0u, lane);
+    return true;
 }
 
 // Wave 0: the wait between calls (epoch e = calls finished so far).  Each
@@ -521,6 +561,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     // the kernel arguments at the start of every call costs a cache miss each
     // time; from LDS it is a few cycles.  The words are wave-uniform.
     __shared__ CallDesc s_calls[SEQ ? kSeqMax : 1];
+    __shared__ unsigned s_fin;   // shared strips this workgroup completes (bits 0, 1)
     constexpr int kDescWords = sizeof(CallDesc) / 4;
     if (SEQ) {
         const uint32_t *src = reinterpret_cast<const uint32_t *>(a.call);
@@ -708,14 +749,64 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             finish_segment<ROWS, AR>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
         }
-        if (wave == 0) {
-            if (pub[0] | pub[1]) {
+        // Pieces of shared strips: wave 0 counts them; where this workgroup's
+        // count completes a strip, it is summed either by wave 0 alone or by
+        // every wave, some rows each, into LDS (`red`, free once wave 0 has
+        // read its last segment's sums), and wave 0 writes the outputs.
+        // Whether a piece was published follows from the geometry, so every
+        // wave takes the same branch.
+        const bool pieces = (q.nsh > 0 && q.np0 > 1) || (q.nsh > 1 && q.np1 > 1);
+        // Wave 0 alone needs a round trip per QB pieces; the other waves have
+        // the next call's first super-tiles in flight (from 3 rows on), and
+        // their loads wait behind those: they help only where wave 0 alone
+        // would need more than 4 rounds (measured: 2 rounds alone beat help).
+        const int qb0 = pair ? final_sum_qb<ROWS, 2>() : final_sum_qb<ROWS, 1>();
+        const int np_max = max(q.nsh > 0 ? q.np0 : 1, q.nsh > 1 ? q.np1 : 1);
+        const bool spread = !kLateFetch && nwb > 1 && np_max > 4 * qb0;
+        if (pieces && !spread) {
+            if (wave == 0) {
                 wait_own_writes();   // the partials are visible before they are counted
-                if (pub[0]) arrive_piece<ROWS>(a, d, q.fs, q.np0, sg, yr, lane);
-                if (pub[1]) arrive_piece<ROWS>(a, d, q.fs + 1, q.np1, sg, yr, lane);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int np = h ? q.np1 : q.np0;
+                    if (pub[h] && arrive_piece(a, q.fs + h, np, lane)) {
+                        if (pair) final_sum<ROWS, 2>(a, d, q.fs + h, np, sg, yr, lane);
+                        else final_sum<ROWS, 1>(a, d, q.fs + h, np, sg, yr, lane);
+                    }
+                }
             }
-            if (has_next) released = arrive_call(a, g, (unsigned)(c + 1), lane);
+        } else if (pieces) {
+            if (wave == 0) {
+                wait_own_writes();   // the partials are visible before they are counted
+                unsigned fin = 0;
+                if (pub[0] && arrive_piece(a, q.fs, q.np0, lane)) fin |= 1u;
+                if (pub[1] && arrive_piece(a, q.fs + 1, q.np1, lane)) fin |= 2u;
+                if (lane == 0) s_fin = fin;
+            }
+            __syncthreads();
+            const unsigned fin = (unsigned)__builtin_amdgcn_readfirstlane((int)s_fin);
+            if (fin) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    if (fin & (1u << h)) {
+                        float *fs = red + 2 * h * ROWS * kStripN;
+                        if (pair) sum_pieces<ROWS, 2>(a, d, q.fs + h, h ? q.np1 : q.np0, wave, nwb, lane, fs);
+                        else sum_pieces<ROWS, 1>(a, d, q.fs + h, h ? q.np1 : q.np0, wave, nwb, lane, fs);
+                    }
+                __syncthreads();
+                if (wave == 0) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        if (fin & (1u << h))
+#pragma unroll
+                            for (int r = 0; r < ROWS; ++r)
+                                epilogue<ROWS>(d, yr, red[((2 * h) * ROWS + r) * kStripN + lane],
+                                               red[((2 * h + 1) * ROWS + r) * kStripN + lane], sg,
+                                               d.G * d.F + q.fs + h, r, lane);
+                }
+            }
         }
+        if (wave == 0 && has_next) released = arrive_call(a, g, (unsigned)(c + 1), lane);
         if (has_next) {
             if (kLateFetch) __syncthreads();   // wave 0 has counted the call done
             if ((kLateFetch || wave == 0) && nxt.fetch) {
@@ -866,7 +957,9 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
 
 size_t stream_lds_bytes(int rows, int waves) {
     const size_t lds_x = (size_t)waves * x_stage_bytes(rows);
-    const size_t lds_red = (size_t)waves * 2 * red_rows(rows) * kStripN * sizeof(float);
+    // the wave-reduction slots; they also hold the final sums of up to two
+    // shared strips (4 x rows x 64 floats), hence at least two waves' worth
+    const size_t lds_red = (size_t)(waves < 2 ? 2 : waves) * 2 * red_rows(rows) * kStripN * sizeof(float);
     // at least ~81 KB so that no CU ever holds two of these workgroups
     return lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;
 }
