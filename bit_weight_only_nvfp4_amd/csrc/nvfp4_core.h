@@ -308,54 +308,82 @@ __device__ __forceinline__ void core_mx1(const uint4 (&wc)[kCodeChunks / 2], con
 template <int ROWS>
 struct XStage16 {
     static constexpr int XR = (ROWS * 32 + 63) / 64;   // 16-byte activation chunks per lane
+    static constexpr int RA = 2 * XR;                  // rows staged: ROWS rounded up to even
     static constexpr int ROW_BYTES = 528;              // 256 fp16 + 16 (rows start 4 banks apart)
-    static constexpr int ZERO_OFF = ROWS * ROW_BYTES;  // 16 zero bytes: the A rows past ROWS
-    // per product row (16): the float undoing its row's scale, zero past ROWS
-    // (zeroed with the 16 bytes before it, once per launch)
+    static constexpr int ZERO_OFF = RA * ROW_BYTES;    // 16 zero bytes: the A rows past ROWS
+    // per product row (16): the float undoing its row's scale (zero past RA,
+    // zeroed with the 16 bytes before it, once per launch)
     static constexpr int SCALE_OFF = ZERO_OFF + 16;
     static constexpr int WS_OFF = SCALE_OFF + 64;      // the lanes' 16-byte group-scale entries
     static constexpr int BYTES = WS_OFF + 1024;
     static constexpr int ZERO_WORDS = 20;              // zero bytes and row scales, as words
 };
 
+// Largest of the two 16-bit halves of m over the 32 lanes of each half-wave:
+// within rows of 16 lanes by DPP (quads, half-rows, rows), then across the
+// two rows of a half-wave with one v_permlane16_swap, whose two results hold
+// rows 2 h and 2 h + 1 in some order (the maximum does not depend on it).
+__device__ __forceinline__ uint32_t halfwave_max_u16x2(uint32_t m) {
+    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));   // row_mirror
+    const auto r = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    return pk_max_u16(r[0], r[1]);
+}
+
+// Two fp32 values times sc, each rounded once to fp16 (nearest even, fp16
+// denormals kept), packed low first: one v_fma_mixlo_f16 and one
+// v_fma_mixhi_f16 into the same register (the compiler splits such pairs
+// into multiplies, conversions and packs).
+__device__ __forceinline__ uint32_t mul_pk_f16(float lo, float hi, float sc) {
+    uint32_t out;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %3, %2, 0 op_sel_hi:[0,0,0]"
+        : "=&v"(out)
+        : "v"(lo), "v"(sc), "v"(hi));
+    return out;
+}
+
 // Stage the super-tile's activations as fp16, each row scaled by 2^(14 - E)
 // where its largest |x| in the super-tile is below 2^(E+1).  Chunk c = lane +
 // 64 i holds row c / 32, k = 8 (c % 32) .. + 7: the 32 lanes of a half-wave
-// hold one row.
+// hold one row.  Rows past ROWS are zeros (their loads read nothing) and are
+// staged like the others; no lane branches.
 template <int ROWS>
 __device__ __forceinline__ void stage_x16(const uint4 (&xv)[XStage16<ROWS>::XR], uint8_t *xs, int lane) {
     using S = XStage16<ROWS>;
+    constexpr int XR = S::XR, NP = (XR + 1) / 2;
+    // |x| maxima of each chunk, two chunks per word (chunk 2 j low, 2 j + 1 high)
+    uint32_t mp[NP];
 #pragma unroll
-    for (int i = 0; i < S::XR; ++i) {
+    for (int j = 0; j < NP; ++j) mp[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+        uint32_t m = pk_max_u16(pk_max_u16(xv[i].x & 0x7fff7fffu, xv[i].y & 0x7fff7fffu),
+                                pk_max_u16(xv[i].z & 0x7fff7fffu, xv[i].w & 0x7fff7fffu));
+        m = max(m & 0xffffu, m >> 16);
+        mp[i >> 1] |= (i & 1) ? m << 16 : m;
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) mp[j] = halfwave_max_u16x2(mp[j]);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
         const int c = lane + 64 * i;
         const int r = c >> 5, kk = (c & 31) * 8;
-        const uint32_t d[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-        uint32_t m = pk_max_u16(pk_max_u16(d[0] & 0x7fff7fffu, d[1] & 0x7fff7fffu),
-                                pk_max_u16(d[2] & 0x7fff7fffu, d[3] & 0x7fff7fffu));
-        m = max(m & 0xffffu, m >> 16);
-        // largest over the 32 lanes of the row: quads (lane ^ 1, lane ^ 2),
-        // half-rows and rows of 16 (mirrors), then the two rows of 16
-        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
-        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
-        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));   // row_half_mirror
-        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));   // row_mirror
-        m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+        const uint32_t m = (i & 1) ? mp[i >> 1] >> 16 : mp[i >> 1] & 0xffffu;
         // biased exponent of the row's largest |x|, kept where both scales are
         // normal floats (rows of all zeros or of tiny values take the bottom)
         const int ef = min(max((int)(m >> 7), 15), 254);
         const float sc = __builtin_bit_cast(float, (268 - ef) << 23);    // 2^(141 - ef) = 2^(14 - E)
         const float un = __builtin_bit_cast(float, (ef - 14) << 23);     // 2^(E - 14)
-        typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-        half8_t h;
+        const uint32_t d[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        uint32_t h[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            h[2 * q] = (_Float16)(__builtin_bit_cast(float, d[q] << 16) * sc);
-            h[2 * q + 1] = (_Float16)(__builtin_bit_cast(float, d[q] & 0xffff0000u) * sc);
-        }
-        if (r < ROWS) {
-            *reinterpret_cast<half8_t *>(xs + r * S::ROW_BYTES + kk * 2) = h;
-            if ((c & 31) == 0) *reinterpret_cast<float *>(xs + S::SCALE_OFF + r * 4) = un;
-        }
+        for (int q = 0; q < 4; ++q)
+            h[q] = mul_pk_f16(__builtin_bit_cast(float, d[q] << 16), __builtin_bit_cast(float, d[q] & 0xffff0000u), sc);
+        *reinterpret_cast<uint4 *>(xs + r * S::ROW_BYTES + kk * 2) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<float *>(xs + S::SCALE_OFF + r * 4) = un;   // the row's 32 lanes store the same value
     }
 }
 

@@ -151,7 +151,7 @@ __host__ __device__ constexpr int pipe_depth_for_rows(int rows) { return 2; }
 constexpr int kF16FromRows = 5;
 __host__ __device__ constexpr bool use_f16_core(int rows) { return rows >= kF16FromRows; }
 __host__ __device__ constexpr int x_stage_bytes(int rows) {
-    return use_f16_core(rows) ? rows * 528 + 16 + 64 + 1024 : rows == 1 ? 2112 : 2304 * ((rows + 3) / 4) + 32;
+    return use_f16_core(rows) ? (rows + 1) / 2 * 2 * 528 + 16 + 64 + 1024 : rows == 1 ? 2112 : 2304 * ((rows + 3) / 4) + 32;
 }
 
 // Rows per wave-reduction slot (a wave's sums of one matrix for one strip):
