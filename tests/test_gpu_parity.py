@@ -224,6 +224,30 @@ def test_dual_random_all_rows(nv, n, k):
         check.check_dual(o32, o16, d, label="dual %dx%d rows=%d" % (n, k, rows))
 
 
+@pytest.mark.parametrize("n,k", [(130, 4112), (300, 4352), (72, 17408)])
+def test_rows_invariant_within_tier(nv, n, k):
+    """A row's result does not depend on how many rows share the call, within
+    one arithmetic tier: rows 5-16 (fp16 products) and rows 2-4 (block-scaled
+    products) give every row bit-identical fp32 and bf16 outputs whatever the
+    call's row count (the plan, the per-row activation scales, the product
+    rows and every summation order are independent of the row count).  Single
+    projection and gate/up pair; shapes with and without split-K pieces."""
+    c = workloads.case(n, k, 16, seed=n + 7 * k, dual=True)
+    gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
+    gw, uw = _pack(nv, gq), _pack(nv, uq)
+    for tier in ((5, 16), (2, 4)):
+        lo, hi = tier
+        y_ref, y16_ref = _run_gemv(nv, gw, c["x"][:hi])
+        o_ref, o16_ref = _run_dual(nv, gw, uw, c["x"][:hi])
+        for rows in range(lo, hi):
+            y, y16 = _run_gemv(nv, gw, c["x"][:rows])
+            o, o16 = _run_dual(nv, gw, uw, c["x"][:rows])
+            assert np.array_equal(y.view(np.uint32), y_ref[:rows].view(np.uint32)), (n, k, rows)
+            assert np.array_equal(y16, y16_ref[:rows]), (n, k, rows)
+            assert np.array_equal(o.view(np.uint32), o_ref[:rows].view(np.uint32)), (n, k, rows)
+            assert np.array_equal(o16, o16_ref[:rows]), (n, k, rows)
+
+
 def _wide_x(rng, rows, k, binades):
     """bf16 activations sign * 2^u, u uniform over [-binades, binades]: groups
     and super-tiles whose values span up to 2 * binades binades."""
