@@ -64,7 +64,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="1,2,4,8,16", help="row counts to time; the first is the headline")
+    ap.add_argument("--rows", default="1,2,4,8,16,32", help="row counts to time; the first is the headline")
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4_hip.so")
 
 NVFP4_LAYOUT_MAGIC = 0x34465056
 NVFP4_LAYOUT_VERSION = 2
-NVFP4_MAX_ROWS = 16
+NVFP4_MAX_ROWS = 128
 NVFP4_OUT_BF16 = 0
 NVFP4_OUT_F32 = 1
 

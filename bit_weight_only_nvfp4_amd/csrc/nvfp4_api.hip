@@ -129,16 +129,54 @@ int check_overlaps(const char *fn, const StreamCall *calls, int ncalls, const vo
     return NVFP4_OK;
 }
 
-StreamCall make_call(const nvfp4_weight *w, const nvfp4_weight *up, const void *x, int rows, void *y,
-                     int out_dtype) {
-    StreamCall c{};
-    c.plan = make_stream_plan(w->n, w->k, rows, up != nullptr);
-    c.w0 = w->data;
-    c.w1 = up ? up->data : nullptr;
-    c.x = x;
-    c.y = y;
-    c.out_f32 = out_dtype == NVFP4_OUT_F32;
-    return c;
+// A call of more than kKernelMaxRows rows runs as ceil(rows / 16) calls of
+// balanced row counts (every chunk has at least rows / nchunks rows, so from
+// 5 rows on every chunk stays on the fp16 products and a row's result does
+// not depend on the call's row count); each chunk reads the weights once.
+int num_chunks(int rows) { return (rows + kKernelMaxRows - 1) / kKernelMaxRows; }
+
+void chunk_of(int rows, int j, int &r0, int &nr) {
+    const int nch = num_chunks(rows), base = rows / nch, extra = rows % nch;
+    r0 = j * base + (j < extra ? j : extra);
+    nr = base + (j < extra ? 1 : 0);
+}
+
+// Append the calls one projection or pair call runs as (one per row chunk).
+void add_calls(std::vector<StreamCall> &out, const nvfp4_weight *w, const nvfp4_weight *up, const void *x,
+               int rows, void *y, int out_dtype) {
+    const size_t ybytes = out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    for (int j = 0; j < num_chunks(rows); ++j) {
+        int r0, nr;
+        chunk_of(rows, j, r0, nr);
+        StreamCall c{};
+        c.plan = make_stream_plan(w->n, w->k, nr, up != nullptr);
+        c.w0 = w->data;
+        c.w1 = up ? up->data : nullptr;
+        c.x = static_cast<const uint8_t *>(x) + (size_t)r0 * w->k * 2;
+        c.y = static_cast<uint8_t *>(y) + (size_t)r0 * w->n * ybytes;
+        c.out_f32 = out_dtype == NVFP4_OUT_F32;
+        out.push_back(c);
+    }
+}
+
+// Plans only (for the size queries): the chunk row counts of a call.
+void add_plans(std::vector<StreamCall> &out, int64_t n, int64_t k, int rows, bool dual) {
+    for (int j = 0; j < num_chunks(rows); ++j) {
+        int r0, nr;
+        chunk_of(rows, j, r0, nr);
+        StreamCall c{};
+        c.plan = make_stream_plan(n, k, nr, dual);
+        out.push_back(c);
+    }
+}
+
+// A call's outputs may not overlap its own activations (checked on the whole
+// call, before it is cut into row chunks).
+int check_self_overlap(const char *fn, const nvfp4_weight *w, const void *x, int rows, const void *y,
+                       int out_dtype) {
+    const size_t xb = (size_t)rows * w->k * 2, yb = (size_t)rows * w->n * (out_dtype == NVFP4_OUT_F32 ? 4 : 2);
+    if (overlap(y, yb, x, xb)) return fail(NVFP4_E_OVERLAP, "%s: y overlaps its x", fn);
+    return NVFP4_OK;
 }
 
 // Validate one projection or pair call (everything but the workspace).
@@ -160,14 +198,18 @@ int run_one(const char *fn, const nvfp4_weight *w, const nvfp4_weight *up, const
             int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_call(fn, w, up, x, rows, y, out_dtype);
     if (st) return st;
-    const StreamCall c = make_call(w, up, x, rows, y, out_dtype);
-    st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(&c, 1));
+    st = check_self_overlap(fn, w, x, rows, y, out_dtype);
     if (st) return st;
-    st = check_overlaps(fn, &c, 1, workspace, workspace_bytes);
+    std::vector<StreamCall> sc;
+    add_calls(sc, w, up, x, rows, y, out_dtype);
+    const int nc = (int)sc.size();
+    st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(sc.data(), nc));
+    if (st) return st;
+    st = check_overlaps(fn, sc.data(), nc, workspace, workspace_bytes);
     if (st) return st;
     st = check_device(fn);
     if (st) return st;
-    return hip_status(fn, launch_sequence(&c, 1, workspace, static_cast<hipStream_t>(stream)));
+    return hip_status(fn, launch_sequence(sc.data(), nc, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -281,9 +323,9 @@ int nvfp4_quantize(const float *W, int64_t n, int64_t k, void *packed, size_t pa
 
 size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual) {
     if (!valid_shape(n, k) || rows < 1 || rows > NVFP4_MAX_ROWS) return 0;
-    StreamCall c{};
-    c.plan = make_stream_plan(n, k, rows, dual != 0);
-    return sequence_workspace_bytes(&c, 1);
+    std::vector<StreamCall> sc;
+    add_plans(sc, n, k, rows, dual != 0);
+    return sequence_workspace_bytes(sc.data(), (int)sc.size());
 }
 
 int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype, void *workspace,
@@ -304,9 +346,7 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls) {
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
         if (!c.w || !valid_shape(c.w->n, c.w->k) || c.rows < 1 || c.rows > NVFP4_MAX_ROWS) continue;
-        StreamCall s{};
-        s.plan = make_stream_plan(c.w->n, c.w->k, c.rows, c.up != nullptr);
-        sc.push_back(s);
+        add_plans(sc, c.w->n, c.w->k, c.rows, c.up != nullptr);
     }
     return sequence_workspace_bytes(sc.data(), (int)sc.size());
 }
@@ -317,11 +357,16 @@ int nvfp4_sequence_launches(const nvfp4_call *calls, int ncalls) {
     sc.reserve(ncalls);
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
-        StreamCall s{};
-        s.plan.rows = c.rows;
-        sc.push_back(s);
+        if (c.rows < 1 || c.rows > NVFP4_MAX_ROWS) continue;
+        for (int j = 0; j < num_chunks(c.rows); ++j) {
+            int r0, nr;
+            chunk_of(c.rows, j, r0, nr);
+            StreamCall s{};
+            s.plan.rows = nr;
+            sc.push_back(s);
+        }
     }
-    return sequence_launches(sc.data(), ncalls);
+    return sequence_launches(sc.data(), (int)sc.size());
 }
 
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
@@ -331,30 +376,37 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
     if (ncalls == 0) return ok();
     if (!calls) return fail(NVFP4_E_NULL, "%s: calls is NULL", fn);
     char name[64];
-    std::vector<StreamCall> sc((size_t)ncalls);
+    std::vector<StreamCall> sc;
+    std::vector<int> first((size_t)ncalls + 1);   // call i runs as sc[first[i] .. first[i + 1])
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
         snprintf(name, sizeof name, "%s call %d", fn, i);
         int st = check_call(name, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
         if (st) return st;
-        sc[i] = make_call(c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
+        st = check_self_overlap(name, c.w, c.x, c.rows, c.y, c.out_dtype);
+        if (st) return st;
+        first[i] = (int)sc.size();
+        add_calls(sc, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
     }
-    int st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(sc.data(), ncalls));
+    first[ncalls] = (int)sc.size();
+    const int nsc = (int)sc.size();
+    int st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(sc.data(), nsc));
     if (st) return st;
-    st = check_overlaps(fn, sc.data(), ncalls, workspace, workspace_bytes);
+    st = check_overlaps(fn, sc.data(), nsc, workspace, workspace_bytes);
     if (st) return st;
     st = check_device(fn);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!events) return hip_status(fn, launch_sequence(sc.data(), ncalls, workspace, s));
-    // per-call timing: one launch per call, each between its two events
+    if (!events) return hip_status(fn, launch_sequence(sc.data(), nsc, workspace, s));
+    // per-call timing: each call (all its row chunks) launched between its two events
     for (int i = 0; i < ncalls; ++i) {
         if (events[2 * i]) {
             hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[2 * i]), s);
             if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: hipEventRecord before call %d: %s", fn, i,
                                              hipGetErrorString(e));
         }
-        hipError_t e = launch_sequence(&sc[i], 1, workspace, s);
+        hipError_t e = hipSuccess;
+        for (int j = first[i]; j < first[i + 1] && e == hipSuccess; ++j) e = launch_sequence(&sc[j], 1, workspace, s);
         if (e != hipSuccess) return fail(NVFP4_E_HIP, "%s: launch of call %d failed: %s", fn, i, hipGetErrorString(e));
         if (events[2 * i + 1]) {
             e = hipEventRecord(static_cast<hipEvent_t>(events[2 * i + 1]), s);

@@ -123,6 +123,10 @@ constexpr int kMaxWorkgroups = 256;      // one per CU on MI355X
 constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workgroup
 constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
 constexpr int kMaxWavesPerWg = 8;
+// Rows one kernel call computes (the instantiated row counts are 1..16);
+// calls of more rows are cut into row chunks by the host.
+constexpr int kKernelMaxRows = 16;
+static_assert(NVFP4_MAX_ROWS >= kKernelMaxRows, "the ABI's row limit covers the kernel's");
 // Waves per workgroup and super-tiles each wave keeps in flight (NB, even,
 // so that a pair's gate and up super-tiles of one position are always in
 // flight together).  The super-tiles in flight live in registers.  Two waves

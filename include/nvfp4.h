@@ -3,7 +3,7 @@
  *
  * Weight-only 4-bit projection ("w4a16" GEMV): weights are NVFP4 -- E2M1 codes,
  * one OCP E4M3 scale per 16 consecutive weights of an output row, one FP32
- * per-tensor scale -- and activations are bf16, 1..16 rows per call.  The
+ * per-tensor scale -- and activations are bf16, 1..128 rows per call.  The
  * format and kernel family are the ones named on the Qwen3.8-27B-NVFP4
  * blueprint page: "Precision" table (weights nvfp4/g16, activations bf16) and
  * "Kernels" table (w4a16_gemv_qg / _sw / _dual / _dual_sw, with the planner
@@ -62,7 +62,7 @@ extern "C" {
 #define NVFP4_ABI_VERSION 1
 #define NVFP4_LAYOUT_MAGIC 0x34465056u /* "VPF4" */
 #define NVFP4_LAYOUT_VERSION 2u
-#define NVFP4_MAX_ROWS 16
+#define NVFP4_MAX_ROWS 128
 
 enum {
     NVFP4_OK = 0,
@@ -145,7 +145,12 @@ size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual);
  * (NVFP4_OUT_BF16, round to nearest even) or fp32 (NVFP4_OUT_F32), aligned
  * to its element size; y must not overlap x, the weight or the workspace
  * (NVFP4_E_OVERLAP).  fp32 accumulation; results are bitwise deterministic
- * run to run.
+ * run to run.  A kernel computes up to 16 rows; a call of more rows runs as
+ * ceil(rows / 16) chunks of balanced row counts, each reading the weights
+ * once (the pages' wider row tiers: up to 32 draft and 128 multi-sequence
+ * rows).  From 5 rows on, a row's result does not depend on the call's row
+ * count (the same holds among 2..4 rows); across those tiers it differs by
+ * fp32 rounding only.
  * workspace: >= nvfp4_workspace_bytes(n, k, rows, 0) bytes, 16-byte aligned,
  * ZERO-FILLED before its first use.  Its first 65 KiB hold counters at fixed
  * positions and every call returns them to zero, so one workspace serves any

@@ -64,7 +64,12 @@ def test_workspace_bytes(nv):
     assert w1 > 0 and w1 == nv.nvfp4_workspace_bytes(5120, 17408, 1)
     assert nv.nvfp4_workspace_bytes(5120, 17408, 8) > w1
     assert nv.nvfp4_workspace_bytes(17408, 5120, 1, dual=True) > nv.nvfp4_workspace_bytes(17408, 5120, 1) > 0
-    for bad in [(256, 512, 0), (256, 512, 9), (0, 512, 1), (256, 24, 1)]:
+    # more than 16 rows run as row chunks, whose waits need the counters (65 KiB)
+    assert nv.nvfp4_workspace_bytes(256, 512, 16) == 0
+    assert nv.nvfp4_workspace_bytes(256, 512, 17) == 65 * 1024
+    assert nv.nvfp4_workspace_bytes(256, 512, 128) == 65 * 1024
+    assert nv.nvfp4_workspace_bytes(5120, 17408, 128) == nv.nvfp4_workspace_bytes(5120, 17408, 16)
+    for bad in [(256, 512, 0), (256, 512, 129), (0, 512, 1), (256, 24, 1)]:
         assert nv.nvfp4_workspace_bytes(*bad) == 0
     assert nv.nvfp4_quantize_workspace_bytes(256, 512) > 0
     assert nv.nvfp4_quantize_workspace_bytes(256, 20) == 0
@@ -101,7 +106,7 @@ def test_gemv_argument_errors(nv):
     assert _gemv(nv, _weight(nv), x=None) == E["NVFP4_E_NULL"]
     assert _gemv(nv, _weight(nv), y=None) == E["NVFP4_E_NULL"]
     assert _gemv(nv, _weight(nv), rows=0) == E["NVFP4_E_ROWS"]
-    assert _gemv(nv, _weight(nv), rows=17) == E["NVFP4_E_ROWS"]
+    assert _gemv(nv, _weight(nv), rows=129) == E["NVFP4_E_ROWS"]
     assert _gemv(nv, _weight(nv), dtype=2) == E["NVFP4_E_DTYPE"]
     assert _gemv(nv, _weight(nv), x=XF + 2) == E["NVFP4_E_ALIGN"]
     assert _gemv(nv, _weight(nv), y=YF + 1) == E["NVFP4_E_ALIGN"]
@@ -175,7 +180,7 @@ def test_sequence_argument_errors(nv):
     assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_LAYOUT"]
     assert "call 2" in nv.nvfp4_last_error()
     arr[2].w = ctypes.pointer(good)
-    arr[1].rows = 17
+    arr[1].rows = 129
     assert L.nvfp4_gemv_sequence(arr, 3, None, 0, None, None) == E["NVFP4_E_ROWS"]
     assert "call 1" in nv.nvfp4_last_error()
     arr[1].rows = 8
@@ -195,6 +200,12 @@ def test_sequence_argument_errors(nv):
     assert L.nvfp4_sequence_workspace_bytes(arr, 1) == 0
     assert L.nvfp4_sequence_launches(arr, 0) == 0 and L.nvfp4_sequence_launches(None, 3) == 0
     assert 1 <= L.nvfp4_sequence_launches(arr, 3) <= 3
+    # a call of 40 rows runs as three row chunks (14, 13, 13): one call alone
+    # needs the counters, and up to three launches
+    arr[0].rows = 40
+    assert L.nvfp4_sequence_workspace_bytes(arr, 1) == 65 * 1024
+    assert 2 <= L.nvfp4_sequence_launches(arr, 1) <= 3
+    arr[0].rows = 1
     assert L.nvfp4_gemv_sequence(None, 3, None, 0, None, None) == E["NVFP4_E_NULL"]
 
 

@@ -248,6 +248,88 @@ def test_rows_invariant_within_tier(nv, n, k):
             assert np.array_equal(o16, o16_ref[:rows]), (n, k, rows)
 
 
+# ---- more than 16 rows: row chunks ----------------------------------------------
+
+MANY_ROWS = (17, 24, 32, 33, 64, 128)
+
+
+def _oracle_rows(fn, *args, x):
+    """The oracle takes up to 64 rows per call; every output row depends on its
+    own activation row only, so larger row counts go through it in blocks."""
+    parts = [fn(*args, x[r:r + 64]) for r in range(0, x.shape[0], 64)]
+    if isinstance(parts[0], dict):
+        return {key: np.concatenate([p[key] for p in parts]) for key in parts[0]}
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(len(parts[0])))
+
+
+@pytest.mark.parametrize("n,k", [(130, 4112), (300, 784), (72, 17408)])
+def test_gemv_random_many_rows(nv, n, k):
+    """Calls of 17..128 rows (the pages' draft and multi-sequence row tiers)
+    run as balanced chunks of at most 16 rows; every output against the
+    oracle, with and without split-K pieces."""
+    for rows in MANY_ROWS:
+        c = workloads.case(n, k, rows, seed=400 * rows + n, outlier_frac=0.01)
+        q = oracle.quantize(c["W"])
+        y32, y16 = _run_gemv(nv, _pack(nv, q), c["x"])
+        ref, absd, ref16 = _oracle_rows(oracle.gemv, *q, x=c["x"])
+        check.check_gemv(y32, y16, ref, absd, ref16, label="gemv %dx%d rows=%d" % (n, k, rows))
+
+
+def test_dual_random_many_rows(nv):
+    for rows in (17, 32, 128):
+        c = workloads.case(130, 4112, rows, seed=500 + rows, dual=True)
+        gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
+        o32, o16 = _run_dual(nv, _pack(nv, gq), _pack(nv, uq), c["x"])
+        d = _oracle_rows(oracle.gemv_dual_silu, gq, uq, x=c["x"])
+        check.check_dual(o32, o16, d, label="dual 130x4112 rows=%d" % rows)
+
+
+@pytest.mark.parametrize("n,k", [(130, 4112), (72, 17408)])
+def test_rows_invariant_across_chunks(nv, n, k):
+    """From 5 rows on every row chunk runs on the fp16 products, so a row's
+    result is the same bits in a call of any row count 5..128."""
+    c = workloads.case(n, k, 128, seed=n + 11 * k, dual=True)
+    gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
+    gw, uw = _pack(nv, gq), _pack(nv, uq)
+    y_ref, y16_ref = _run_gemv(nv, gw, c["x"])
+    o_ref, o16_ref = _run_dual(nv, gw, uw, c["x"])
+    for rows in (5, 16, 17, 37, 64, 100):
+        y, y16 = _run_gemv(nv, gw, c["x"][:rows])
+        o, o16 = _run_dual(nv, gw, uw, c["x"][:rows])
+        assert np.array_equal(y.view(np.uint32), y_ref[:rows].view(np.uint32)), (n, k, rows)
+        assert np.array_equal(y16, y16_ref[:rows]), (n, k, rows)
+        assert np.array_equal(o.view(np.uint32), o_ref[:rows].view(np.uint32)), (n, k, rows)
+        assert np.array_equal(o16, o16_ref[:rows]), (n, k, rows)
+
+
+def test_sequence_with_many_row_calls(nv):
+    """A call list whose calls have 40 rows (three row chunks each), the
+    second reading the first's output as its activations, equals the calls
+    made one by one, bit for bit, with and without per-call events; the
+    workspace's counters are back at zero afterwards."""
+    dev = torch.device("cuda")
+    c1 = workloads.case(320, 784, 40, seed=61)
+    c2 = workloads.case(130, 320, 1, seed=62)
+    w1 = _pack(nv, oracle.quantize(c1["W"]))
+    w2 = _pack(nv, oracle.quantize(c2["W"]))
+    x1 = _x_dev(c1["x"])
+    y1 = torch.empty((40, 320), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((40, 130), dtype=torch.float32, device=dev)
+    seq = nv.Sequence([(w1, None, x1, y1), (w2, None, y1, y2)])
+    ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device=dev)
+    for events in (None, [None] * 4):
+        y1.zero_()
+        y2.zero_()
+        seq.launch(ws, events=events)
+        torch.cuda.synchronize()
+        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+        a1 = nv.nvfp4_gemv(w1, x1)
+        a2 = nv.nvfp4_gemv(w2, a1, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(a1.view(torch.int16), y1.view(torch.int16))
+        assert torch.equal(a2.view(torch.int32), y2.view(torch.int32))
+
+
 def _wide_x(rng, rows, k, binades):
     """bf16 activations sign * 2^u, u uniform over [-binades, binades]: groups
     and super-tiles whose values span up to 2 * binades binades."""

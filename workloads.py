@@ -31,7 +31,7 @@ LAYER_PROJECTIONS = (
     ("down", 5120, 17408),
 )
 SWEEP_LAYERS = 64
-SWEEP_ROWS = (1, 2, 4, 8, 16)
+SWEEP_ROWS = (1, 2, 4, 8, 16, 32)
 
 
 def bf16_bits(x32: np.ndarray) -> np.ndarray:
