@@ -69,6 +69,8 @@ def _load():
                                        i64, i64, c_u16p, ctypes.c_int, c_i64p, i64,
                                        c_f64p, c_f64p, c_f64p, c_f64p, c_f64p, c_u16p]
     lib.nvo_gemv_dual_silu.restype = None
+    lib.nvo_dense_gemv.argtypes = [c_u16p, i64, i64, c_u16p, ctypes.c_int, c_i64p, i64, c_f64p, c_f64p, c_u16p]
+    lib.nvo_dense_gemv.restype = None
     lib.nvo_num_threads.argtypes = []
     lib.nvo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -201,3 +203,23 @@ def gemv_dual_silu(gate, up, x_bf16, sel=None):
 
 def num_threads() -> int:
     return int(_load().nvo_num_threads())
+
+
+def dense_gemv(W_bf16, x_bf16, sel=None):
+    """Dense bf16 projection in fp64.  W_bf16: uint16 [n, k], x_bf16: uint16
+    [rows, k] (bf16 bit patterns).  Returns (y fp64 [rows, nsel], sum|W*x| fp64
+    [rows, nsel], y_bf16 uint16 [rows, nsel])."""
+    W = _c(W_bf16, np.uint16)
+    x = _c(x_bf16, np.uint16)
+    n, k = W.shape
+    rows = x.shape[0]
+    if x.ndim != 2 or x.shape[1] != k or rows < 1:
+        raise ValueError("x must be [rows, k]")
+    sel, nsel = _sel(sel, n)
+    y = np.zeros((rows, nsel), np.float64)
+    a = np.zeros((rows, nsel), np.float64)
+    yb = np.zeros((rows, nsel), np.uint16)
+    _load().nvo_dense_gemv(_ptr(W, ctypes.c_uint16), n, k, _ptr(x, ctypes.c_uint16), rows,
+                           _ptr(sel, ctypes.c_int64), nsel, _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double),
+                           _ptr(yb, ctypes.c_uint16))
+    return y, a, yb

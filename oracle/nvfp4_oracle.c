@@ -280,3 +280,29 @@ int nvo_num_threads(void)
     return 1;
 #endif
 }
+
+/* ---- dense bf16 projection (the lm head's weights stay bf16: the
+ * Qwen3.8-27B-NVFP4 blueprint page, "Precision" table, bf16 x bf16 nodes, and
+ * its kernel table, gemv::dense_gemv_bf16):
+ * y[r][j] = sum_k W[j][k] x[r][k] in fp64, ascending k ---- */
+void nvo_dense_gemv(const uint16_t *W, int64_t n, int64_t k, const uint16_t *x, int rows,
+                    const int64_t *sel, int64_t nsel,
+                    double *y, double *absdot, uint16_t *y_bf16)
+{
+    if (!sel) nsel = n;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nsel; ++j) {
+        const int64_t feat = sel ? sel[j] : j;
+        for (int r = 0; r < rows; ++r) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t c = 0; c < k; ++c) {
+                double p = nvo_bf16_value(W[feat * k + c]) * nvo_bf16_value(x[(int64_t)r * k + c]);
+                acc += p;
+                aacc += fabs(p);
+            }
+            if (y) y[r * nsel + j] = acc;
+            if (absdot) absdot[r * nsel + j] = aacc;
+            if (y_bf16) y_bf16[r * nsel + j] = nvo_bf16_from_double(acc);
+        }
+    }
+}

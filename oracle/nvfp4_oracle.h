@@ -64,6 +64,12 @@ void nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g
                         uint16_t *o_bf16);
 int  nvo_num_threads(void);
 
+/* Dense bf16 projection: W bf16 [n][k], x bf16 [rows][k]; y, |D.x| sums and a
+ * bf16 copy of y for the selected features (sel NULL: all), [rows][nsel]. */
+void nvo_dense_gemv(const uint16_t *W, int64_t n, int64_t k, const uint16_t *x, int rows,
+                    const int64_t *sel, int64_t nsel,
+                    double *y, double *absdot, uint16_t *y_bf16);
+
 #ifdef __cplusplus
 }
 #endif
