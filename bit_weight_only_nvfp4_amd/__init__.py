@@ -39,7 +39,7 @@ EXPORTS = (
     "nvfp4_abi_version", "nvfp4_strerror", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
     "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
-    "nvfp4_gemv_sequence", "nvfp4_sequence_launches",
+    "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16",
 )
 
 
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "nvfp4_sequence_launches": ([ctypes.POINTER(nvfp4_call), ctypes.c_int], ctypes.c_int),
             "nvfp4_gemv_sequence": ([ctypes.POINTER(nvfp4_call), ctypes.c_int, vp, sz,
                                      ctypes.POINTER(ctypes.c_void_p), vp], ctypes.c_int),
+            "nvfp4_dense_gemv_bf16": ([vp, i64, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
         }
         for name, (argt, rest) in sig.items():
             f = getattr(L, name)
@@ -289,6 +290,21 @@ def nvfp4_gemv_dual_silu(gate: PackedWeight, up: PackedWeight, x: torch.Tensor, 
            lib().nvfp4_gemv_dual_silu(ctypes.byref(gate.desc), ctypes.byref(up.desc), _ptr(x), rows, _ptr(out),
                                       _OUT[out.dtype], _ptr(workspace),
                                       0 if workspace is None else workspace.numel(), _stream(x.device)))
+    return out
+
+
+def nvfp4_dense_gemv_bf16(W: torch.Tensor, x: torch.Tensor, out_dtype=torch.bfloat16,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[rows, n] = x[rows, k] @ W[n, k]^T with bf16 W (the lm head), fp32
+    accumulation."""
+    if W.dtype != torch.bfloat16 or W.dim() != 2:
+        raise TypeError("W must be a 2-D bfloat16 tensor")
+    W = W.contiguous()
+    n, k = W.shape
+    x, rows, out = _gemv_common(x, None, out_dtype, out, n)
+    _check("nvfp4_dense_gemv_bf16",
+           lib().nvfp4_dense_gemv_bf16(_ptr(W), n, k, _ptr(x), rows, _ptr(out), _OUT[out.dtype],
+                                       _stream(x.device)))
     return out
 
 

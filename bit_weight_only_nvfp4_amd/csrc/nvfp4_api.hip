@@ -369,6 +369,33 @@ int nvfp4_sequence_launches(const nvfp4_call *calls, int ncalls) {
     return sequence_launches(sc.data(), (int)sc.size());
 }
 
+int nvfp4_dense_gemv_bf16(const void *W, int64_t n, int64_t k, const void *x, int rows, void *y, int out_dtype,
+                          void *stream) {
+    static const char *fn = "nvfp4_dense_gemv_bf16";
+    if (!W) return fail(NVFP4_E_NULL, "%s: W is NULL", fn);
+    if (!valid_shape(n, k))
+        return fail(NVFP4_E_SHAPE, "%s: n=%lld k=%lld (need 1 <= n <= 2^20, k a positive multiple of 16, k <= 2^24)",
+                    fn, (long long)n, (long long)k);
+    if (!aligned(W, 16)) return fail(NVFP4_E_ALIGN, "%s: W is not 16-byte aligned", fn);
+    int st = check_gemv_args(fn, x, rows, y, out_dtype);
+    if (st) return st;
+    const size_t xb = (size_t)rows * k * 2, yb = (size_t)rows * n * (out_dtype == NVFP4_OUT_F32 ? 4 : 2);
+    if (overlap(y, yb, x, xb)) return fail(NVFP4_E_OVERLAP, "%s: y overlaps x", fn);
+    if (overlap(y, yb, W, (size_t)n * k * 2)) return fail(NVFP4_E_OVERLAP, "%s: y overlaps W", fn);
+    st = check_device(fn);
+    if (st) return st;
+    const size_t ye = out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    for (int j = 0; j < num_chunks(rows); ++j) {
+        int r0, nr;
+        chunk_of(rows, j, r0, nr);
+        hipError_t e = launch_dense(W, n, k, static_cast<const uint8_t *>(x) + (size_t)r0 * k * 2, nr,
+                                    static_cast<uint8_t *>(y) + (size_t)r0 * n * ye, out_dtype == NVFP4_OUT_F32,
+                                    static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_status(fn, e);
+    }
+    return ok();
+}
+
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
                         void *const *events, void *stream) {
     static const char *fn = "nvfp4_gemv_sequence";

@@ -195,6 +195,10 @@ hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace,
 // Launches launch_sequence makes for these calls.
 int sequence_launches(const StreamCall *calls, int ncalls);
 
+// Dense bf16 projection (rows <= kKernelMaxRows): y[r][j] = sum_k W[j][k] x[r][k].
+hipError_t launch_dense(const void *w, int64_t n, int64_t k, const void *x, int rows, void *y, int out_f32,
+                        hipStream_t stream);
+
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
                        int64_t n, int64_t k, void *packed, hipStream_t stream);
 hipError_t launch_unpack(const void *packed, int64_t n, int64_t k, uint8_t *codes,

@@ -202,6 +202,20 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
                         void *const *events, void *stream);
 
+/* Dense bf16 projection, for the projection whose weights stay bf16: the lm
+ * head (the Qwen3.8-27B-NVFP4 blueprint page, "Precision" table, bf16 x bf16
+ * nodes; its kernel table names the step gemv::dense_gemv_bf16).
+ * y[r][j] = sum_k W[j][k] x[r][k] for r < rows, j < n, fp32 accumulation.
+ * W: device bf16 [n][k] row-major (as stored), 16-byte aligned; n, k as for
+ * the NVFP4 calls (1 <= n <= 2^20, k a positive multiple of 16, k <= 2^24).
+ * x: device bf16 [rows][k], 16-byte aligned, rows 1..NVFP4_MAX_ROWS (a kernel
+ * pass takes up to 16 rows; more run as balanced row chunks, each reading W
+ * once).  y: device [rows][n], bf16 (NVFP4_OUT_BF16, RNE) or fp32, aligned to
+ * its element size, not overlapping W or x (NVFP4_E_OVERLAP).  No workspace;
+ * bitwise deterministic; enqueued on `stream`. */
+int nvfp4_dense_gemv_bf16(const void *W, int64_t n, int64_t k, const void *x, int rows, void *y,
+                          int out_dtype, void *stream);
+
 /* Number of kernel launches nvfp4_gemv_sequence makes for these calls without
  * events on the current device (one per call where shared launches are not
  * available); 0 if ncalls <= 0 or calls is NULL. */

@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(nv):
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     L = ctypes.CDLL(nv.LIB_PATH)
     for name in names:
         assert hasattr(L, name), name
@@ -207,6 +207,33 @@ def test_sequence_argument_errors(nv):
     assert 2 <= L.nvfp4_sequence_launches(arr, 1) <= 3
     arr[0].rows = 1
     assert L.nvfp4_gemv_sequence(None, 3, None, 0, None, None) == E["NVFP4_E_NULL"]
+
+
+def _dense(nv, W=FAKE, n=256, k=512, x=XF, rows=1, y=YF, dtype=0):
+    return nv.lib().nvfp4_dense_gemv_bf16(W, n, k, x, rows, y, dtype, None)
+
+
+def test_dense_gemv_argument_errors(nv):
+    """Every argument check of the dense bf16 projection runs before any HIP
+    call (these fake pointers are never dereferenced)."""
+    E = {v: k for k, v in nv.STATUS.items()}
+    assert _dense(nv, W=None) == E["NVFP4_E_NULL"]
+    assert "W is NULL" in nv.nvfp4_last_error()
+    assert _dense(nv, x=None) == E["NVFP4_E_NULL"]
+    assert _dense(nv, y=None) == E["NVFP4_E_NULL"]
+    assert _dense(nv, k=24) == E["NVFP4_E_SHAPE"]
+    assert _dense(nv, n=0) == E["NVFP4_E_SHAPE"]
+    assert _dense(nv, n=(1 << 20) + 1) == E["NVFP4_E_SHAPE"]
+    assert _dense(nv, rows=0) == E["NVFP4_E_ROWS"]
+    assert _dense(nv, rows=129) == E["NVFP4_E_ROWS"]
+    assert _dense(nv, dtype=2) == E["NVFP4_E_DTYPE"]
+    assert _dense(nv, W=FAKE + 8) == E["NVFP4_E_ALIGN"]
+    assert _dense(nv, x=XF + 2) == E["NVFP4_E_ALIGN"]
+    assert _dense(nv, y=YF + 2, dtype=1) == E["NVFP4_E_ALIGN"]
+    assert _dense(nv, y=XF + 256) == E["NVFP4_E_OVERLAP"]        # y inside x
+    assert "y overlaps x" in nv.nvfp4_last_error()
+    assert _dense(nv, y=FAKE + 4096) == E["NVFP4_E_OVERLAP"]     # y inside W
+    assert "y overlaps W" in nv.nvfp4_last_error()
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="valid arguments would launch on a real device")
