@@ -68,6 +68,7 @@ def parse_args():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense bf16 lm-head timing")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LAUNCHES_PER_STEP"),
                     help="write the rows=1 decode-step kernel's HBM traffic per launch from two rocprofv3 "
                          "--pmc counter collections (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run of "
@@ -257,6 +258,41 @@ def summarize_pmc(fetch_csv, write_csv, launches_per_step):
     print(json.dumps(t))
 
 
+DENSE_N, DENSE_K = 151936, 5120   # an lm head of a vocabulary-sized n (the pages give no vocabulary size)
+
+
+def time_dense(nv, torch, dev, rows_list, reps):
+    """The dense bf16 projection (nvfp4_dense_gemv_bf16) on a [151936 x 5120]
+    bf16 lm head: average duration of `reps` back-to-back calls (1.56 GB of
+    weights: nothing stays cached between them) between HIP events, per row
+    count; GB/s counts the weight bytes once per call."""
+    g = torch.Generator(device=dev).manual_seed(4321)
+    W = (torch.randn((DENSE_N, DENSE_K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    wbytes = DENSE_N * DENSE_K * 2
+    out = {"shape": [DENSE_N, DENSE_K], "weight_bytes": wbytes, "by_rows": {}}
+    stream = torch.cuda.current_stream()
+    for r in rows_list:
+        x = torch.randn((r, DENSE_K), generator=g, device=dev).to(torch.bfloat16)
+        y = torch.empty((r, DENSE_N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            nv.nvfp4_dense_gemv_bf16(W, x, out=y)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            nv.nvfp4_dense_gemv_bf16(W, x, out=y)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        us = start.elapsed_time(stop) * 1e3 / reps
+        gbs = wbytes / (us * 1e-6) / 1e9
+        out["by_rows"][str(r)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1),
+                                  "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        log("dense lm head %dx%d bf16, rows=%d: %.2f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (
+            DENSE_N, DENSE_K, r, us, gbs, 100 * gbs / HBM_PEAK_GBS))
+    del W
+    return out
+
+
 def main():
     args = parse_args()
     if args.summarize_pmc:
@@ -333,6 +369,11 @@ def main():
         "avg_launch_us": round(launch_us, 2),
     }
 
+    dense = None
+    if not args.no_dense:
+        dense = time_dense(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
+                           max(5, args.steps // 5))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on layer 0 ...")
@@ -365,6 +406,7 @@ def main():
         "by_rows": by_rows,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "dense_lm_head": dense,
     }
     print(json.dumps(line), flush=True)
 
