@@ -71,6 +71,9 @@ def _load():
     lib.nvo_gemv_dual_silu.restype = None
     lib.nvo_dense_gemv.argtypes = [c_u16p, i64, i64, c_u16p, ctypes.c_int, c_i64p, i64, c_f64p, c_f64p, c_u16p]
     lib.nvo_dense_gemv.restype = None
+    lib.nvo_residual_rmsnorm.argtypes = [c_u16p, c_u16p, c_u16p, i64, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                         c_u16p, c_u16p, c_f64p]
+    lib.nvo_residual_rmsnorm.restype = None
     lib.nvo_num_threads.argtypes = []
     lib.nvo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -223,3 +226,22 @@ def dense_gemv(W_bf16, x_bf16, sel=None):
                            _ptr(sel, ctypes.c_int64), nsel, _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double),
                            _ptr(yb, ctypes.c_uint16))
     return y, a, yb
+
+
+def residual_rmsnorm(r_bf16, h_bf16, w_bf16, eps, gemma_offset=False):
+    """Residual add + RMSNorm per row in fp64 over bf16 inputs.  r, h: uint16
+    [rows, k]; w: uint16 [k].  Returns (r_out uint16 [rows, k], x uint16
+    [rows, k], inv_rms fp64 [rows])."""
+    r = _c(r_bf16, np.uint16)
+    h = _c(h_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    rows, k = r.shape
+    if h.shape != r.shape or w.shape != (k,):
+        raise ValueError("r, h must be [rows, k] and w [k]")
+    ro = np.zeros((rows, k), np.uint16)
+    xo = np.zeros((rows, k), np.uint16)
+    inv = np.zeros(rows, np.float64)
+    _load().nvo_residual_rmsnorm(_ptr(r, ctypes.c_uint16), _ptr(h, ctypes.c_uint16), _ptr(w, ctypes.c_uint16), k,
+                                 rows, float(eps), int(bool(gemma_offset)), _ptr(ro, ctypes.c_uint16),
+                                 _ptr(xo, ctypes.c_uint16), _ptr(inv, ctypes.c_double))
+    return ro, xo, inv

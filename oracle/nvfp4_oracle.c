@@ -306,3 +306,30 @@ void nvo_dense_gemv(const uint16_t *W, int64_t n, int64_t k, const uint16_t *x, 
         }
     }
 }
+
+/* ---- residual add + RMSNorm, the step before a projection (the blueprint
+ * page's kernel table: norm::residual_add_rms_norm; kern's gemma_rms_norm is
+ * the variant with the Gemma offset).  Per row: v = bf16(r + h) is the new
+ * residual stream; x = bf16(v * w' / sqrt(mean(v^2) + eps)) with w' = w, or
+ * 1 + w with the offset; fp64 throughout. ---- */
+void nvo_residual_rmsnorm(const uint16_t *r, const uint16_t *h, const uint16_t *w, int64_t k, int rows,
+                          double eps, int gemma_offset, uint16_t *r_out, uint16_t *x_out, double *inv_rms)
+{
+    for (int row = 0; row < rows; ++row) {
+        const uint16_t *rr = r + (int64_t)row * k, *hh = h + (int64_t)row * k;
+        uint16_t *ro = r_out + (int64_t)row * k, *xo = x_out + (int64_t)row * k;
+        double ss = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            ro[j] = nvo_bf16_from_double(nvo_bf16_value(rr[j]) + nvo_bf16_value(hh[j]));
+            double v = nvo_bf16_value(ro[j]);
+            ss += v * v;
+        }
+        const double inv = 1.0 / sqrt(ss / (double)k + eps);
+        if (inv_rms) inv_rms[row] = inv;
+        for (int64_t j = 0; j < k; ++j) {
+            double wj = nvo_bf16_value(w[j]);
+            if (gemma_offset) wj += 1.0;
+            xo[j] = nvo_bf16_from_double(nvo_bf16_value(ro[j]) * inv * wj);
+        }
+    }
+}

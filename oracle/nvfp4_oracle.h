@@ -70,6 +70,12 @@ void nvo_dense_gemv(const uint16_t *W, int64_t n, int64_t k, const uint16_t *x, 
                     const int64_t *sel, int64_t nsel,
                     double *y, double *absdot, uint16_t *y_bf16);
 
+/* Residual add + RMSNorm per row: r_out = bf16(r + h), x = bf16(r_out * w' /
+ * sqrt(mean(r_out^2) + eps)), w' = w or 1 + w (gemma_offset); inv_rms
+ * (optional) receives 1 / sqrt(mean + eps) per row. */
+void nvo_residual_rmsnorm(const uint16_t *r, const uint16_t *h, const uint16_t *w, int64_t k, int rows,
+                          double eps, int gemma_offset, uint16_t *r_out, uint16_t *x_out, double *inv_rms);
+
 #ifdef __cplusplus
 }
 #endif
