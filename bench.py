@@ -68,7 +68,7 @@ def parse_args():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true", help="skip the dense bf16 lm-head timing")
+    ap.add_argument("--no-dense", action="store_true", help="skip the lm-head and RMSNorm timings")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LAUNCHES_PER_STEP"),
                     help="write the rows=1 decode-step kernel's HBM traffic per launch from two rocprofv3 "
                          "--pmc counter collections (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run of "
@@ -293,6 +293,37 @@ def time_dense(nv, torch, dev, rows_list, reps):
     return out
 
 
+def time_norm(nv, torch, dev, reps):
+    """nvfp4_residual_rmsnorm at the 27B model's hidden size (k = 5120): the
+    average call at decode row counts (1 and 8: a few tens of KB, bound by
+    latency) and GB/s at 4096 rows (reads residual and delta, writes
+    residual_out and x: 8 bytes per element)."""
+    g = torch.Generator(device=dev).manual_seed(99)
+    k = 5120
+    w = torch.randn((k,), generator=g, device=dev).to(torch.bfloat16)
+    out = {"k": k, "by_rows": {}}
+    stream = torch.cuda.current_stream()
+    for rows in (1, 8, 4096):
+        r = torch.randn((rows, k), generator=g, device=dev).to(torch.bfloat16)
+        h = torch.randn((rows, k), generator=g, device=dev).to(torch.bfloat16)
+        ro, x = torch.empty_like(r), torch.empty_like(r)
+        for _ in range(3):
+            nv.nvfp4_residual_rmsnorm(r, h, w, residual_out=ro, x=x)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            nv.nvfp4_residual_rmsnorm(r, h, w, residual_out=ro, x=x)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        us = start.elapsed_time(stop) * 1e3 / reps
+        gbs = rows * k * 8 / (us * 1e-6) / 1e9
+        out["by_rows"][str(rows)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1),
+                                     "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        log("residual add + RMSNorm k=%d rows=%d: %.2f us, %.1f GB/s" % (k, rows, us, gbs))
+    return out
+
+
 def main():
     args = parse_args()
     if args.summarize_pmc:
@@ -374,6 +405,8 @@ def main():
         dense = time_dense(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
                            max(5, args.steps // 5))
 
+    norm = None if args.no_dense else time_norm(nv, torch, dev, max(10, args.steps // 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on layer 0 ...")
@@ -407,6 +440,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_lm_head": dense,
+        "residual_rmsnorm": norm,
     }
     print(json.dumps(line), flush=True)
 

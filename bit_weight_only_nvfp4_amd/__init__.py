@@ -39,7 +39,7 @@ EXPORTS = (
     "nvfp4_abi_version", "nvfp4_strerror", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
     "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
-    "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16",
+    "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16", "nvfp4_residual_rmsnorm",
 )
 
 
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
             "nvfp4_gemv_sequence": ([ctypes.POINTER(nvfp4_call), ctypes.c_int, vp, sz,
                                      ctypes.POINTER(ctypes.c_void_p), vp], ctypes.c_int),
             "nvfp4_dense_gemv_bf16": ([vp, i64, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
+            "nvfp4_residual_rmsnorm": ([vp, vp, vp, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, vp, vp],
+                                       ctypes.c_int),
         }
         for name, (argt, rest) in sig.items():
             f = getattr(L, name)
@@ -306,6 +308,28 @@ def nvfp4_dense_gemv_bf16(W: torch.Tensor, x: torch.Tensor, out_dtype=torch.bflo
            lib().nvfp4_dense_gemv_bf16(_ptr(W), n, k, _ptr(x), rows, _ptr(out), _OUT[out.dtype],
                                        _stream(x.device)))
     return out
+
+
+def nvfp4_residual_rmsnorm(residual: torch.Tensor, delta: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
+                           gemma_offset: bool = False, residual_out: torch.Tensor | None = None,
+                           x: torch.Tensor | None = None):
+    """residual_out = bf16(residual + delta); x = RMSNorm(residual_out) * w'
+    (w' = weight, or 1 + weight with the Gemma offset).  Returns
+    (residual_out, x); pass residual_out=residual to update it in place."""
+    for name, t in (("residual", residual), ("delta", delta), ("weight", weight)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("%s must be bfloat16" % name)
+    residual, delta, weight = residual.contiguous(), delta.contiguous(), weight.contiguous()
+    rows, k = residual.shape
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if x is None:
+        x = torch.empty_like(residual)
+    _check("nvfp4_residual_rmsnorm",
+           lib().nvfp4_residual_rmsnorm(_ptr(residual), _ptr(delta), _ptr(weight), k, rows, float(eps),
+                                        int(bool(gemma_offset)), _ptr(residual_out), _ptr(x),
+                                        _stream(residual.device)))
+    return residual_out, x
 
 
 class Sequence:

@@ -396,6 +396,36 @@ int nvfp4_dense_gemv_bf16(const void *W, int64_t n, int64_t k, const void *x, in
     return ok();
 }
 
+int nvfp4_residual_rmsnorm(const void *residual, const void *delta, const void *weight, int64_t k, int rows,
+                           float eps, int gemma_offset, void *residual_out, void *x, void *stream) {
+    static const char *fn = "nvfp4_residual_rmsnorm";
+    if (!residual) return fail(NVFP4_E_NULL, "%s: residual is NULL", fn);
+    if (!delta) return fail(NVFP4_E_NULL, "%s: delta is NULL", fn);
+    if (!weight) return fail(NVFP4_E_NULL, "%s: weight is NULL", fn);
+    if (!residual_out) return fail(NVFP4_E_NULL, "%s: residual_out is NULL", fn);
+    if (!x) return fail(NVFP4_E_NULL, "%s: x is NULL", fn);
+    if (k < 16 || k % 16 != 0 || k > norm_max_k())
+        return fail(NVFP4_E_SHAPE, "%s: k=%lld (need a positive multiple of 16, at most %lld)", fn, (long long)k,
+                    (long long)norm_max_k());
+    if (rows < 1 || rows > (1 << 20)) return fail(NVFP4_E_ROWS, "%s: rows=%d outside 1..2^20", fn, rows);
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(NVFP4_E_SHAPE, "%s: eps must be finite and >= 0", fn);
+    for (const void *p : {residual, delta, weight, (const void *)residual_out, (const void *)x})
+        if (!aligned(p, 16)) return fail(NVFP4_E_ALIGN, "%s: every buffer must be 16-byte aligned", fn);
+    const size_t rb = (size_t)rows * k * 2, wb = (size_t)k * 2;
+    // the residual may be updated in place (residual_out == residual), nothing else may overlap
+    if (residual_out != residual && overlap(residual_out, rb, residual, rb))
+        return fail(NVFP4_E_OVERLAP, "%s: residual_out overlaps residual without being it", fn);
+    if (overlap(residual_out, rb, delta, rb) || overlap(residual_out, rb, weight, wb))
+        return fail(NVFP4_E_OVERLAP, "%s: residual_out overlaps delta or weight", fn);
+    if (overlap(x, rb, residual, rb) || overlap(x, rb, delta, rb) || overlap(x, rb, weight, wb) ||
+        overlap(x, rb, residual_out, rb))
+        return fail(NVFP4_E_OVERLAP, "%s: x overlaps another buffer", fn);
+    int st = check_device(fn);
+    if (st) return st;
+    return hip_status(fn, launch_residual_rmsnorm(residual, delta, weight, k, rows, eps, gemma_offset != 0,
+                                                  residual_out, x, static_cast<hipStream_t>(stream)));
+}
+
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
                         void *const *events, void *stream) {
     static const char *fn = "nvfp4_gemv_sequence";

@@ -199,6 +199,11 @@ int sequence_launches(const StreamCall *calls, int ncalls);
 hipError_t launch_dense(const void *w, int64_t n, int64_t k, const void *x, int rows, void *y, int out_f32,
                         hipStream_t stream);
 
+// Residual add + RMSNorm, one workgroup per row (k <= norm_max_k()).
+int64_t norm_max_k();
+hipError_t launch_residual_rmsnorm(const void *r, const void *h, const void *w, int64_t k, int rows, float eps,
+                                   int gemma_offset, void *r_out, void *x, hipStream_t stream);
+
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
                        int64_t n, int64_t k, void *packed, hipStream_t stream);
 hipError_t launch_unpack(const void *packed, int64_t n, int64_t k, uint8_t *codes,

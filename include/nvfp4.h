@@ -216,6 +216,20 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
 int nvfp4_dense_gemv_bf16(const void *W, int64_t n, int64_t k, const void *x, int rows, void *y,
                           int out_dtype, void *stream);
 
+/* Residual add + RMSNorm, the step that produces a projection's activations
+ * (the blueprint page's kernel table: norm::residual_add_rms_norm; kern's
+ * gemma_rms_norm is the variant with the Gemma offset).  Per row r < rows:
+ *   residual_out[r] = bf16(residual[r] + delta[r])            (RNE)
+ *   x[r][j] = bf16(residual_out[r][j] * w'[j] / sqrt(mean_j(residual_out[r]^2) + eps))
+ * with w' = weight, or 1 + weight when gemma_offset != 0; fp32 arithmetic.
+ * residual, delta, residual_out, x: device bf16 [rows][k]; weight: device bf16
+ * [k]; every buffer 16-byte aligned; k a positive multiple of 16, at most
+ * 65536; rows 1..2^20; eps finite and >= 0.  residual_out may be residual
+ * itself (in-place update); no other overlap (NVFP4_E_OVERLAP).  Bitwise
+ * deterministic; enqueued on `stream`. */
+int nvfp4_residual_rmsnorm(const void *residual, const void *delta, const void *weight, int64_t k, int rows,
+                           float eps, int gemma_offset, void *residual_out, void *x, void *stream);
+
 /* Number of kernel launches nvfp4_gemv_sequence makes for these calls without
  * events on the current device (one per call where shared launches are not
  * available); 0 if ncalls <= 0 or calls is NULL. */

@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(nv):
     names = _declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     L = ctypes.CDLL(nv.LIB_PATH)
     for name in names:
         assert hasattr(L, name), name
@@ -234,6 +234,30 @@ def test_dense_gemv_argument_errors(nv):
     assert "y overlaps x" in nv.nvfp4_last_error()
     assert _dense(nv, y=FAKE + 4096) == E["NVFP4_E_OVERLAP"]     # y inside W
     assert "y overlaps W" in nv.nvfp4_last_error()
+
+
+def _norm(nv, r=XF, h=WF, w=FAKE, k=512, rows=2, eps=1e-6, gemma=0, ro=YF, x=YF + 0x100000):
+    return nv.lib().nvfp4_residual_rmsnorm(r, h, w, k, rows, eps, gemma, ro, x, None)
+
+
+def test_residual_rmsnorm_argument_errors(nv):
+    E = {v: k for k, v in nv.STATUS.items()}
+    assert _norm(nv, r=None) == E["NVFP4_E_NULL"]
+    assert _norm(nv, h=None) == E["NVFP4_E_NULL"]
+    assert _norm(nv, w=None) == E["NVFP4_E_NULL"]
+    assert _norm(nv, ro=None) == E["NVFP4_E_NULL"]
+    assert _norm(nv, x=None) == E["NVFP4_E_NULL"]
+    assert _norm(nv, k=24) == E["NVFP4_E_SHAPE"]
+    assert _norm(nv, k=0) == E["NVFP4_E_SHAPE"]
+    assert _norm(nv, k=65536 + 16) == E["NVFP4_E_SHAPE"]
+    assert _norm(nv, rows=0) == E["NVFP4_E_ROWS"]
+    assert _norm(nv, eps=-1.0) == E["NVFP4_E_SHAPE"]
+    assert _norm(nv, eps=float("nan")) == E["NVFP4_E_SHAPE"]
+    assert _norm(nv, h=WF + 8) == E["NVFP4_E_ALIGN"]
+    assert _norm(nv, ro=XF + 512) == E["NVFP4_E_OVERLAP"]       # partly over the residual
+    assert _norm(nv, x=WF) == E["NVFP4_E_OVERLAP"]              # over delta
+    assert _norm(nv, x=YF) == E["NVFP4_E_OVERLAP"]              # over residual_out
+    assert "x overlaps" in nv.nvfp4_last_error()
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="valid arguments would launch on a real device")
