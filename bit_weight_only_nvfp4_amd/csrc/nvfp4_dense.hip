@@ -8,9 +8,12 @@
 //
 // The weight stream is the whole cost (2 bytes per weight against 4.5 bits for
 // NVFP4), so the kernel is shaped for it:
-//   * one workgroup per 32 features (two 16-feature matrix-core products), 8
-//     waves each taking one eighth of k; many more workgroups than CUs, so the
-//     hardware's dispatcher balances them;
+//   * one workgroup per 32 features (two 16-feature matrix-core products), 4
+//     waves each taking a quarter of k; many more workgroups than CUs (several
+//     resident per CU), so the hardware's dispatcher balances them.  Measured
+//     on a [151936 x 5120] head against 8 waves per workgroup: 4.8% faster at
+//     1 row; 2 waves, 64 features per workgroup, or 5-6 steps in flight were
+//     slower, 3 steps equal;
 //   * a wave's k-range in steps of 64: per step a lane loads 32 contiguous
 //     bytes of each of its two weight rows (16 rows x 128 bytes per product:
 //     whole lines) and 32 bytes of its activation row, four steps in flight;
@@ -33,8 +36,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kDenseFeatures = 32;   // features per workgroup
-constexpr int kDenseWaves = 8;
+constexpr int kDenseFB = 2;          // 16-feature blocks per workgroup
+constexpr int kDenseFeatures = 16 * kDenseFB;
+constexpr int kDenseWaves = 4;
 constexpr int kDenseStepK = 64;
 constexpr int kDenseBufs = 4;        // steps in flight per wave
 constexpr int kDropped = 0x7fffffff; // past any buffer: loads read 0, stores are dropped
@@ -56,7 +60,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 // One step's operands of this lane: two weight rows (feature blocks) and the
 // activation row, 32 bytes each (k = k0 + 16 q .. + 15).
 struct DenseStep {
-    u32x4_t b[2][2];
+    u32x4_t b[kDenseFB][2];
     u32x4_t a[2];
 };
 
@@ -71,9 +75,9 @@ __device__ __forceinline__ void load_step(__amdgpu_buffer_rsrc_t wr, __amdgpu_bu
     const int kk = k0 + 16 * q;
     const bool in = kk < kend;   // k is a multiple of 16: a lane's 16 values are all in or all out
     const int wo = in ? (n16 * k + kk) * 2 : kOutside;
-    const int fbo = 16 * k * 2;   // the second feature block's rows
+    const int fbo = 16 * k * 2;   // the next feature block's rows
 #pragma unroll
-    for (int fb = 0; fb < 2; ++fb) {
+    for (int fb = 0; fb < kDenseFB; ++fb) {
         s.b[fb][0] = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + fb * fbo, 0, 0);
         s.b[fb][1] = __builtin_amdgcn_raw_buffer_load_b128(wr, wo + fb * fbo + 16, 0, 0);
     }
@@ -83,12 +87,12 @@ __device__ __forceinline__ void load_step(__amdgpu_buffer_rsrc_t wr, __amdgpu_bu
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void mac_step(const DenseStep &s, f32x4_t (&d)[2]) {
+__device__ __forceinline__ void mac_step(const DenseStep &s, f32x4_t (&d)[kDenseFB]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s.a[m]);
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
+        for (int fb = 0; fb < kDenseFB; ++fb)
             d[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, s.b[fb][m]), d[fb], 0,
                                                             0, 0);
     }
@@ -102,7 +106,7 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 }
 
 __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(DenseArgs a) {
-    __shared__ float red[kDenseWaves][2][16][16];   // [wave][feature block][row][feature]
+    __shared__ float red[kDenseWaves][kDenseFB][16][16];   // [wave][feature block][row][feature]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, n16 = lane & 15;
@@ -114,7 +118,9 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(DenseArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((size_t)a.rows * a.k * 2));
     const int kb = wave * a.kw, ke = min(a.k, kb + a.kw);
     const int steps = ke > kb ? (ke - kb + kDenseStepK - 1) / kDenseStepK : 0;
-    f32x4_t d[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    f32x4_t d[kDenseFB];
+#pragma unroll
+    for (int fb = 0; fb < kDenseFB; ++fb) d[fb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     DenseStep s[kDenseBufs];
 #pragma unroll
     for (int i = 0; i < kDenseBufs; ++i) load_step(wr, xr, kb + i * kDenseStepK, ke, a.k, q, n16, n16, s[i]);
@@ -129,24 +135,25 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(DenseArgs a) {
     }
     // lane (q, n16) holds rows 4 q .. 4 q + 3 of features 16 fb + n16
 #pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
+    for (int fb = 0; fb < kDenseFB; ++fb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][fb][4 * q + v][n16] = d[fb][v];
     __syncthreads();
-    // 512 outputs (16 rows x 32 features), one per thread, summed in wave order
-    const int r = tid >> 5, f = tid & 31;
-    float t = red[0][f >> 4][r][f & 15];
+    // 16 rows x kDenseFeatures outputs, summed in wave order
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, (uint32_t)((size_t)a.rows * a.n * (a.out_f32 ? 4 : 2)));
 #pragma unroll
-    for (int w = 1; w < kDenseWaves; ++w) t += red[w][f >> 4][r][f & 15];
-    const int at = r * a.n + f0 + f;
-    const bool keep = r < a.rows && f < nf;
-    if (a.out_f32) {
-        const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, (uint32_t)((size_t)a.rows * a.n * 4));
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, t), yr, keep ? at * 4 : kDropped, 0,
-                                              kDeviceCoherent);
-    } else {
-        const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, (uint32_t)((size_t)a.rows * a.n * 2));
-        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(t), yr, keep ? at * 2 : kDropped, 0, kDeviceCoherent);
+    for (int o = tid; o < 16 * kDenseFeatures; o += kDenseWaves * 64) {
+        const int r = o / kDenseFeatures, f = o % kDenseFeatures;
+        float t = red[0][f >> 4][r][f & 15];
+#pragma unroll
+        for (int w = 1; w < kDenseWaves; ++w) t += red[w][f >> 4][r][f & 15];
+        const int at = r * a.n + f0 + f;
+        const bool keep = r < a.rows && f < nf;
+        if (a.out_f32)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, t), yr, keep ? at * 4 : kDropped, 0,
+                                                  kDeviceCoherent);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16(bf16_rne(t), yr, keep ? at * 2 : kDropped, 0, kDeviceCoherent);
     }
 }
 
