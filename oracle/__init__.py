@@ -74,6 +74,14 @@ def _load():
     lib.nvo_residual_rmsnorm.argtypes = [c_u16p, c_u16p, c_u16p, i64, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                          c_u16p, c_u16p, c_f64p]
     lib.nvo_residual_rmsnorm.restype = None
+    lib.nvo_e8m0_value.argtypes = [ctypes.c_uint]
+    lib.nvo_e8m0_value.restype = ctypes.c_double
+    lib.nvo_mx_quantize.argtypes = [c_f32p, i64, i64, c_u8p, c_u8p]
+    lib.nvo_mx_quantize.restype = ctypes.c_int
+    lib.nvo_mx_dequant.argtypes = [c_u8p, c_u8p, i64, i64, c_f64p]
+    lib.nvo_mx_dequant.restype = None
+    lib.nvo_mx_gemv.argtypes = [c_u8p, c_u8p, i64, i64, c_u16p, ctypes.c_int, c_i64p, i64, c_f64p, c_f64p, c_u16p]
+    lib.nvo_mx_gemv.restype = None
     lib.nvo_num_threads.argtypes = []
     lib.nvo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -245,3 +253,51 @@ def residual_rmsnorm(r_bf16, h_bf16, w_bf16, eps, gemma_offset=False):
                                  rows, float(eps), int(bool(gemma_offset)), _ptr(ro, ctypes.c_uint16),
                                  _ptr(xo, ctypes.c_uint16), _ptr(inv, ctypes.c_double))
     return ro, xo, inv
+
+
+# ---- MXFP4 (E2M1 codes + one E8M0 scale per 32 k) ---------------------------
+
+def e8m0_value(byte: int) -> float:
+    return float(_load().nvo_e8m0_value(int(byte)))
+
+
+def mx_quantize(W):
+    """W float32 [n, k] (k % 32 == 0) -> (codes uint8 [n, k/2], scales uint8 [n, k/32])."""
+    W = _c(W, np.float32)
+    n, k = W.shape
+    codes = np.zeros((n, k // 2), np.uint8)
+    scales = np.zeros((n, k // 32), np.uint8)
+    st = _load().nvo_mx_quantize(_ptr(W, ctypes.c_float), n, k, _ptr(codes, ctypes.c_uint8),
+                                 _ptr(scales, ctypes.c_uint8))
+    if st != 0:
+        raise ValueError("mx_quantize: k must be a multiple of 32 and W finite (status %d)" % st)
+    return codes, scales
+
+
+def mx_dequant(codes, scales):
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    out = np.zeros((n, k), np.float64)
+    _load().nvo_mx_dequant(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), n, k,
+                           _ptr(out, ctypes.c_double))
+    return out
+
+
+def mx_gemv(codes, scales, x_bf16, sel=None):
+    """MXFP4 projection in fp64: (y [rows, nsel], sum|D*x| [rows, nsel], y_bf16)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    x = _c(x_bf16, np.uint16)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    rows = x.shape[0]
+    if x.shape[1] != k or scales.shape != (n, k // 32):
+        raise ValueError("x must be [rows, k] and scales [n, k/32]")
+    sel, nsel = _sel(sel, n)
+    y = np.zeros((rows, nsel), np.float64)
+    a = np.zeros((rows, nsel), np.float64)
+    yb = np.zeros((rows, nsel), np.uint16)
+    _load().nvo_mx_gemv(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), n, k, _ptr(x, ctypes.c_uint16),
+                        rows, _ptr(sel, ctypes.c_int64), nsel, _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double),
+                        _ptr(yb, ctypes.c_uint16))
+    return y, a, yb

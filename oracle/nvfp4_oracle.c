@@ -333,3 +333,85 @@ void nvo_residual_rmsnorm(const uint16_t *r, const uint16_t *h, const uint16_t *
         }
     }
 }
+
+/* ---- MXFP4 (the OCP microscaling format: E2M1 elements, one E8M0
+ * power-of-two scale per 32 consecutive k of a row, no tensor scale).  The
+ * pages only name it (gpu_mxfp4 kernels in the kern build listing); the
+ * readings: the block's shared exponent is floor(log2(amax)) - 2 (2 is
+ * E2M1's largest exponent), clamped to E8M0's -127..127; elements are
+ * V / 2^X rounded as E2M1 everywhere else here (nearest, ties to the even
+ * mantissa, saturating at +-6, sign of zero kept); an all-zero block gets
+ * scale byte 127 (2^0) and zero codes; E8M0 byte 255 (NaN) is never
+ * produced. ---- */
+double nvo_e8m0_value(unsigned b)
+{
+    return b == 255u ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+int nvo_mx_quantize(const float *W, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales)
+{
+    if (k % 32 != 0) return -1;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!isfinite(W[i])) return -2;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const float *v = W + r * k + b * 32;
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+            uint8_t *c = codes + r * (k / 2) + b * 16;
+            if (amax == 0.0f) {
+                scales[r * (k / 32) + b] = 127;
+                for (int j = 0; j < 16; ++j) c[j] = 0;
+                continue;
+            }
+            int ex;
+            frexp((double)amax, &ex);          /* amax = m 2^ex, 0.5 <= m < 1: floor(log2) = ex - 1 */
+            int X = ex - 1 - 2;
+            if (X < -127) X = -127;
+            if (X > 127) X = 127;
+            scales[r * (k / 32) + b] = (uint8_t)(X + 127);
+            for (int j = 0; j < 32; j += 2) {
+                unsigned lo = nvo_e2m1_encode((float)ldexp((double)v[j], -X));
+                unsigned hi = nvo_e2m1_encode((float)ldexp((double)v[j + 1], -X));
+                c[j / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    return 0;
+}
+
+void nvo_mx_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t k, double *out)
+{
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t c = 0; c < k; ++c) {
+            unsigned byte = codes[r * (k / 2) + c / 2];
+            unsigned code = (c & 1) ? byte >> 4 : byte & 15u;
+            out[r * k + c] = nvo_e2m1_value(code) * nvo_e8m0_value(scales[r * (k / 32) + c / 32]);
+        }
+}
+
+void nvo_mx_gemv(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t k, const uint16_t *x, int rows,
+                 const int64_t *sel, int64_t nsel, double *y, double *absdot, uint16_t *y_bf16)
+{
+    if (!sel) nsel = n;
+#pragma omp parallel
+    {
+        double *drow = (double *)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int64_t j = 0; j < nsel; ++j) {
+            const int64_t feat = sel ? sel[j] : j;
+            nvo_mx_dequant(codes + feat * (k / 2), scales + feat * (k / 32), 1, k, drow);
+            for (int r = 0; r < rows; ++r) {
+                double acc = 0.0, aacc = 0.0;
+                for (int64_t c = 0; c < k; ++c) {
+                    double p = drow[c] * nvo_bf16_value(x[(int64_t)r * k + c]);
+                    acc += p;
+                    aacc += fabs(p);
+                }
+                if (y) y[r * nsel + j] = acc;
+                if (absdot) absdot[r * nsel + j] = aacc;
+                if (y_bf16) y_bf16[r * nsel + j] = nvo_bf16_from_double(acc);
+            }
+        }
+        free(drow);
+    }
+}

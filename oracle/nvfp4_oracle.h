@@ -76,6 +76,13 @@ void nvo_dense_gemv(const uint16_t *W, int64_t n, int64_t k, const uint16_t *x, 
 void nvo_residual_rmsnorm(const uint16_t *r, const uint16_t *h, const uint16_t *w, int64_t k, int rows,
                           double eps, int gemma_offset, uint16_t *r_out, uint16_t *x_out, double *inv_rms);
 
+/* MXFP4: E2M1 codes [n][k/2] (low nibble first) + E8M0 scales [n][k/32]. */
+double nvo_e8m0_value(unsigned b);
+int nvo_mx_quantize(const float *W, int64_t n, int64_t k, uint8_t *codes, uint8_t *scales);
+void nvo_mx_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t k, double *out);
+void nvo_mx_gemv(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t k, const uint16_t *x, int rows,
+                 const int64_t *sel, int64_t nsel, double *y, double *absdot, uint16_t *y_bf16);
+
 #ifdef __cplusplus
 }
 #endif
