@@ -216,6 +216,19 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
 int nvfp4_dense_gemv_bf16(const void *W, int64_t n, int64_t k, const void *x, int rows, void *y,
                           int out_dtype, void *stream);
 
+/* MXFP4 projection, the microscaling format variant (E2M1 codes with one E8M0
+ * power-of-two scale per 32 consecutive k of a row, no tensor scale; the
+ * pages name it through the kern build's gpu_mxfp4 kernels), in the format's
+ * own row-major layout, no repacking:
+ *   y[r][j] = sum_k e2m1(code[j][k]) * 2^(scale[j][k/32] - 127) * x[r][k].
+ * codes: device [n][k/2] bytes (element 2i in the low nibble of byte i),
+ * 16-byte aligned; scales: device [n][k/32] E8M0 bytes (255, NaN, gives NaN
+ * results); 1 <= n <= 2^20, k a positive multiple of 32, k <= 2^24; x, rows,
+ * y, out_dtype as for nvfp4_gemv (more than 16 rows run as row chunks, each
+ * reading the weight once).  No workspace; bitwise deterministic. */
+int nvfp4_mxfp4_gemv(const void *codes, const void *scales, int64_t n, int64_t k, const void *x, int rows,
+                     void *y, int out_dtype, void *stream);
+
 /* Residual add + RMSNorm, the step that produces a projection's activations
  * (the blueprint page's kernel table: norm::residual_add_rms_norm; kern's
  * gemma_rms_norm is the variant with the Gemma offset).  Per row r < rows:
