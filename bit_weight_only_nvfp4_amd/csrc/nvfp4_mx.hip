@@ -14,7 +14,7 @@
 // code * 2^e for e in -126..125).  The activations then feed the bf16 matrix
 // cores as stored: no activation staging, no scale multiply.
 //   * one workgroup per 64 features (four 16-feature products), 4 waves each
-//     over a quarter of k in steps of 128; four steps in flight;
+//     over a quarter of k in steps of 128; two steps in flight;
 //   * per step a lane (q, n) takes k = 32 q .. 32 q + 31 of the step -- one MX
 //     block, so one scale byte per feature block -- as 16 bytes of codes per
 //     feature block and 64 bytes of its activation row; product m of the step
@@ -37,7 +37,12 @@ constexpr int kMxFB = 4;            // 16-feature blocks per workgroup
 constexpr int kMxFeatures = 16 * kMxFB;
 constexpr int kMxWaves = 4;
 constexpr int kMxStepK = 128;
-constexpr int kMxBufs = 4;          // steps in flight per wave
+// Steps in flight per wave.  Measured on a [151936 x 5120] matrix: 2 (116
+// registers, four waves per SIMD) 130 us at 1 row against 138 with 4 (176
+// registers); 128 features per workgroup with 3 steps 134 us.  The kernel is
+// far from its bytes (about 3 TB/s): each step also makes as many scale-byte
+// requests (16 rows per feature block) as code requests.
+constexpr int kMxBufs = 2;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kDeviceCoherent = 16;
 constexpr int kDropped = 0x7fffffff;
