@@ -82,6 +82,15 @@ def _load():
     lib.nvo_mx_dequant.restype = None
     lib.nvo_mx_gemv.argtypes = [c_u8p, c_u8p, i64, i64, c_u16p, ctypes.c_int, c_i64p, i64, c_f64p, c_f64p, c_u16p]
     lib.nvo_mx_gemv.restype = None
+    c_i8p = ctypes.POINTER(ctypes.c_int8)
+    lib.nvo_f16_value.argtypes = [ctypes.c_uint16]
+    lib.nvo_f16_value.restype = ctypes.c_double
+    lib.nvo_w8_quantize.argtypes = [c_f32p, i64, i64, c_i8p, c_u16p]
+    lib.nvo_w8_quantize.restype = ctypes.c_int
+    lib.nvo_w8_dequant.argtypes = [c_i8p, c_u16p, i64, i64, c_f64p]
+    lib.nvo_w8_dequant.restype = None
+    lib.nvo_w8_gemv.argtypes = [c_i8p, c_u16p, i64, i64, c_u16p, ctypes.c_int, c_i64p, i64, c_f64p, c_f64p, c_u16p]
+    lib.nvo_w8_gemv.restype = None
     lib.nvo_num_threads.argtypes = []
     lib.nvo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -298,6 +307,54 @@ def mx_gemv(codes, scales, x_bf16, sel=None):
     a = np.zeros((rows, nsel), np.float64)
     yb = np.zeros((rows, nsel), np.uint16)
     _load().nvo_mx_gemv(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), n, k, _ptr(x, ctypes.c_uint16),
+                        rows, _ptr(sel, ctypes.c_int64), nsel, _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double),
+                        _ptr(yb, ctypes.c_uint16))
+    return y, a, yb
+
+
+# ---- W8G32_F16S (int8 codes + one fp16 scale per 32 k) ---------------------
+
+def f16_value(bits: int) -> float:
+    return float(_load().nvo_f16_value(int(bits)))
+
+
+def w8_quantize(W):
+    """W float32 [n, k] (k % 32 == 0) -> (codes int8 [n, k], scales uint16 fp16 bits [n, k/32])."""
+    W = _c(W, np.float32)
+    n, k = W.shape
+    codes = np.zeros((n, k), np.int8)
+    scales = np.zeros((n, k // 32), np.uint16)
+    st = _load().nvo_w8_quantize(_ptr(W, ctypes.c_float), n, k, _ptr(codes, ctypes.c_int8),
+                                 _ptr(scales, ctypes.c_uint16))
+    if st != 0:
+        raise ValueError("w8_quantize: k must be a multiple of 32 and W finite (status %d)" % st)
+    return codes, scales
+
+
+def w8_dequant(codes, scales):
+    codes = _c(codes, np.int8)
+    scales = _c(scales, np.uint16)
+    n, k = codes.shape
+    out = np.zeros((n, k), np.float64)
+    _load().nvo_w8_dequant(_ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_uint16), n, k,
+                           _ptr(out, ctypes.c_double))
+    return out
+
+
+def w8_gemv(codes, scales, x_bf16, sel=None):
+    """W8G32_F16S projection in fp64: (y [rows, nsel], sum|D*x| [rows, nsel], y_bf16)."""
+    codes = _c(codes, np.int8)
+    scales = _c(scales, np.uint16)
+    x = _c(x_bf16, np.uint16)
+    n, k = codes.shape
+    rows = x.shape[0]
+    if x.shape[1] != k or scales.shape != (n, k // 32):
+        raise ValueError("x must be [rows, k] and scales [n, k/32]")
+    sel, nsel = _sel(sel, n)
+    y = np.zeros((rows, nsel), np.float64)
+    a = np.zeros((rows, nsel), np.float64)
+    yb = np.zeros((rows, nsel), np.uint16)
+    _load().nvo_w8_gemv(_ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_uint16), n, k, _ptr(x, ctypes.c_uint16),
                         rows, _ptr(sel, ctypes.c_int64), nsel, _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double),
                         _ptr(yb, ctypes.c_uint16))
     return y, a, yb

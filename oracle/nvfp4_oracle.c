@@ -415,3 +415,96 @@ void nvo_mx_gemv(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t
         free(drow);
     }
 }
+
+/* ---- W8G32_F16S (the pages name this encoding for the DFlash2 drafter's
+ * matrices and give nothing else): signed 8-bit weights with one fp16 scale
+ * per 32 consecutive k of a row, symmetric (no zero point).  Readings: the
+ * quantizer takes scale = fp16(amax / 127) (nearest even) and code =
+ * rint(w / scale) (ties to even) clamped to +-127; a group whose scale is 0
+ * gets codes 0; the weight is code * scale (exact in fp32). ---- */
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits. */
+double nvo_f16_value(uint16_t h)
+{
+    const double sign = (h & 0x8000u) ? -1.0 : 1.0;
+    const int e = (h >> 10) & 31, m = h & 1023;
+    if (e == 31) return m ? NAN : sign * INFINITY;
+    if (e == 0) return sign * ldexp((double)m, -24);
+    return sign * ldexp((double)(1024 + m), e - 25);
+}
+
+/* float -> binary16, nearest with ties to even (rint in the default mode) */
+static uint16_t f16_from_float(float f)
+{
+    const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+    const double a = fabs((double)f);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);      /* the halfway point above 65504 rounds to even: inf */
+    if (a < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)rint(ldexp(a, 24)));   /* subnormal (1024 = 2^-14) */
+    int e;
+    frexp(a, &e);                                             /* a = m 2^e, 0.5 <= m < 1 */
+    double q = rint(ldexp(a, 11 - e));                        /* 1024 .. 2048 */
+    if (q == 2048.0) {
+        q = 1024.0;
+        ++e;
+    }
+    const int E = e - 1 + 15;
+    if (E >= 31) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024));
+}
+
+int nvo_w8_quantize(const float *W, int64_t n, int64_t k, int8_t *codes, uint16_t *scales)
+{
+    if (k % 32 != 0) return -1;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!isfinite(W[i])) return -2;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const float *v = W + r * k + b * 32;
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+            const uint16_t sh = f16_from_float(amax / 127.0f);
+            scales[r * (k / 32) + b] = sh;
+            const double S = nvo_f16_value(sh);
+            for (int j = 0; j < 32; ++j) {
+                double q = (S == 0.0 || !isfinite(S)) ? 0.0 : rint((double)v[j] / S);
+                if (q > 127.0) q = 127.0;
+                if (q < -127.0) q = -127.0;
+                codes[r * k + b * 32 + j] = (int8_t)q;
+            }
+        }
+    return 0;
+}
+
+void nvo_w8_dequant(const int8_t *codes, const uint16_t *scales, int64_t n, int64_t k, double *out)
+{
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t c = 0; c < k; ++c)
+            out[r * k + c] = (double)codes[r * k + c] * nvo_f16_value(scales[r * (k / 32) + c / 32]);
+}
+
+void nvo_w8_gemv(const int8_t *codes, const uint16_t *scales, int64_t n, int64_t k, const uint16_t *x, int rows,
+                 const int64_t *sel, int64_t nsel, double *y, double *absdot, uint16_t *y_bf16)
+{
+    if (!sel) nsel = n;
+#pragma omp parallel
+    {
+        double *drow = (double *)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int64_t j = 0; j < nsel; ++j) {
+            const int64_t feat = sel ? sel[j] : j;
+            nvo_w8_dequant(codes + feat * k, scales + feat * (k / 32), 1, k, drow);
+            for (int r = 0; r < rows; ++r) {
+                double acc = 0.0, aacc = 0.0;
+                for (int64_t c = 0; c < k; ++c) {
+                    double p = drow[c] * nvo_bf16_value(x[(int64_t)r * k + c]);
+                    acc += p;
+                    aacc += fabs(p);
+                }
+                if (y) y[r * nsel + j] = acc;
+                if (absdot) absdot[r * nsel + j] = aacc;
+                if (y_bf16) y_bf16[r * nsel + j] = nvo_bf16_from_double(acc);
+            }
+        }
+        free(drow);
+    }
+}

@@ -83,6 +83,13 @@ void nvo_mx_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, int6
 void nvo_mx_gemv(const uint8_t *codes, const uint8_t *scales, int64_t n, int64_t k, const uint16_t *x, int rows,
                  const int64_t *sel, int64_t nsel, double *y, double *absdot, uint16_t *y_bf16);
 
+/* W8G32_F16S: int8 codes [n][k] + fp16 scale bits [n][k/32], symmetric. */
+double nvo_f16_value(uint16_t h);
+int nvo_w8_quantize(const float *W, int64_t n, int64_t k, int8_t *codes, uint16_t *scales);
+void nvo_w8_dequant(const int8_t *codes, const uint16_t *scales, int64_t n, int64_t k, double *out);
+void nvo_w8_gemv(const int8_t *codes, const uint16_t *scales, int64_t n, int64_t k, const uint16_t *x, int rows,
+                 const int64_t *sel, int64_t nsel, double *y, double *absdot, uint16_t *y_bf16);
+
 #ifdef __cplusplus
 }
 #endif
