@@ -68,7 +68,7 @@ def parse_args():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true", help="skip the lm-head, RMSNorm and MXFP4 timings")
+    ap.add_argument("--no-dense", action="store_true", help="skip the lm-head, RMSNorm, MXFP4 and W8G32_F16S timings")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LAUNCHES_PER_STEP"),
                     help="write the rows=1 decode-step kernel's HBM traffic per launch from two rocprofv3 "
                          "--pmc counter collections (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run of "
@@ -329,6 +329,42 @@ def time_mx(nv, torch, dev, rows_list, reps):
     return out
 
 
+def time_w8(nv, torch, dev, rows_list, reps):
+    """The W8G32_F16S projection (nvfp4_w8g32_gemv) on a gate-sized [17408 x
+    5120] and a down-sized [5120 x 17408] matrix: random int8 codes and fp16
+    scales 2^-8..2^-6 drawn on the device, back-to-back calls between HIP
+    events; GB/s counts codes + scales once per call."""
+    g = torch.Generator(device=dev).manual_seed(2025)
+    out = {}
+    stream = torch.cuda.current_stream()
+    for n, k in ((17408, 5120), (5120, 17408)):
+        codes = torch.randint(-127, 128, (n, k), generator=g, device=dev, dtype=torch.int8)
+        scales = torch.exp2(torch.randint(-8, -5, (n, k // 32), generator=g, device=dev).float()).half()
+        wbytes = n * k + n * k // 32 * 2
+        res = {"shape": [n, k], "weight_bytes": wbytes, "by_rows": {}}
+        for r in rows_list:
+            x = torch.randn((r, k), generator=g, device=dev).to(torch.bfloat16)
+            y = torch.empty((r, n), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                nv.nvfp4_w8g32_gemv(codes, scales, x, out=y)
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(reps):
+                nv.nvfp4_w8g32_gemv(codes, scales, x, out=y)
+            stop.record(stream)
+            torch.cuda.synchronize()
+            us = start.elapsed_time(stop) * 1e3 / reps
+            gbs = wbytes / (us * 1e-6) / 1e9
+            res["by_rows"][str(r)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1),
+                                      "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+            log("w8g32 %dx%d rows=%d: %.2f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (
+                n, k, r, us, gbs, 100 * gbs / HBM_PEAK_GBS))
+        out["%dx%d" % (n, k)] = res
+        del codes, scales
+    return out
+
+
 def time_norm(nv, torch, dev, reps):
     """nvfp4_residual_rmsnorm at the 27B model's hidden size (k = 5120): the
     average call at decode row counts (1 and 8: a few tens of KB, bound by
@@ -444,6 +480,8 @@ def main():
     norm = None if args.no_dense else time_norm(nv, torch, dev, max(10, args.steps // 2))
     mx = None if args.no_dense else time_mx(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
                                             max(5, args.steps // 5))
+    w8 = None if args.no_dense else time_w8(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
+                                            max(5, args.steps // 5))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -480,6 +518,7 @@ def main():
         "dense_lm_head": dense,
         "residual_rmsnorm": norm,
         "mxfp4": mx,
+        "w8g32_f16s": w8,
     }
     print(json.dumps(line), flush=True)
 

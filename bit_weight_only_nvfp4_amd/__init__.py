@@ -40,7 +40,7 @@ EXPORTS = (
     "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
     "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16", "nvfp4_residual_rmsnorm",
-    "nvfp4_mxfp4_gemv",
+    "nvfp4_mxfp4_gemv", "nvfp4_w8g32_gemv",
 )
 
 
@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_void_p), vp], ctypes.c_int),
             "nvfp4_dense_gemv_bf16": ([vp, i64, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
             "nvfp4_mxfp4_gemv": ([vp, vp, i64, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
+            "nvfp4_w8g32_gemv": ([vp, vp, i64, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
             "nvfp4_residual_rmsnorm": ([vp, vp, vp, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, vp, vp],
                                        ctypes.c_int),
         }
@@ -325,6 +326,23 @@ def nvfp4_mxfp4_gemv(codes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
     x, rows, out = _gemv_common(x, None, out_dtype, out, n)
     _check("nvfp4_mxfp4_gemv",
            lib().nvfp4_mxfp4_gemv(_ptr(codes), _ptr(scales), n, k, _ptr(x), rows, _ptr(out), _OUT[out.dtype],
+                                  _stream(x.device)))
+    return out
+
+
+def nvfp4_w8g32_gemv(codes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out_dtype=torch.bfloat16,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """W8G32_F16S projection: codes int8 [n, k], scales float16 [n, k/32], x
+    bf16 [rows, k] -> y [rows, n]."""
+    if codes.dtype != torch.int8 or scales.dtype != torch.float16 or codes.dim() != 2:
+        raise TypeError("codes must be a 2-D int8 tensor and scales float16")
+    codes, scales = codes.contiguous(), scales.contiguous()
+    n, k = codes.shape
+    if tuple(scales.shape) != (n, k // 32):
+        raise ValueError("scales must be [n, k/32]")
+    x, rows, out = _gemv_common(x, None, out_dtype, out, n)
+    _check("nvfp4_w8g32_gemv",
+           lib().nvfp4_w8g32_gemv(_ptr(codes), _ptr(scales), n, k, _ptr(x), rows, _ptr(out), _OUT[out.dtype],
                                   _stream(x.device)))
     return out
 

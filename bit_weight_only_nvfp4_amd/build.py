@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnvfp4_hip.so")
-SOURCES = ["nvfp4_api.hip", "nvfp4_stream.hip", "nvfp4_pack.hip", "nvfp4_dense.hip", "nvfp4_norm.hip", "nvfp4_mx.hip"]
+SOURCES = ["nvfp4_api.hip", "nvfp4_stream.hip", "nvfp4_pack.hip", "nvfp4_dense.hip", "nvfp4_norm.hip", "nvfp4_mx.hip", "nvfp4_w8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

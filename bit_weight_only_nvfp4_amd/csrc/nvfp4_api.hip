@@ -425,6 +425,36 @@ int nvfp4_mxfp4_gemv(const void *codes, const void *scales, int64_t n, int64_t k
     return ok();
 }
 
+int nvfp4_w8g32_gemv(const void *codes, const void *scales, int64_t n, int64_t k, const void *x, int rows, void *y,
+                     int out_dtype, void *stream) {
+    static const char *fn = "nvfp4_w8g32_gemv";
+    if (!codes) return fail(NVFP4_E_NULL, "%s: codes is NULL", fn);
+    if (!scales) return fail(NVFP4_E_NULL, "%s: scales is NULL", fn);
+    if (n < 1 || n > kMaxN || k < 128 || k % 128 != 0 || k > ((int64_t)1 << 24))
+        return fail(NVFP4_E_SHAPE, "%s: n=%lld k=%lld (need 1 <= n <= 2^20, k a positive multiple of 128, k <= 2^24)",
+                    fn, (long long)n, (long long)k);
+    if (!aligned(codes, 16) || !aligned(scales, 8))
+        return fail(NVFP4_E_ALIGN, "%s: codes must be 16-byte and scales 8-byte aligned", fn);
+    int st = check_gemv_args(fn, x, rows, y, out_dtype);
+    if (st) return st;
+    const size_t ye = out_dtype == NVFP4_OUT_F32 ? 4 : 2;
+    const size_t xb = (size_t)rows * k * 2, yb = (size_t)rows * n * ye;
+    if (overlap(y, yb, x, xb)) return fail(NVFP4_E_OVERLAP, "%s: y overlaps x", fn);
+    if (overlap(y, yb, codes, (size_t)n * k) || overlap(y, yb, scales, (size_t)n * k / 16))
+        return fail(NVFP4_E_OVERLAP, "%s: y overlaps the weight", fn);
+    st = check_device(fn);
+    if (st) return st;
+    for (int j = 0; j < num_chunks(rows); ++j) {
+        int r0, nr;
+        chunk_of(rows, j, r0, nr);
+        hipError_t e = launch_w8(codes, scales, n, k, static_cast<const uint8_t *>(x) + (size_t)r0 * k * 2, nr,
+                                 static_cast<uint8_t *>(y) + (size_t)r0 * n * ye, out_dtype == NVFP4_OUT_F32,
+                                 static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_status(fn, e);
+    }
+    return ok();
+}
+
 int nvfp4_residual_rmsnorm(const void *residual, const void *delta, const void *weight, int64_t k, int rows,
                            float eps, int gemma_offset, void *residual_out, void *x, void *stream) {
     static const char *fn = "nvfp4_residual_rmsnorm";

@@ -203,6 +203,11 @@ hipError_t launch_dense(const void *w, int64_t n, int64_t k, const void *x, int 
 hipError_t launch_mx(const void *codes, const void *scales, int64_t n, int64_t k, const void *x, int rows, void *y,
                      int out_f32, hipStream_t stream);
 
+// W8G32_F16S projection (rows <= kKernelMaxRows, k % 128 == 0): int8 codes [n][k],
+// fp16 scales [n][k/32].
+hipError_t launch_w8(const void *codes, const void *scales, int64_t n, int64_t k, const void *x, int rows, void *y,
+                     int out_f32, hipStream_t stream);
+
 // Residual add + RMSNorm, one workgroup per row (k <= norm_max_k()).
 int64_t norm_max_k();
 hipError_t launch_residual_rmsnorm(const void *r, const void *h, const void *w, int64_t k, int rows, float eps,

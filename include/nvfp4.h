@@ -229,6 +229,17 @@ int nvfp4_dense_gemv_bf16(const void *W, int64_t n, int64_t k, const void *x, in
 int nvfp4_mxfp4_gemv(const void *codes, const void *scales, int64_t n, int64_t k, const void *x, int rows,
                      void *y, int out_dtype, void *stream);
 
+/* W8G32_F16S projection, the 8-bit format variant (signed 8-bit weights with
+ * one fp16 scale per 32 consecutive k of a row, symmetric; the pages name this
+ * encoding for the DFlash2 drafter's matrices), row-major:
+ *   y[r][j] = sum_k code[j][k] * scale[j][k/32] * x[r][k].
+ * codes: device int8 [n][k], 16-byte aligned; scales: device fp16 [n][k/32],
+ * 8-byte aligned; 1 <= n <= 2^20, k a positive multiple of 128, k <= 2^24;
+ * x, rows, y, out_dtype as for nvfp4_gemv (more than 16 rows run as row
+ * chunks).  No workspace; bitwise deterministic. */
+int nvfp4_w8g32_gemv(const void *codes, const void *scales, int64_t n, int64_t k, const void *x, int rows,
+                     void *y, int out_dtype, void *stream);
+
 /* Residual add + RMSNorm, the step that produces a projection's activations
  * (the blueprint page's kernel table: norm::residual_add_rms_norm; kern's
  * gemma_rms_norm is the variant with the Gemma offset).  Per row r < rows:

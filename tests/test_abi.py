@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(nv):
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     L = ctypes.CDLL(nv.LIB_PATH)
     for name in names:
         assert hasattr(L, name), name
@@ -252,6 +252,23 @@ def test_mxfp4_gemv_argument_errors(nv):
     assert _mx(nv, dtype=5) == E["NVFP4_E_DTYPE"]
     assert _mx(nv, y=XF + 64) == E["NVFP4_E_OVERLAP"]
     assert _mx(nv, y=FAKE + 1024) == E["NVFP4_E_OVERLAP"]
+
+
+def _w8(nv, c=FAKE, s=WF, n=256, k=512, x=XF, rows=1, y=YF, dtype=0):
+    return nv.lib().nvfp4_w8g32_gemv(c, s, n, k, x, rows, y, dtype, None)
+
+
+def test_w8g32_gemv_argument_errors(nv):
+    E = {v: k for k, v in nv.STATUS.items()}
+    assert _w8(nv, c=None) == E["NVFP4_E_NULL"]
+    assert _w8(nv, s=None) == E["NVFP4_E_NULL"]
+    assert _w8(nv, k=96) == E["NVFP4_E_SHAPE"]               # not a multiple of 128
+    assert _w8(nv, n=(1 << 20) + 1) == E["NVFP4_E_SHAPE"]
+    assert _w8(nv, rows=0) == E["NVFP4_E_ROWS"]
+    assert _w8(nv, s=WF + 4) == E["NVFP4_E_ALIGN"]
+    assert _w8(nv, c=FAKE + 8) == E["NVFP4_E_ALIGN"]
+    assert _w8(nv, y=XF + 64) == E["NVFP4_E_OVERLAP"]
+    assert _w8(nv, y=FAKE + 4096) == E["NVFP4_E_OVERLAP"]
 
 
 def _norm(nv, r=XF, h=WF, w=FAKE, k=512, rows=2, eps=1e-6, gemma=0, ro=YF, x=YF + 0x100000):
