@@ -478,10 +478,11 @@ def main():
                            max(5, args.steps // 5))
 
     norm = None if args.no_dense else time_norm(nv, torch, dev, max(10, args.steps // 2))
+    # calls of 25-150 us: enough back-to-back calls that launch start-up is a small share
     mx = None if args.no_dense else time_mx(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
-                                            max(5, args.steps // 5))
+                                            max(50, args.steps))
     w8 = None if args.no_dense else time_w8(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
-                                            max(5, args.steps // 5))
+                                            max(50, args.steps))
 
     cpu = None
     if not args.no_cpu_baseline:
