@@ -14,11 +14,16 @@
 // code * 2^e for e in -126..125).  The activations then feed the bf16 matrix
 // cores as stored: no activation staging, no scale multiply.
 //   * one workgroup per 64 features (four 16-feature products), 4 waves each
-//     over a quarter of k in steps of 128; two steps in flight;
-//   * per step a lane (q, n) takes k = 32 q .. 32 q + 31 of the step -- one MX
-//     block, so one scale byte per feature block -- as 16 bytes of codes per
-//     feature block and 64 bytes of its activation row; product m of the step
-//     uses k = 32 q + 8 m .. + 7 in both operands;
+//     over a quarter of k in steps of 256; two steps in flight (176
+//     registers, two waves per SIMD);
+//   * per step a lane (q, n) takes k = 64 q .. 64 q + 63 of the step -- two
+//     MX blocks, so two scale bytes per feature block -- as 32 contiguous
+//     bytes of codes per feature block (a row's four lanes read 128
+//     contiguous bytes) and 128 bytes of its activation row; product m of
+//     the step uses word m & 3 of block m >> 2 in both operands.  Measured on
+//     a [151936 x 5120] matrix: 126 us at 1 row against 130 with one block
+//     per lane in steps of 128 (116 registers, four waves per SIMD); 32
+//     features per workgroup or three steps in flight slower;
 //   * the waves' sums are added in LDS in wave order (deterministic).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,16 +38,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMxFB = 4;            // 16-feature blocks per workgroup
-constexpr int kMxFeatures = 16 * kMxFB;
 constexpr int kMxWaves = 4;
-constexpr int kMxStepK = 128;
-// Steps in flight per wave.  Measured on a [151936 x 5120] matrix: 2 (116
-// registers, four waves per SIMD) 130 us at 1 row against 138 with 4 (176
-// registers); 128 features per workgroup with 3 steps 134 us.  The kernel is
-// far from its bytes (about 3 TB/s): each step also makes as many scale-byte
-// requests (16 rows per feature block) as code requests.
-constexpr int kMxBufs = 2;
+constexpr int kMxStepK = 256;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kDeviceCoherent = 16;
 constexpr int kDropped = 0x7fffffff;
@@ -62,28 +59,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
+template <int FB>
 struct MxStep {
-    u32x4_t c[kMxFB];     // codes: k = 32 q .. + 31 of each feature block's row n
-    uint32_t s[kMxFB];    // its E8M0 scale byte
-    u32x4_t a[4];         // activations of row n, k = 32 q .. + 31
+    u32x4_t c[FB][2];     // codes: blocks 2 q and 2 q + 1 (k = 64 q .. + 63) of each feature block's row n
+    uint32_t s[FB][2];    // their E8M0 scale bytes
+    u32x4_t a[8];         // activations of row n, k = 64 q .. + 63
 };
 
+template <int FB>
 __device__ __forceinline__ void load_step(__amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr,
                                           __amdgpu_buffer_rsrc_t xr, int k0, int kend, int k, int q, int n16,
-                                          MxStep &st) {
-    const int kk = k0 + 32 * q;
-    const bool in = kk < kend;   // k is a multiple of 32: a lane's block is all in or all out
+                                          MxStep<FB> &st) {
+    // k is a multiple of 32: each of a lane's two blocks is all in or all out
+    const int kk = k0 + 64 * q;
+    const bool in0 = kk < kend, in1 = kk + 32 < kend;
     const int kh = k / 2, kb = k / 32;
-    const int co = in ? n16 * kh + kk / 2 : kOutside;
-    const int so = in ? n16 * kb + kk / 32 : kOutside;
-    const int xo = in ? (n16 * k + kk) * 2 : kOutside;
+    const int co0 = in0 ? n16 * kh + kk / 2 : kOutside, co1 = in1 ? n16 * kh + kk / 2 + 16 : kOutside;
+    const int so0 = in0 ? n16 * kb + kk / 32 : kOutside, so1 = in1 ? n16 * kb + kk / 32 + 1 : kOutside;
+    const int xo0 = in0 ? (n16 * k + kk) * 2 : kOutside, xo1 = in1 ? (n16 * k + kk) * 2 + 64 : kOutside;
 #pragma unroll
-    for (int fb = 0; fb < kMxFB; ++fb) {
-        st.c[fb] = __builtin_amdgcn_raw_buffer_load_b128(cr, co + fb * 16 * kh, 0, 0);
-        st.s[fb] = __builtin_amdgcn_raw_buffer_load_b8(sr, so + fb * 16 * kb, 0, 0);
+    for (int fb = 0; fb < FB; ++fb) {
+        st.c[fb][0] = __builtin_amdgcn_raw_buffer_load_b128(cr, co0 + fb * 16 * kh, 0, 0);
+        st.c[fb][1] = __builtin_amdgcn_raw_buffer_load_b128(cr, co1 + fb * 16 * kh, 0, 0);
+        st.s[fb][0] = __builtin_amdgcn_raw_buffer_load_b8(sr, so0 + fb * 16 * kb, 0, 0);
+        st.s[fb][1] = __builtin_amdgcn_raw_buffer_load_b8(sr, so1 + fb * 16 * kb, 0, 0);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st.a[m] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 16 * m, 0, 0);
+    for (int m = 0; m < 4; ++m) {
+        st.a[m] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo0 + 16 * m, 0, 0);
+        st.a[4 + m] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo1 + 16 * m, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -96,16 +101,23 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float scale) {
     return bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-__device__ __forceinline__ void mac_step(const MxStep &st, f32x4_t (&d)[kMxFB]) {
-    float sc[kMxFB];
+// Product m of the step takes word m & 3 of block m >> 2 in both operands: a
+// lane's codes are dequantized with its own block's scale, so a product may
+// mix the blocks of different lanes.
+template <int FB>
+__device__ __forceinline__ void mac_step(const MxStep<FB> &st, f32x4_t (&d)[FB]) {
+    float sc[FB][2];
 #pragma unroll
-    for (int fb = 0; fb < kMxFB; ++fb) sc[fb] = __builtin_bit_cast(float, (st.s[fb] & 0xffu) << 23);
+    for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+        for (int h = 0; h < 2; ++h) sc[fb][h] = __builtin_bit_cast(float, (st.s[fb][h] & 0xffu) << 23);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, st.a[m]);
 #pragma unroll
-        for (int fb = 0; fb < kMxFB; ++fb)
-            d[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dequant8(st.c[fb][m], sc[fb]), d[fb], 0, 0, 0);
+        for (int fb = 0; fb < FB; ++fb)
+            d[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dequant8(st.c[fb][m >> 2][m & 3], sc[fb][m >> 2]),
+                                                            d[fb], 0, 0, 0);
     }
 }
 
@@ -116,8 +128,11 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
     return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? nan : rne);
 }
 
+// FB 16-feature blocks per workgroup, BUFS steps in flight per wave.
+template <int FB, int BUFS>
 __global__ __launch_bounds__(kMxWaves * 64) void mx_kernel(MxArgs a) {
-    __shared__ float red[kMxWaves][kMxFB][16][16];   // [wave][feature block][row][feature]
+    constexpr int kMxFeatures = 16 * FB;
+    __shared__ float red[kMxWaves][FB][16][16];   // [wave][feature block][row][feature]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, n16 = lane & 15;
@@ -128,23 +143,23 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_kernel(MxArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)((size_t)a.rows * a.k * 2));
     const int kb = wave * a.kw, ke = min(a.k, kb + a.kw);
     const int steps = ke > kb ? (ke - kb + kMxStepK - 1) / kMxStepK : 0;
-    f32x4_t d[kMxFB];
+    f32x4_t d[FB];
 #pragma unroll
-    for (int fb = 0; fb < kMxFB; ++fb) d[fb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    MxStep st[kMxBufs];
+    for (int fb = 0; fb < FB; ++fb) d[fb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    MxStep<FB> st[BUFS];
 #pragma unroll
-    for (int i = 0; i < kMxBufs; ++i) load_step(cr, sr, xr, kb + i * kMxStepK, ke, a.k, q, n16, st[i]);
+    for (int i = 0; i < BUFS; ++i) load_step(cr, sr, xr, kb + i * kMxStepK, ke, a.k, q, n16, st[i]);
     // steps past the wave's last are loaded (reading nothing) but not used,
     // so the loads in flight never depend on control flow
-    for (int j = 0; j < steps; j += kMxBufs) {
+    for (int j = 0; j < steps; j += BUFS) {
 #pragma unroll
-        for (int i = 0; i < kMxBufs; ++i) {
+        for (int i = 0; i < BUFS; ++i) {
             if (j + i < steps) mac_step(st[i], d);
-            load_step(cr, sr, xr, kb + (j + i + kMxBufs) * kMxStepK, ke, a.k, q, n16, st[i]);
+            load_step(cr, sr, xr, kb + (j + i + BUFS) * kMxStepK, ke, a.k, q, n16, st[i]);
         }
     }
 #pragma unroll
-    for (int fb = 0; fb < kMxFB; ++fb)
+    for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][fb][4 * q + v][n16] = d[fb][v];
     __syncthreads();
@@ -180,8 +195,9 @@ hipError_t launch_mx(const void *codes, const void *scales, int64_t n, int64_t k
     a.out_f32 = out_f32;
     const int64_t per = (k + kMxWaves - 1) / kMxWaves;
     a.kw = (int)((per + kMxStepK - 1) / kMxStepK * kMxStepK);
-    const unsigned grid = (unsigned)((n + kMxFeatures - 1) / kMxFeatures);
-    hipLaunchKernelGGL(mx_kernel, dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+    constexpr int FB = 4, BUFS = 2;
+    const unsigned grid = (unsigned)((n + 16 * FB - 1) / (16 * FB));
+    hipLaunchKernelGGL((mx_kernel<FB, BUFS>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
