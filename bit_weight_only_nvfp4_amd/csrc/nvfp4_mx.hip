@@ -24,6 +24,10 @@
 //     a [151936 x 5120] matrix: 126 us at 1 row against 130 with one block
 //     per lane in steps of 128 (116 registers, four waves per SIMD); 32
 //     features per workgroup or three steps in flight slower;
+//   * scale bytes: byte loads cost more than their bytes (the same kernel
+//     with no scale loads took 85 us instead of 126), so where k is a
+//     multiple of 256 the row's 8 scale bytes of a step are one 8-byte load
+//     shared by its four lanes: 104 us;
 //   * the waves' sums are added in LDS in wave order (deterministic).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -62,11 +66,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 template <int FB>
 struct MxStep {
     u32x4_t c[FB][2];     // codes: blocks 2 q and 2 q + 1 (k = 64 q .. + 63) of each feature block's row n
-    uint32_t s[FB][2];    // their E8M0 scale bytes
+    uint32_t s[FB][2];    // their E8M0 scale bytes, or (WIDE) the row's 8 scale bytes of the step
     u32x4_t a[8];         // activations of row n, k = 64 q .. + 63
 };
 
-template <int FB>
+// WIDE (k a multiple of 256, scales 8-byte aligned): the four lanes of a row
+// load the row's 8 scale bytes of the step as one 8-byte word (one address,
+// merged), each picking its two bytes when it computes; otherwise each lane
+// loads its two bytes.
+template <int FB, bool WIDE>
 __device__ __forceinline__ void load_step(__amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr,
                                           __amdgpu_buffer_rsrc_t xr, int k0, int kend, int k, int q, int n16,
                                           MxStep<FB> &st) {
@@ -81,8 +89,16 @@ __device__ __forceinline__ void load_step(__amdgpu_buffer_rsrc_t cr, __amdgpu_bu
     for (int fb = 0; fb < FB; ++fb) {
         st.c[fb][0] = __builtin_amdgcn_raw_buffer_load_b128(cr, co0 + fb * 16 * kh, 0, 0);
         st.c[fb][1] = __builtin_amdgcn_raw_buffer_load_b128(cr, co1 + fb * 16 * kh, 0, 0);
-        st.s[fb][0] = __builtin_amdgcn_raw_buffer_load_b8(sr, so0 + fb * 16 * kb, 0, 0);
-        st.s[fb][1] = __builtin_amdgcn_raw_buffer_load_b8(sr, so1 + fb * 16 * kb, 0, 0);
+        if constexpr (WIDE) {
+            // steps are whole (k and the waves' k ranges are multiples of 256):
+            // so0 is the row's first scale of the step, 8-byte aligned
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, so0 - (in0 ? q * 2 : 0) + fb * 16 * kb, 0, 0);
+            st.s[fb][0] = v[0];
+            st.s[fb][1] = v[1];
+        } else {
+            st.s[fb][0] = __builtin_amdgcn_raw_buffer_load_b8(sr, so0 + fb * 16 * kb, 0, 0);
+            st.s[fb][1] = __builtin_amdgcn_raw_buffer_load_b8(sr, so1 + fb * 16 * kb, 0, 0);
+        }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -104,13 +120,20 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float scale) {
 // Product m of the step takes word m & 3 of block m >> 2 in both operands: a
 // lane's codes are dequantized with its own block's scale, so a product may
 // mix the blocks of different lanes.
-template <int FB>
-__device__ __forceinline__ void mac_step(const MxStep<FB> &st, f32x4_t (&d)[FB]) {
+template <int FB, bool WIDE>
+__device__ __forceinline__ void mac_step(const MxStep<FB> &st, int q, f32x4_t (&d)[FB]) {
     float sc[FB][2];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) sc[fb][h] = __builtin_bit_cast(float, (st.s[fb][h] & 0xffu) << 23);
+    for (int fb = 0; fb < FB; ++fb) {
+        uint32_t b0 = st.s[fb][0], b1 = st.s[fb][1];
+        if constexpr (WIDE) {   // bytes 2 q and 2 q + 1 of the row's 8
+            const uint32_t w = (q & 2) ? st.s[fb][1] : st.s[fb][0];
+            b0 = w >> (16 * (q & 1));
+            b1 = b0 >> 8;
+        }
+        sc[fb][0] = __builtin_bit_cast(float, (b0 & 0xffu) << 23);
+        sc[fb][1] = __builtin_bit_cast(float, (b1 & 0xffu) << 23);
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, st.a[m]);
@@ -129,7 +152,7 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 }
 
 // FB 16-feature blocks per workgroup, BUFS steps in flight per wave.
-template <int FB, int BUFS>
+template <int FB, int BUFS, bool WIDE>
 __global__ __launch_bounds__(kMxWaves * 64) void mx_kernel(MxArgs a) {
     constexpr int kMxFeatures = 16 * FB;
     __shared__ float red[kMxWaves][FB][16][16];   // [wave][feature block][row][feature]
@@ -148,14 +171,14 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_kernel(MxArgs a) {
     for (int fb = 0; fb < FB; ++fb) d[fb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     MxStep<FB> st[BUFS];
 #pragma unroll
-    for (int i = 0; i < BUFS; ++i) load_step(cr, sr, xr, kb + i * kMxStepK, ke, a.k, q, n16, st[i]);
+    for (int i = 0; i < BUFS; ++i) load_step<FB, WIDE>(cr, sr, xr, kb + i * kMxStepK, ke, a.k, q, n16, st[i]);
     // steps past the wave's last are loaded (reading nothing) but not used,
     // so the loads in flight never depend on control flow
     for (int j = 0; j < steps; j += BUFS) {
 #pragma unroll
         for (int i = 0; i < BUFS; ++i) {
-            if (j + i < steps) mac_step(st[i], d);
-            load_step(cr, sr, xr, kb + (j + i + BUFS) * kMxStepK, ke, a.k, q, n16, st[i]);
+            if (j + i < steps) mac_step<FB, WIDE>(st[i], q, d);
+            load_step<FB, WIDE>(cr, sr, xr, kb + (j + i + BUFS) * kMxStepK, ke, a.k, q, n16, st[i]);
         }
     }
 #pragma unroll
@@ -197,7 +220,10 @@ hipError_t launch_mx(const void *codes, const void *scales, int64_t n, int64_t k
     a.kw = (int)((per + kMxStepK - 1) / kMxStepK * kMxStepK);
     constexpr int FB = 4, BUFS = 2;
     const unsigned grid = (unsigned)((n + 16 * FB - 1) / (16 * FB));
-    hipLaunchKernelGGL((mx_kernel<FB, BUFS>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+    if (k % 256 == 0 && reinterpret_cast<uintptr_t>(scales) % 8 == 0)
+        hipLaunchKernelGGL((mx_kernel<FB, BUFS, true>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((mx_kernel<FB, BUFS, false>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -94,3 +94,26 @@ def test_mx_single_weights_over_the_scale_range(nv):
     bad = np.argwhere(~ok)
     assert ok.all(), "first mismatches (row, feature, got, want, scale byte): %s" % [
         (int(r), int(f), float(y32[r, f]), float(want[r, f]), int(s[f, 0])) for r, f in bad[:6]]
+
+
+@pytest.mark.parametrize("offset", [0, 1, 4])
+def test_mx_scale_pointer_alignment(nv, offset):
+    """k a multiple of 256 takes 8-byte scale loads when the scale pointer is
+    8-byte aligned and byte loads otherwise: the same matrix with its scales at
+    a byte offset inside a larger buffer must give the same, correct result."""
+    n, k = 300, 1024
+    rng = np.random.default_rng(4242)
+    c, s = oracle.mx_quantize((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    big = torch.zeros(s.size + 16, dtype=torch.uint8, device="cuda")
+    big[offset:offset + s.size] = _u8(s.reshape(-1))
+    sd = big[offset:offset + s.size].view(n, k // 32)
+    cd = _u8(c)
+    for rows in (1, 8):
+        xb = workloads.bf16_bits(rng.standard_normal((rows, k)).astype(np.float32))
+        x = _x(xb)
+        y32 = nv.nvfp4_mxfp4_gemv(cd, sd, x, out_dtype=torch.float32)
+        y16 = nv.nvfp4_mxfp4_gemv(cd, sd, x)
+        torch.cuda.synchronize()
+        ref, absd, ref16 = oracle.mx_gemv(c, s, xb)
+        check.check_gemv(y32.cpu().numpy(), y16.cpu().view(torch.int16).numpy().view(np.uint16), ref, absd, ref16,
+                         label="mxfp4 scales at +%d rows=%d" % (offset, rows))
