@@ -24,7 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnvfp4_hip.so")
 
 NVFP4_LAYOUT_MAGIC = 0x34465056
-NVFP4_LAYOUT_VERSION = 2
+NVFP4_LAYOUT_VERSION = 3
 NVFP4_MAX_ROWS = 128
 NVFP4_OUT_BF16 = 0
 NVFP4_OUT_F32 = 1

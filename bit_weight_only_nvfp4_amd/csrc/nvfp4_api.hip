@@ -130,9 +130,9 @@ int check_overlaps(const char *fn, const StreamCall *calls, int ncalls, const vo
 }
 
 // A call of more than kKernelMaxRows rows runs as ceil(rows / 16) calls of
-// balanced row counts (every chunk has at least rows / nchunks rows, so from
-// 5 rows on every chunk stays on the fp16 products and a row's result does
-// not depend on the call's row count); each chunk reads the weights once.
+// balanced row counts; each chunk reads the weights once.  A row's result does
+// not depend on the chunk it falls in (every row count runs the same
+// arithmetic per row).
 int num_chunks(int rows) { return (rows + kKernelMaxRows - 1) / kKernelMaxRows; }
 
 void chunk_of(int rows, int j, int &r0, int &nr) {
@@ -363,6 +363,7 @@ int nvfp4_sequence_launches(const nvfp4_call *calls, int ncalls) {
             chunk_of(c.rows, j, r0, nr);
             StreamCall s{};
             s.plan.rows = nr;
+            s.plan.krows = kernel_rows(nr);
             sc.push_back(s);
         }
     }

@@ -4,9 +4,10 @@
 // Device codecs (verified exhaustively against the CPU oracle through
 // nvfp4_dequant and the quantizer tests):
 //   * E2M1 pair -> bf16 pair: v_cvt_scalef32_pk_bf16_fp4 with scale 1.0.  The
-//     instruction applies only the exponent of its fp32 scale operand, so the
-//     E4M3 group scale (which has mantissa bits) is applied separately; the low
-//     nibble becomes the low bf16.
+//     instruction applies only the exponent of its fp32 scale operand (measured:
+//     scale 1.5 leaves a code as is, 3.0 doubles it), so the E4M3 group scale
+//     (which has mantissa bits) is applied separately; the low nibble becomes
+//     the low bf16.
 //   * OCP E4M3 byte -> fp32: v_cvt_f32_fp8 (OCP encoding on gfx950, NaN kept).
 #pragma once
 
@@ -17,31 +18,36 @@
 
 namespace nvfp4 {
 
-// ---- packed layout (version 2) -------------------------------------------
-// A super-tile (strip s of 64 features, k from 256 u) is an array of 16-byte
-// entries: 16 code chunks of 32 entries (chunk c = 4 kb + fb, entry 16 h + j:
-// codes of feature 16 fb + j, k = 64 kb + 32 h .. + 31 of the super-tile),
-// then 64 scale entries (entry 16 g + j, byte 4 kb + fb: scale of feature
-// 16 fb + j, group 4 kb + g of the super-tile).
+// ---- packed layout (version 3) -------------------------------------------
+// A super-tile (strip s of 64 features, k from 256 u) is 8 code chunks of
+// 1 KB, then a 1 KB scale chunk.  Lane l = 16 q + n of a wave reads bytes
+// 16 l .. 16 l + 15 of each chunk:
+//   code chunk c, dword j: the 8 codes (4 bytes, low nibble first) of feature
+//     16 (c >> 1) + n, k = 32 (4 (c & 1) + j) + 8 q .. + 7 of the super-tile;
+//   scale chunk, byte 8 b + t: the E4M3 scale of feature 16 (2 (q >> 1) + b) + n,
+//     group 2 t + (q & 1) of the super-tile.
+// This is the B operand of the 16x16x32 matrix-core product exactly as one
+// lane needs it (nvfp4_core.h), and every wave load is a run of whole,
+// aligned 128-byte lines.
 constexpr int kHeaderBytes = 256;
 constexpr int kStripN = 64;        // output features per strip
 constexpr int kSuperK = 256;       // k per super-tile
-constexpr int kFeatureBlock = 16;  // features per matrix-core product
-constexpr int kKBlock = 64;        // k per matrix-core product
-constexpr int kCodeChunks = (kStripN / kFeatureBlock) * (kSuperK / kKBlock);   // 16
-constexpr int kCodeChunkBytes = kFeatureBlock * kKBlock / 2;                    // 512
+constexpr int kCodeChunks = 8;
+constexpr int kCodeChunkBytes = 1024;
 constexpr int kScaleOffset = kCodeChunks * kCodeChunkBytes;                     // 8192
 constexpr int kSuperBytes = kScaleOffset + 16 * kStripN;                        // 9216
 constexpr int kEntriesPerSuper = kSuperBytes / 16;                              // 576
 
-// Byte offset, within a super-tile, of the code entry holding feature f (0..63
-// in the strip) and k = kr .. kr + 31 (kr a multiple of 32 below 256).
-__host__ __device__ inline int code_entry_offset(int f, int kr) {
-    return ((kr >> 6) * 4 + (f >> 4)) * kCodeChunkBytes + ((((kr >> 5) & 1) << 4) + (f & 15)) * 16;
+// Byte offset, within a super-tile, of the 4 code bytes of feature f (0..63 in
+// the strip) for k = kp .. kp + 7 (kp a multiple of 8 below 256).
+__host__ __device__ inline int code_piece_offset(int f, int kp) {
+    const int ks = kp >> 5, q = (kp >> 3) & 3;
+    return (2 * (f >> 4) + (ks >> 2)) * kCodeChunkBytes + (16 * q + (f & 15)) * 16 + 4 * (ks & 3);
 }
 // Byte offset, within a super-tile, of the scale of feature f, group gt (0..15).
 __host__ __device__ inline int scale_byte_offset(int f, int gt) {
-    return kScaleOffset + (((gt & 3) << 4) + (f & 15)) * 16 + (gt >> 2) * 4 + (f >> 4);
+    const int fb = f >> 4, q = 2 * (fb >> 1) + (gt & 1);
+    return kScaleOffset + (16 * q + (f & 15)) * 16 + 8 * (fb & 1) + (gt >> 1);
 }
 
 // Projection workspace layout.  Fixed regions that do not depend on the
@@ -123,53 +129,39 @@ constexpr int kMaxWorkgroups = 256;      // one per CU on MI355X
 constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workgroup
 constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
 constexpr int kMaxWavesPerWg = 8;
-// Rows one kernel call computes (the instantiated row counts are 1..16);
-// calls of more rows are cut into row chunks by the host.
+// Rows one kernel call computes; calls of more rows are cut into row chunks
+// by the host.  A call runs on the kernel instantiated for the smallest of
+// 1, 2, 4, 6, 8, 12, 16 rows that holds it: the rows past the call's read
+// zero activations and their outputs are dropped.  Every row is computed by
+// the same instructions in the same product positions at every row count, so
+// padding changes no result.
 constexpr int kKernelMaxRows = 16;
 static_assert(NVFP4_MAX_ROWS >= kKernelMaxRows, "the ABI's row limit covers the kernel's");
+__host__ __device__ constexpr int kernel_rows(int rows) {
+    return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 6 ? 6 : rows <= 8 ? 8 : rows <= 12 ? 12 : 16;
+}
 // Waves per workgroup and super-tiles each wave keeps in flight (NB, even,
 // so that a pair's gate and up super-tiles of one position are always in
-// flight together).  The super-tiles in flight live in registers.  Two waves
-// per SIMD with two super-tiles each fit in 256 registers at every row count
-// (about 145 at 1 row, 245 at 8).  Measured against it on the decode-step
-// sweep: one wave per SIMD with six in flight and three waves per SIMD with
-// two were 6-15% slower at 1-2 rows, and four in flight at two waves per SIMD
-// (1-2 rows, 225-252 registers) within 1% either way.  The calls of a decode
-// step are short (a few super-tiles per wave), and what a call costs beyond
-// its bytes is latency at its start and end, which more bytes in flight do
-// not shorten.  A wave can have at most 63 vector-memory loads outstanding (a
-// super-tile takes 9 plus one per 64 lanes of activations), which bounds NB
-// at 6 (1-2 rows) or 4 (up to 8 rows).
-__host__ __device__ constexpr int max_waves_for_rows(int rows) { return 8; }
-__host__ __device__ constexpr int pipe_depth_for_rows(int rows) { return 2; }
-// Super-tile arithmetic: the fp16 matrix-core path (dequantized weights, fp16
-// activations) from 5 rows on, the block-scaled fp8 x fp4 path below; and the
-// per-wave LDS bytes of its staged activations (core::XStage16, core::XStage1
-// at one row, core::XStage).
-// The fp8 path masks 3 of every 4 product rows and splits each activation in
-// two; the fp16 path pays instead for converting every code (about 512 vector
-// instructions per super-tile, whatever the row count).  Measured on the
-// decode-step sweep, fp16 is 8-12% slower at 1-4 rows (one row quad: 16
-// products per super-tile on the fp8 path) and 1.4-4.7% faster at 5-8 (two
-// row quads, 32 products).
-constexpr int kF16FromRows = 5;
-__host__ __device__ constexpr bool use_f16_core(int rows) { return rows >= kF16FromRows; }
-__host__ __device__ constexpr int x_stage_bytes(int rows) {
-    return use_f16_core(rows) ? (rows + 1) / 2 * 2 * 528 + 16 + 64 + 1024 : rows == 1 ? 2112 : 2304 * ((rows + 3) / 4) + 32;
+// flight together).  The super-tiles in flight live in registers.  Neither
+// depends on the row count: the plan, and with it every summation order, is
+// the same for every row count.
+__host__ __device__ constexpr int max_waves_for_rows(int) { return 8; }
+__host__ __device__ constexpr int pipe_depth_for_rows(int) { return 2; }
+// Per-wave LDS bytes of the staged activations (core::XStageG) and rows per
+// wave-reduction slot (the D rows the lanes hold: 2 per v, 8 per row set).
+__host__ __device__ constexpr int x_stage_bytes(int krows) { return 2 * ((krows + 1) / 2) * 528 + 16; }
+__host__ __device__ constexpr int red_rows(int krows) {
+    return 8 * ((krows + 7) / 8 - 1) + 2 * (((krows < 8 ? krows : 8) + 1) / 2);
 }
-
-// Rows per wave-reduction slot (a wave's sums of one matrix for one strip):
-// on the fp16 path each lane stores the rows of its own products, all 16.
-__host__ __device__ constexpr int red_rows(int rows) { return use_f16_core(rows) ? 16 : rows; }
 
 struct StreamPlan {
     int64_t n, k;
-    int rows, nmat;
+    int rows, krows, nmat;    // rows of the call, rows of the kernel that runs it
     int strips, supers;       // S, T
     int G, F, R;              // workgroups, owned strips per workgroup, shared strips
     int waves;                // waves per workgroup taking part in the call
     int max_pieces;           // most pieces any shared strip is cut into
-    size_t partial_bytes;     // fp32 partial sums [R][max_pieces][nmat][rows][64] (0 if no strip is cut)
+    size_t partial_bytes;     // fp32 partial sums [R][max_pieces][nmat][krows][64] (0 if no strip is cut)
     size_t lds_bytes;
 };
 
@@ -183,7 +175,7 @@ struct StreamCall {
 };
 
 StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual);
-size_t stream_lds_bytes(int rows, int waves);
+size_t stream_lds_bytes(int krows, int waves);
 // Workspace bytes for these calls run by launch_sequence (one call: what
 // nvfp4_gemv needs; several: the completion counts too).
 size_t sequence_workspace_bytes(const StreamCall *calls, int ncalls);

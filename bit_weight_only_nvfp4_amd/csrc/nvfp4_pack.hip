@@ -1,7 +1,8 @@
 // nvfp4_pack.hip -- weight preparation on the device for gfx950:
 //   pack     canonical codes/scales -> super-tiled layout (byte permutation);
 //   unpack   the inverse;
-//   dequant  packed -> fp32 through the projection kernels' decode routines;
+//   dequant  packed -> fp32 (codes converted by the same instruction the
+//            projection kernels use; scales and s_g applied in fp32);
 //   quantize fp32 weights -> packed NVFP4 (the step before the projection).
 // The kern README describes this stage as device-side weight preparation
 // ("weight_prep" kernel, a "load" program that fills fused qkv / gate_up
@@ -22,27 +23,31 @@ __device__ void write_header(void *packed, float global_scale, int64_t n, int64_
     for (int i = 2; i < kHeaderBytes / 16; ++i) h[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Feature (in the strip), first k (in the super-tile) and kind of entry e of
-// a super-tile: code entries e < 512, scale entries after.
+// Entry e of a super-tile (16 bytes, read by lane l = e % 64 of a wave):
+// code entries e < 512 (chunk c = e / 64), then the 64 scale entries.
+//   code entry: dword j = the 8 codes of feature 16 (c >> 1) + n for
+//     k = 32 (4 (c & 1) + j) + 8 q .. + 7 (q = l >> 4, n = l & 15);
+//   scale entry: byte b = the scale of feature 16 (2 (q >> 1) + (b >> 3)) + n,
+//     group 2 (b & 7) + (q & 1).
 struct Entry {
     bool code;
-    int f;    // code entry: its feature; scale entry: feature of byte 0 (fb = 0)
-    int kr;   // code entry: first k; scale entry: group g (0..3) of its bytes
+    int c, q, n;
 };
 __device__ __forceinline__ Entry entry_of(int e) {
     Entry d;
-    d.code = e < kCodeChunks * 32;
-    if (d.code) {
-        const int c = e >> 5, le = e & 31;
-        d.f = (c & 3) * 16 + (le & 15);
-        d.kr = (c >> 2) * kKBlock + (le >> 4) * 32;
-    } else {
-        const int l = e - kCodeChunks * 32;
-        d.f = l & 15;
-        d.kr = l >> 4;
-    }
+    d.code = e < kCodeChunks * 64;
+    const int l = d.code ? (e & 63) : e - kCodeChunks * 64;
+    d.c = d.code ? e >> 6 : 0;
+    d.q = l >> 4;
+    d.n = l & 15;
     return d;
 }
+// code entry: feature (in the strip) and first k (in the super-tile) of dword j
+__device__ __forceinline__ int code_f(const Entry &d) { return 16 * (d.c >> 1) + d.n; }
+__device__ __forceinline__ int code_k(const Entry &d, int j) { return 32 * (4 * (d.c & 1) + j) + 8 * d.q; }
+// scale entry: feature (in the strip) and group (in the super-tile) of byte b
+__device__ __forceinline__ int scale_f(const Entry &d, int b) { return 16 * (2 * (d.q >> 1) + (b >> 3)) + d.n; }
+__device__ __forceinline__ int scale_g(const Entry &d, int b) { return 2 * (b & 7) + (d.q & 1); }
 
 __device__ __forceinline__ uint4 pack16(const uint8_t (&b)[16]) {
     uint4 o;
@@ -69,16 +74,20 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
 #pragma unroll
     for (int i = 0; i < 16; ++i) b[i] = 0;
     if (d.code) {
-        const int64_t f = s * kStripN + d.f, k0 = u * kSuperK + d.kr;
+        const int64_t f = s * kStripN + code_f(d);
         if (f < n) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (k0 + 2 * i < k) b[i] = codes[f * (k / 2) + k0 / 2 + i];
+            for (int j = 0; j < 4; ++j) {
+                const int64_t k0 = u * kSuperK + code_k(d, j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (k0 + 2 * i < k) b[4 * j + i] = codes[f * (k / 2) + k0 / 2 + i];
+            }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {   // byte 4 kb + fb
-            const int64_t f = s * kStripN + (i & 3) * 16 + d.f, gi = u * (kSuperK / 16) + (i >> 2) * 4 + d.kr;
+        for (int i = 0; i < 16; ++i) {
+            const int64_t f = s * kStripN + scale_f(d, i), gi = u * (kSuperK / 16) + scale_g(d, i);
             if (f < n && gi < k / 16) b[i] = scales[f * (k / 16) + gi];
         }
     }
@@ -98,51 +107,54 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__
     const uint4 o = *reinterpret_cast<const uint4 *>(packed + kHeaderBytes + st * kSuperBytes + e * 16);
     const uint32_t w[4] = {o.x, o.y, o.z, o.w};
     if (d.code) {
-        const int64_t f = s * kStripN + d.f, k0 = u * kSuperK + d.kr;
+        const int64_t f = s * kStripN + code_f(d);
         if (f >= n) return;
-        for (int i = 0; i < 16; ++i)
-            if (k0 + 2 * i < k) codes[f * (k / 2) + k0 / 2 + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        for (int j = 0; j < 4; ++j) {
+            const int64_t k0 = u * kSuperK + code_k(d, j);
+            for (int i = 0; i < 4; ++i)
+                if (k0 + 2 * i < k) codes[f * (k / 2) + k0 / 2 + i] = (uint8_t)(w[j] >> (8 * i));
+        }
     } else {
         for (int i = 0; i < 16; ++i) {
-            const int64_t f = s * kStripN + (i & 3) * 16 + d.f, gi = u * (kSuperK / 16) + (i >> 2) * 4 + d.kr;
+            const int64_t f = s * kStripN + scale_f(d, i), gi = u * (kSuperK / 16) + scale_g(d, i);
             if (f < n && gi < k / 16) scales[f * (k / 16) + gi] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
         }
     }
 }
 
-// one thread per code entry: 32 weights of one feature
+// one thread per code entry: 4 runs of 8 weights of one feature, each run
+// converted by the instruction the projection kernels use for the codes
+// (v_cvt_scalef32_pk_bf16_fp4, exact) and multiplied by its group's E4M3 scale
+// (exact: at most 6 significant bits), then by s_g (one rounding)
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ packed, int64_t n, int64_t k,
                                                       int64_t T, int64_t total, float *__restrict__ out) {
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= total) return;
-    const int64_t st = id / (kCodeChunks * 32);
-    const int e = (int)(id - st * (kCodeChunks * 32));
+    const int64_t st = id / (kCodeChunks * 64);
+    const int e = (int)(id - st * (kCodeChunks * 64));
     const int64_t s = st / T, u = st % T;
     const Entry d = entry_of(e);
-    const int64_t f = s * kStripN + d.f;
+    const int fs = code_f(d);
+    const int64_t f = s * kStripN + fs;
     if (f >= n) return;
     const uint8_t *sup = packed + kHeaderBytes + st * kSuperBytes;
     const uint4 cw = *reinterpret_cast<const uint4 *>(sup + e * 16);
     const float sg = reinterpret_cast<const Header *>(packed)->global_scale;
     const uint32_t cwv[4] = {cw.x, cw.y, cw.z, cw.w};
-    const int64_t k0 = u * kSuperK + d.kr;
-    float *dst = out + f * k + k0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (k0 + 16 * h >= k) break;
-        const uint32_t sbyte = sup[scale_byte_offset(d.f, (d.kr >> 4) + h)];
-        const float sc = e4m3_to_f32_dyn(sbyte, 0);
+    for (int j = 0; j < 4; ++j) {
+        const int kp = code_k(d, j);
+        const int64_t k0 = u * kSuperK + kp;
+        if (k0 >= k) continue;
+        const float sc = e4m3_to_f32<0>(sup[scale_byte_offset(fs, kp >> 4)]);
+        const uint32_t word = cwv[j];
+        const bf16x2_t p[4] = {e2m1x2_to_bf16x2<0>(word), e2m1x2_to_bf16x2<1>(word),
+                               e2m1x2_to_bf16x2<2>(word), e2m1x2_to_bf16x2<3>(word)};
+        float *dst = out + f * k + k0;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint32_t word = cwv[2 * h + q];
-            const bf16x2_t p[4] = {e2m1x2_to_bf16x2<0>(word), e2m1x2_to_bf16x2<1>(word),
-                                   e2m1x2_to_bf16x2<2>(word), e2m1x2_to_bf16x2<3>(word)};
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                // code*scale is exact (<= 6 significant bits); one rounding for * s_g
-                dst[16 * h + 8 * q + 2 * b] = (bf16_lo_to_f32(p[b]) * sc) * sg;
-                dst[16 * h + 8 * q + 2 * b + 1] = (bf16_hi_to_f32(p[b]) * sc) * sg;
-            }
+        for (int b = 0; b < 4; ++b) {
+            dst[2 * b] = (bf16_lo_to_f32(p[b]) * sc) * sg;
+            dst[2 * b + 1] = (bf16_hi_to_f32(p[b]) * sc) * sg;
         }
     }
 }
@@ -260,7 +272,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
     const int64_t s = f / kStripN, fs = f % kStripN;
     const int64_t u = g / (kSuperK / 16), q = g % (kSuperK / 16);
     uint8_t *sup = packed + kHeaderBytes + (s * T + u) * kSuperBytes;
-    *reinterpret_cast<uint2 *>(sup + code_entry_offset((int)fs, (int)(q * 16) & ~31) + (q & 1) * 8) = make_uint2(lo, hi);
+    *reinterpret_cast<uint32_t *>(sup + code_piece_offset((int)fs, (int)q * 16)) = lo;
+    *reinterpret_cast<uint32_t *>(sup + code_piece_offset((int)fs, (int)q * 16 + 8)) = hi;
     sup[scale_byte_offset((int)fs, (int)q)] = (uint8_t)e;
 }
 
@@ -288,7 +301,7 @@ hipError_t launch_unpack(const void *packed, int64_t n, int64_t k, uint8_t *code
 
 hipError_t launch_dequant(const void *packed, int64_t n, int64_t k, float *out, hipStream_t stream) {
     const int64_t T = num_supers(k);
-    const int64_t total = num_strips(n) * T * kCodeChunks * 32;
+    const int64_t total = num_strips(n) * T * kCodeChunks * 64;
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
                        static_cast<const uint8_t *>(packed), n, k, T, total, out);
     return hipGetLastError();

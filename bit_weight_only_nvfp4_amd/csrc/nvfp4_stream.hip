@@ -58,7 +58,7 @@ struct CallDesc {
     int max_pieces;
     int waves;            // waves taking part
     int flags;            // kPair | kOutF32 | kReloadX
-    int pad;
+    int rows;             // the call's rows (the kernel's ROWS may be more: those rows read and write nothing)
 };
 constexpr int kPair = 1, kOutF32 = 2;
 // x is written by the call before this one in the same launch: the activations
@@ -112,8 +112,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t b
 // this lane's chunks of the activation window.
 template <int ROWS>
 struct Tile {
-    static constexpr int XR = core::XStage<ROWS>::XR;
-    uint4 wc[kCodeChunks / 2];
+    static constexpr int XR = core::XStageG<ROWS>::XR;
+    uint4 wc[kCodeChunks];
     uint4 ws;
     uint4 xv[XR];
 };
@@ -155,8 +155,8 @@ __device__ __forceinline__ void load_tile(const TileSrc &t, const uint8_t *zero,
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int l = 0; l < kCodeChunks / 2; ++l)
-        b.wc[l] = load_nt(t.real ? t.base + l * 2 * kCodeChunkBytes + lane * 16 : zero);
+    for (int l = 0; l < kCodeChunks; ++l)
+        b.wc[l] = load_nt(t.real ? t.base + l * kCodeChunkBytes + lane * 16 : zero);
     b.ws = load_nt(t.real ? t.base + kScaleOffset + lane * 16 : zero);
     // keep the whole tile's loads ahead of what follows (the scheduler would
     // otherwise sink them into the previous tile's arithmetic, after its wait)
@@ -176,15 +176,15 @@ __device__ __forceinline__ TileSrc pick(bool first, const TileSrc &a, const Tile
 
 // Buffer resource over a call's outputs: stores at an offset past its size
 // are dropped by the hardware, which masks the lanes past the last feature
-// without a branch.
-template <int ROWS>
+// and the kernel rows past the call's without a branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t output_rsrc(const CallDesc &d) {
-    return rsrc(d.y, (uint32_t)(ROWS * d.n * ((d.flags & kOutF32) ? 4 : 2)));
+    return rsrc(d.y, (uint32_t)(d.rows * d.n * ((d.flags & kOutF32) ? 4 : 2)));
 }
 
-template <int ROWS>
+// Buffer resource over a call's activations: loads past them (the kernel
+// rows past the call's, k past the last) read zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const CallDesc &d) {
-    return rsrc(d.x, (uint32_t)(ROWS * d.k * 2));
+    return rsrc(d.x, (uint32_t)(d.rows * d.k * 2));
 }
 
 // Apply the tensor scales and the SiLU product (pair) to the strip sums g, u
@@ -282,46 +282,48 @@ __device__ __forceinline__ Cursor cursor_at(const CallDesc &d, const Geometry &q
 // wave-uniform guards: a rolled loop or a divergent branch there makes the
 // compiler assume that tile loads may still be in flight at the top of the
 // tile loop, and wait for them.
-template <int ROWS, int AR>
+template <int ROWS>
+using Acc = float[2][4][core::XStageG<ROWS>::RS][core::XStageG<ROWS>::NV];
+
+template <int ROWS>
 __device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc &d, const Geometry &q, int g,
                                                int k, float *red, const float (&sg)[2],
                                                __amdgpu_buffer_rsrc_t yr, int wave, int sw, int nwc, int lane,
-                                               float (&acc)[2][4][AR], int (&pub)[2]) {
+                                               Acc<ROWS> &acc, int (&pub)[2]) {
+    using XS = core::XStageG<ROWS>;
     const bool pair = d.flags & kPair;
     constexpr int RR = red_rows(ROWS);   // rows per slot of `red`
     __syncthreads();   // the previous segment's reads of `red` are done
-    // slots in position order (sw): the sums below run in that order
-    // a pair's accumulators are its gate and up sums; a single projection's
-    // are two halves of its sum (even and odd tiles of the wave)
-    if constexpr (use_f16_core(ROWS)) {
-        // lane 16 q + n holds rows 4 q + v of features 16 fb + n, already
-        // summed over k: each lane writes its own, rows past ROWS (exact
-        // zeros) included, since the slots have 16 rows on this path
-        float *base = red + (sw * 2 * RR + 4 * (lane >> 4)) * kStripN + (lane & 15);
+    // Slots in position order (sw): the sums below run in that order.  A
+    // pair's accumulators are its gate and up sums; a single projection's
+    // are two halves of its sum (even and odd tiles of the wave).  Lane
+    // 16 q + n holds group half q & 1 of rows 8 rs + 2 v + (q >> 1) of feature
+    // 16 fb + n: the two halves are added across lanes 16 apart, and both
+    // lanes store the same sum (every D row of the slot is written, the rows
+    // past ROWS being sums of zeros).
+    const int n = lane & 15, rp = lane >> 5;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int fb = 0; fb < 4; ++fb) {
-                base[v * kStripN + 16 * fb] = pair ? acc[0][fb][v] : acc[0][fb][v] + acc[1][fb][v];
-                if (pair) base[(RR + v) * kStripN + 16 * fb] = acc[1][fb][v];
-                acc[0][fb][v] = 0.0f;
-                acc[1][fb][v] = 0.0f;
-            }
-    } else {
+        for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            float g4[4], u4[4];
+            for (int rs = 0; rs < XS::RS; ++rs)
 #pragma unroll
-            for (int fb = 0; fb < 4; ++fb) {
-                g4[fb] = pair ? acc[0][fb][r] : acc[0][fb][r] + acc[1][fb][r];
-                u4[fb] = acc[1][fb][r];
-                acc[0][fb][r] = 0.0f;
-                acc[1][fb][r] = 0.0f;
-            }
-            red[((sw * 2 + 0) * RR + r) * kStripN + lane] = core::strip_total(g4, lane);
-            if (pair) red[((sw * 2 + 1) * RR + r) * kStripN + lane] = core::strip_total(u4, lane);
-        }
-    }
+                for (int v = 0; v < XS::NV; ++v) {
+                    float t = m == 0 ? (pair ? acc[0][fb][rs][v] : acc[0][fb][rs][v] + acc[1][fb][rs][v])
+                                     : acc[1][fb][rs][v];
+                    t += __shfl_xor(t, 16);
+                    if (m == 0 || pair)
+                        red[((sw * 2 + m) * RR + 8 * rs + 2 * v + rp) * kStripN + 16 * fb + n] = t;
+                }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int rs = 0; rs < XS::RS; ++rs)
+#pragma unroll
+                for (int v = 0; v < XS::NV; ++v) acc[m][fb][rs][v] = 0.0f;
     __syncthreads();
     if (wave != 0) return;
     float v[2][ROWS];
@@ -530,38 +532,27 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     // Position order of the waves: wave 0 comes last, so it gets the fewest
     // super-tiles -- it also reduces and writes every result.
     const int sw = wave == 0 ? nwb - 1 : wave - 1;
-    constexpr bool kF16 = use_f16_core(ROWS), kOne = !kF16 && ROWS == 1;
-    using XS = std::conditional_t<kF16, core::XStage16<ROWS>,
-                                  std::conditional_t<kOne, core::XStage1, core::XStage<ROWS>>>;
+    using XS = core::XStageG<ROWS>;
     static_assert(XS::BYTES == x_stage_bytes(ROWS), "host LDS sizing assumes this staging size");
     static_assert(XS::XR == Tile<ROWS>::XR, "one activation chunk layout");
     uint8_t *xs = smem + (size_t)wave * XS::BYTES;   // this wave's staged activations
     float *red = reinterpret_cast<float *>(smem + (size_t)nwb * XS::BYTES);
-    constexpr int kZeroWords = kF16 ? core::XStage16<ROWS>::ZERO_WORDS : 8;   // the staging's zero bytes
-    if constexpr (kOne) core::init_x1(xs, lane);
-    else if (lane < kZeroWords) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;
-    // one staging and one product per super-tile, on the path chosen for ROWS
-    auto stage = [&](const Tile<ROWS> &t) {
-        if constexpr (kF16) core::stage_x16<ROWS>(t.xv, xs, lane);
-        else if constexpr (kOne) core::stage_x1(t.xv, xs, lane);
-        else core::stage_x<ROWS>(t.xv, xs, lane);
-    };
-    // Accumulators: the fp16 path's lanes hold 4 rows each (their products'
-    // rows), the other paths every row in every lane.
-    constexpr int AR = kF16 ? 4 : ROWS;
-    auto product = [&](const Tile<ROWS> &t, float (&ac)[4][AR]) {
-        if constexpr (kF16) core::core_f16<ROWS>(t.wc, t.ws, xs, lane, ac);
-        else if constexpr (kOne) core::core_mx1(t.wc, t.ws, xs, lane, ac);
-        else core::core_mx<ROWS>(t.wc, t.ws, xs, lane, ac);
+    if (lane < 4) reinterpret_cast<uint32_t *>(xs + XS::ZERO_OFF)[lane] = 0u;   // the staging's zero bytes
+    // one staging and one product per super-tile
+    auto stage = [&](const Tile<ROWS> &t) { core::stage_g<ROWS>(t.xv, xs, lane); };
+    auto product = [&](const Tile<ROWS> &t, float (&ac)[4][XS::RS][XS::NV]) {
+        core::core_g<ROWS>(t.wc, t.ws, xs, lane, ac);
     };
 
-    float acc[2][4][AR];
+    Acc<ROWS> acc;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-            for (int r = 0; r < AR; ++r) acc[m][fb][r] = 0.0f;
+            for (int rs = 0; rs < XS::RS; ++rs)
+#pragma unroll
+                for (int v = 0; v < XS::NV; ++v) acc[m][fb][rs][v] = 0.0f;
     // The call table, copied into LDS once: reading a call's descriptor from
     // the kernel arguments at the start of every call costs a cache miss each
     // time; from LDS it is a few cycles.  The words are wave-uniform.
@@ -638,7 +629,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         TileSrc s;
         const int u = cu.u0 + (i - cu.start);
         s.base = (up ? d.w1 : d.w0) + kHeaderBytes + ((size_t)cu.strip * d.T + u) * kSuperBytes;
-        s.xr = x_rsrc<ROWS>(d);
+        s.xr = x_rsrc(d);
         s.kbase = u * kSuperK;
         s.k = d.k;
         s.real = real;
@@ -666,8 +657,8 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         const bool pair = d.flags & kPair;
         const int nwc = d.waves;
         const uint8_t *zero = d.w0 + kHeaderZeroOffset;
-        const __amdgpu_buffer_rsrc_t xr = x_rsrc<ROWS>(d);
-        const __amdgpu_buffer_rsrc_t yr = output_rsrc<ROWS>(d);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc(d);
+        const __amdgpu_buffer_rsrc_t yr = output_rsrc(d);
         const float sg[2] = {cur.sg[0], cur.sg[1]};
         // The next call's first NB items, fetched while this call ends.  Wave
         // 0 fetches its own only once it has counted this call done: it writes
@@ -704,7 +695,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         // close every segment that ends before position i
         auto close_before = [&](int i) {
             while (i >= cc.end) {
-                finish_segment<ROWS, AR>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
+                finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
                 cc = cursor_at(d, q, g, cc.k + 1);
             }
         };
@@ -751,7 +742,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             }
         }
         while (cc.k < q.nseg) {
-            finish_segment<ROWS, AR>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
+            finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
         }
         // Pieces of shared strips: wave 0 counts them; where this workgroup's
@@ -863,23 +854,14 @@ hipError_t launch_rows(const SeqArgs &a, int waves, size_t lds, hipStream_t s) {
     return a.ncalls > 1 ? launch_kernel<ROWS, true>(a, waves, lds, s) : launch_kernel<ROWS, false>(a, waves, lds, s);
 }
 
-hipError_t launch_args(int rows, const SeqArgs &a, int waves, size_t lds, hipStream_t s) {
-    switch (rows) {
+hipError_t launch_args(int krows, const SeqArgs &a, int waves, size_t lds, hipStream_t s) {
+    switch (krows) {
         case 1: return launch_rows<1>(a, waves, lds, s);
         case 2: return launch_rows<2>(a, waves, lds, s);
-        case 3: return launch_rows<3>(a, waves, lds, s);
         case 4: return launch_rows<4>(a, waves, lds, s);
-        case 5: return launch_rows<5>(a, waves, lds, s);
         case 6: return launch_rows<6>(a, waves, lds, s);
-        case 7: return launch_rows<7>(a, waves, lds, s);
         case 8: return launch_rows<8>(a, waves, lds, s);
-        case 9: return launch_rows<9>(a, waves, lds, s);
-        case 10: return launch_rows<10>(a, waves, lds, s);
-        case 11: return launch_rows<11>(a, waves, lds, s);
         case 12: return launch_rows<12>(a, waves, lds, s);
-        case 13: return launch_rows<13>(a, waves, lds, s);
-        case 14: return launch_rows<14>(a, waves, lds, s);
-        case 15: return launch_rows<15>(a, waves, lds, s);
         case 16: return launch_rows<16>(a, waves, lds, s);
         default: return hipErrorInvalidValue;
     }
@@ -914,6 +896,7 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
     pl.n = n;
     pl.k = k;
     pl.rows = rows;
+    pl.krows = kernel_rows(rows);
     pl.nmat = dual ? 2 : 1;
     const int S = (int)num_strips(n), T = (int)num_supers(k);
     pl.strips = S;
@@ -955,16 +938,17 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
             if (np > pl.max_pieces) pl.max_pieces = np;
         }
     }
-    if (pl.max_pieces > 1) pl.partial_bytes = (size_t)pl.R * pl.max_pieces * pl.nmat * rows * kStripN * sizeof(float);
-    pl.lds_bytes = stream_lds_bytes(rows, pl.waves);
+    if (pl.max_pieces > 1)
+        pl.partial_bytes = (size_t)pl.R * pl.max_pieces * pl.nmat * pl.krows * kStripN * sizeof(float);
+    pl.lds_bytes = stream_lds_bytes(pl.krows, pl.waves);
     return pl;
 }
 
-size_t stream_lds_bytes(int rows, int waves) {
-    const size_t lds_x = (size_t)waves * x_stage_bytes(rows);
+size_t stream_lds_bytes(int krows, int waves) {
+    const size_t lds_x = (size_t)waves * x_stage_bytes(krows);
     // the wave-reduction slots; they also hold the final sums of up to two
     // shared strips (4 x rows x 64 floats), hence at least two waves' worth
-    const size_t lds_red = (size_t)(waves < 2 ? 2 : waves) * 2 * red_rows(rows) * kStripN * sizeof(float);
+    const size_t lds_red = (size_t)(waves < 2 ? 2 : waves) * 2 * red_rows(krows) * kStripN * sizeof(float);
     // at least ~81 KB so that no CU ever holds two of these workgroups
     return lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;
 }
@@ -984,7 +968,7 @@ namespace {
 int launch_end(const StreamCall *calls, int ncalls, int i0, bool shared) {
     if (!shared) return i0 + 1;
     int run = i0 + 1;
-    while (run < ncalls && calls[run].plan.rows == calls[i0].plan.rows) ++run;
+    while (run < ncalls && calls[run].plan.krows == calls[i0].plan.krows) ++run;
     const int left = run - i0, parts = (left + kSeqMax - 1) / kSeqMax;
     return i0 + (left + parts - 1) / parts;
 }
@@ -1002,7 +986,7 @@ hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace,
     const bool shared = ncalls > 1 && cooperative_ok();
     for (int i0 = 0; i0 < ncalls;) {
         const int i1 = launch_end(calls, ncalls, i0, shared);
-        const int rows = calls[i0].plan.rows;
+        const int krows = calls[i0].plan.krows;
         SeqArgs a{};
         a.ncalls = i1 - i0;
         a.counters = reinterpret_cast<unsigned *>(ws);
@@ -1027,16 +1011,17 @@ hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace,
             d.max_pieces = pl.max_pieces;
             d.waves = pl.waves;
             d.flags = (pl.nmat == 2 ? kPair : 0) | (sc.out_f32 ? kOutF32 : 0);
+            d.rows = pl.rows;
             if (i > i0) {
                 const StreamCall &p = calls[i - 1];
                 const size_t ybytes = (size_t)p.plan.rows * p.plan.n * (p.out_f32 ? 4 : 2);
-                if (ranges_overlap(sc.x, (size_t)rows * pl.k * 2, p.y, ybytes)) d.flags |= kReloadX;
+                if (ranges_overlap(sc.x, (size_t)pl.rows * pl.k * 2, p.y, ybytes)) d.flags |= kReloadX;
             }
             if (pl.G > G) G = pl.G;
             if (pl.waves > waves) waves = pl.waves;
         }
         a.G = G;
-        hipError_t e = launch_args(rows, a, waves, stream_lds_bytes(rows, waves), stream);
+        hipError_t e = launch_args(krows, a, waves, stream_lds_bytes(krows, waves), stream);
         if (e != hipSuccess) return e;
         i0 = i1;
     }

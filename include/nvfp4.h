@@ -61,7 +61,7 @@ extern "C" {
 
 #define NVFP4_ABI_VERSION 1
 #define NVFP4_LAYOUT_MAGIC 0x34465056u /* "VPF4" */
-#define NVFP4_LAYOUT_VERSION 2u
+#define NVFP4_LAYOUT_VERSION 3u
 #define NVFP4_MAX_ROWS 128
 
 enum {

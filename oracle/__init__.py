@@ -64,11 +64,14 @@ def _load():
     lib.nvo_dequant.restype = None
     lib.nvo_gemv.argtypes = [c_u8p, c_u8p, ctypes.c_float, i64, i64, c_u16p, ctypes.c_int,
                              c_i64p, i64, c_f64p, c_f64p, c_u16p]
-    lib.nvo_gemv.restype = None
+    lib.nvo_gemv.restype = ctypes.c_int
+    lib.nvo_gemv_f32seq.argtypes = [c_u8p, c_u8p, ctypes.c_float, i64, i64, c_u16p, ctypes.c_int,
+                                    c_i64p, i64, c_f32p, c_u16p]
+    lib.nvo_gemv_f32seq.restype = ctypes.c_int
     lib.nvo_gemv_dual_silu.argtypes = [c_u8p, c_u8p, ctypes.c_float, c_u8p, c_u8p, ctypes.c_float,
                                        i64, i64, c_u16p, ctypes.c_int, c_i64p, i64,
                                        c_f64p, c_f64p, c_f64p, c_f64p, c_f64p, c_u16p]
-    lib.nvo_gemv_dual_silu.restype = None
+    lib.nvo_gemv_dual_silu.restype = ctypes.c_int
     lib.nvo_dense_gemv.argtypes = [c_u16p, i64, i64, c_u16p, ctypes.c_int, c_i64p, i64, c_f64p, c_f64p, c_u16p]
     lib.nvo_dense_gemv.restype = None
     lib.nvo_residual_rmsnorm.argtypes = [c_u16p, c_u16p, c_u16p, i64, ctypes.c_int, ctypes.c_double, ctypes.c_int,
@@ -188,10 +191,35 @@ def gemv(codes, scales, s_g, x_bf16, sel=None):
     y = np.zeros((rows, nsel), np.float64)
     a = np.zeros((rows, nsel), np.float64)
     yb = np.zeros((rows, nsel), np.uint16)
-    _load().nvo_gemv(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), float(s_g), n, k,
-                     _ptr(x, ctypes.c_uint16), rows, _ptr(sel, ctypes.c_int64), nsel,
-                     _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double), _ptr(yb, ctypes.c_uint16))
+    st = _load().nvo_gemv(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), float(s_g), n, k,
+                          _ptr(x, ctypes.c_uint16), rows, _ptr(sel, ctypes.c_int64), nsel,
+                          _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double), _ptr(yb, ctypes.c_uint16))
+    if st:
+        raise ValueError("nvo_gemv refused the arguments")
     return y, a, yb
+
+
+def gemv_f32seq(codes, scales, s_g, x_bf16, sel=None):
+    """Projection as the plain fp32 definition: D = dequant in fp32, then
+    y32 = sum_k D*x with one fp32 rounding per multiply and per add, ascending
+    k from +0.0.  Returns (y32 float32 [rows, nsel], y_bf16 uint16 [rows, nsel])."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    x = _c(x_bf16, np.uint16)
+    n = codes.shape[0]
+    k = codes.shape[1] * 2
+    rows = x.shape[0]
+    if x.shape[1] != k or not 1 <= rows <= 64:
+        raise ValueError("x must be [rows<=64, k]")
+    sel, nsel = _sel(sel, n)
+    y = np.zeros((rows, nsel), np.float32)
+    yb = np.zeros((rows, nsel), np.uint16)
+    st = _load().nvo_gemv_f32seq(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), float(s_g), n, k,
+                                 _ptr(x, ctypes.c_uint16), rows, _ptr(sel, ctypes.c_int64), nsel,
+                                 _ptr(y, ctypes.c_float), _ptr(yb, ctypes.c_uint16))
+    if st:
+        raise ValueError("nvo_gemv_f32seq refused the arguments")
+    return y, yb
 
 
 def gemv_dual_silu(gate, up, x_bf16, sel=None):
@@ -211,12 +239,14 @@ def gemv_dual_silu(gate, up, x_bf16, sel=None):
     out = {name: np.zeros((rows, nsel), np.float64) for name in ("o", "g", "u", "abs_g", "abs_u")}
     ob = np.zeros((rows, nsel), np.uint16)
     f64 = ctypes.c_double
-    _load().nvo_gemv_dual_silu(_ptr(gc, ctypes.c_uint8), _ptr(gs, ctypes.c_uint8), gg,
+    st = _load().nvo_gemv_dual_silu(_ptr(gc, ctypes.c_uint8), _ptr(gs, ctypes.c_uint8), gg,
                                _ptr(uc, ctypes.c_uint8), _ptr(us, ctypes.c_uint8), ug,
                                n, k, _ptr(x, ctypes.c_uint16), rows, _ptr(sel, ctypes.c_int64), nsel,
                                _ptr(out["o"], f64), _ptr(out["g"], f64), _ptr(out["u"], f64),
                                _ptr(out["abs_g"], f64), _ptr(out["abs_u"], f64),
                                _ptr(ob, ctypes.c_uint16))
+    if st:
+        raise ValueError("nvo_gemv_dual_silu refused the arguments")
     out["o_bf16"] = ob
     return out
 

@@ -4,15 +4,18 @@ Projection (per output, fp32 before bf16 rounding):
     |y_dev - y_oracle| <= tol * sum_k |D[n,k] * x[r,k]|,   tol = 1e-3,
 with y_oracle the fp64 sum.  bf16 outputs: the device's bf16 must be the
 round-to-nearest-even of its own fp32 result (bit exact), and within one bf16
-ulp of the oracle's bf16 wherever the two fp32 results are closer than one bf16
-ulp (where they are not -- outputs that cancel to near zero -- two correct fp32
-summation orders may legitimately straddle several bf16 steps, and only the
-fp32 bound applies; those outputs are counted and reported).
+ulp (distance of the ordered bit patterns) of the oracle's bf16 for every
+output whose oracle value is not near cancellation:
+    |y_oracle| >= 2^-12 * sum_k |D[n,k] * x[r,k]|.
+Below that band two correct fp32 summation orders may straddle several bf16
+steps, so only the fp32 bound applies there; those outputs are counted
+("bf16_exempt") and printed with every check.
 
 Gate/up pair o = silu(g) * u: first-order propagation of the per-projection
 bound (|silu'| <= 1.1), plus 2^-20 |o| for the fp32 evaluation of silu:
     |o_dev - o| <= 1.1 tg (|u| + tu) + |silu(g)| tu + 2^-20 |o|,
-    tg = tol * sum|D_g x|,  tu = tol * sum|D_u x|.
+    tg = tol * sum|D_g x|,  tu = tol * sum|D_u x|;
+bf16 within one ulp wherever |o| >= 2^-12 (1.1 sum|D_g x| |u| + |silu(g)| sum|D_u x|).
 """
 from __future__ import annotations
 
@@ -39,22 +42,31 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, (e - 7).astype(np.int64))
 
 
-def _bf16_checks(out32, out16, ref, ref16, err, label):
+BAND = 2.0 ** -12
+
+
+def _bf16_checks(out32, out16, ref, ref16, band, label):
+    """band: fp64 per output; bf16 <= 1 ulp is enforced where |ref| >= band."""
     stats = {}
     if out16 is None:
         return stats
     own = bf16_bits_of(out32)
     nbad_own = int(np.sum(own != out16))
     assert nbad_own == 0, "%s: %d bf16 outputs differ from RNE of the same fp32 result" % (label, nbad_own)
-    u = bf16_ulp(np.minimum(np.abs(ref), np.abs(out32.astype(np.float64))))
-    enforce = err < u
+    enforce = np.abs(ref) >= band
     dist = np.abs(_ordered(out16) - _ordered(ref16))
     nbad = int(np.sum(dist[enforce] > 1))
-    assert nbad == 0, "%s: %d bf16 outputs more than 1 ulp from the oracle (max %d)" % (
+    assert nbad == 0, "%s: %d bf16 outputs more than 1 ulp from the oracle (max %d ulp) outside the cancellation band" % (
         label, nbad, int(dist[enforce].max()))
     stats["bf16_max_ulp"] = int(dist[enforce].max()) if enforce.any() else 0
-    stats["bf16_cancellation_outputs"] = int(np.sum(~enforce))
+    stats["bf16_exempt"] = int(np.sum(~enforce))
+    stats["bf16_exempt_max_ulp"] = int(dist[~enforce].max()) if (~enforce).any() else 0
     return stats
+
+
+def _report(label, stats):
+    print("%s: %s" % (label, ", ".join("%s=%s" % (k, ("%.3g" % v) if isinstance(v, float) else v)
+                                       for k, v in stats.items())))
 
 
 def check_gemv(out32, out16, ref, absdot, ref16, tol=TOL, label="gemv"):
@@ -66,7 +78,8 @@ def check_gemv(out32, out16, ref, absdot, ref16, tol=TOL, label="gemv"):
     rel = err / np.where(absdot > 0, absdot, 1.0)
     assert nbad == 0, "%s: %d outputs exceed %g*sum|w*x| (max ratio %g)" % (label, nbad, tol, rel.max())
     stats = {"max_err_over_absdot": float(rel.max()), "n": int(out32.size)}
-    stats.update(_bf16_checks(out32, out16, ref, ref16, err, label))
+    stats.update(_bf16_checks(out32, out16, ref, ref16, BAND * absdot, label))
+    _report(label, stats)
     return stats
 
 
@@ -84,5 +97,9 @@ def check_dual(out32, out16, d: dict, tol=TOL, label="dual"):
     nbad = int(np.sum(~(err <= bound)))
     assert nbad == 0, "%s: %d outputs exceed the propagated bound" % (label, nbad)
     stats = {"max_err_over_bound": float(np.max(err / np.where(bound > 0, bound, 1.0))), "n": int(out32.size)}
-    stats.update(_bf16_checks(out32, out16, d["o"], d["o_bf16"], err, label))
+    g = d["g"]
+    silu = g / (1.0 + np.exp(-g))
+    band = BAND * (1.1 * d["abs_g"] * np.abs(d["u"]) + np.abs(silu) * d["abs_u"])
+    stats.update(_bf16_checks(out32, out16, d["o"], d["o_bf16"], band, label))
+    _report(label, stats)
     return stats

@@ -214,16 +214,17 @@ static void gemv_row(const uint8_t *codes, const uint8_t *scales, float s_g,
     }
 }
 
-void nvo_gemv(const uint8_t *codes, const uint8_t *scales, float global_scale,
-              int64_t n, int64_t k, const uint16_t *x, int rows,
-              const int64_t *sel, int64_t nsel,
-              double *y, double *absdot, uint16_t *y_bf16)
+int nvo_gemv(const uint8_t *codes, const uint8_t *scales, float global_scale,
+             int64_t n, int64_t k, const uint16_t *x, int rows,
+             const int64_t *sel, int64_t nsel,
+             double *y, double *absdot, uint16_t *y_bf16)
 {
+    if (rows < 1 || rows > NVO_MAX_ROWS || n < 1 || k < 16 || k % 16) return -1;
     if (!sel) nsel = n;
 #pragma omp parallel
     {
         float *drow = (float *)malloc(sizeof(float) * (size_t)k);
-        double yv[64], av[64];
+        double yv[NVO_MAX_ROWS], av[NVO_MAX_ROWS];
 #pragma omp for schedule(static)
         for (int64_t j = 0; j < nsel; ++j) {
             int64_t feat = sel ? sel[j] : j;
@@ -236,22 +237,56 @@ void nvo_gemv(const uint8_t *codes, const uint8_t *scales, float global_scale,
         }
         free(drow);
     }
+    return 0;
 }
 
-/* ---- gate/up pair: o = silu(g) * u = g / (1 + exp(-g)) * u, fp64 ---- */
-
-void nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g_global,
-                        const uint8_t *u_codes, const uint8_t *u_scales, float u_global,
-                        int64_t n, int64_t k, const uint16_t *x, int rows,
-                        const int64_t *sel, int64_t nsel,
-                        double *o, double *g, double *u, double *abs_g, double *abs_u,
-                        uint16_t *o_bf16)
+/* ---- projection as the plain fp32 definition: dequantize, then
+ * y32 = sum_k D[n][k] * x[r][k] with one fp32 rounding per multiply and per
+ * add, starting from +0.0f, ascending k; y16 = bf16 RNE of y32 ---- */
+int nvo_gemv_f32seq(const uint8_t *codes, const uint8_t *scales, float global_scale,
+                    int64_t n, int64_t k, const uint16_t *x, int rows,
+                    const int64_t *sel, int64_t nsel, float *y32, uint16_t *y_bf16)
 {
+    if (rows < 1 || rows > NVO_MAX_ROWS || n < 1 || k < 16 || k % 16) return -1;
     if (!sel) nsel = n;
 #pragma omp parallel
     {
         float *drow = (float *)malloc(sizeof(float) * (size_t)k);
-        double gv[64], ga[64], uv[64], ua[64];
+#pragma omp for schedule(static)
+        for (int64_t j = 0; j < nsel; ++j) {
+            int64_t feat = sel ? sel[j] : j;
+            for (int64_t c = 0; c < k; ++c)
+                drow[c] = dequant_one(codes, scales, global_scale, k, feat, c);
+            for (int r = 0; r < rows; ++r) {
+                float acc = 0.0f;
+                for (int64_t c = 0; c < k; ++c) {
+                    float p = drow[c] * (float)nvo_bf16_value(x[r * k + c]);
+                    acc = acc + p;
+                }
+                if (y32) y32[r * nsel + j] = acc;
+                if (y_bf16) y_bf16[r * nsel + j] = nvo_bf16_from_double((double)acc);
+            }
+        }
+        free(drow);
+    }
+    return 0;
+}
+
+/* ---- gate/up pair: o = silu(g) * u = g / (1 + exp(-g)) * u, fp64 ---- */
+
+int nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g_global,
+                       const uint8_t *u_codes, const uint8_t *u_scales, float u_global,
+                       int64_t n, int64_t k, const uint16_t *x, int rows,
+                       const int64_t *sel, int64_t nsel,
+                       double *o, double *g, double *u, double *abs_g, double *abs_u,
+                       uint16_t *o_bf16)
+{
+    if (rows < 1 || rows > NVO_MAX_ROWS || n < 1 || k < 16 || k % 16) return -1;
+    if (!sel) nsel = n;
+#pragma omp parallel
+    {
+        float *drow = (float *)malloc(sizeof(float) * (size_t)k);
+        double gv[NVO_MAX_ROWS], ga[NVO_MAX_ROWS], uv[NVO_MAX_ROWS], ua[NVO_MAX_ROWS];
 #pragma omp for schedule(static)
         for (int64_t j = 0; j < nsel; ++j) {
             int64_t feat = sel ? sel[j] : j;
@@ -270,6 +305,7 @@ void nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g
         }
         free(drow);
     }
+    return 0;
 }
 
 int nvo_num_threads(void)

@@ -14,6 +14,8 @@
  *   - the projection y[r][n] = sum_k D[n][k] * x[r][k] in fp64 (an FP64
  *     reference per projection class, as the TensorFold issue #603 thread asks
  *     for), with sum_k |D*x| for tolerances and a bf16 round-to-nearest-even copy;
+ *   - the same projection as the plain fp32 definition (dequantize, then a
+ *     sequential fp32 dot product in ascending k);
  *   - the gate/up pair o = silu(g) * u in fp64 (the SwiGLU FFN of the
  *     Qwen3.8-27B-NVFP4 blueprint page, "w4a16_gemv_dual" kernels).
  *
@@ -52,11 +54,20 @@ int  nvo_quantize(const float *W, int64_t n, int64_t k, uint8_t *codes,
                   uint8_t *scales, float *global_scale);
 void nvo_dequant(const uint8_t *codes, const uint8_t *scales, float global_scale,
                  int64_t n, int64_t k, float *D);
-void nvo_gemv(const uint8_t *codes, const uint8_t *scales, float global_scale,
+/* Projections take 1..NVO_MAX_ROWS activation rows and return 0, or -1 (and
+ * compute nothing) for rows outside that range or a bad shape. */
+#define NVO_MAX_ROWS 64
+int  nvo_gemv(const uint8_t *codes, const uint8_t *scales, float global_scale,
               int64_t n, int64_t k, const uint16_t *x, int rows,
               const int64_t *sel, int64_t nsel,
               double *y, double *absdot, uint16_t *y_bf16);
-void nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g_global,
+/* The same projection as the plain fp32 definition: D in fp32, then
+ * sum_k D*x with one fp32 rounding per multiply and add, ascending k from
+ * +0.0f; y32 fp32 and its bf16 RNE copy, [rows][nsel]. */
+int  nvo_gemv_f32seq(const uint8_t *codes, const uint8_t *scales, float global_scale,
+                     int64_t n, int64_t k, const uint16_t *x, int rows,
+                     const int64_t *sel, int64_t nsel, float *y32, uint16_t *y_bf16);
+int  nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g_global,
                         const uint8_t *u_codes, const uint8_t *u_scales, float u_global,
                         int64_t n, int64_t k, const uint16_t *x, int rows,
                         const int64_t *sel, int64_t nsel,

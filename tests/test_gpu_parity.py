@@ -19,7 +19,7 @@ import oracle
 import workloads
 from oracle import check
 
-ALL_ROWS = range(1, 17)   # every activation row count the library takes
+ALL_ROWS = range(1, 17)   # every row count one kernel call takes
 
 pytestmark = pytest.mark.gpu
 
@@ -73,15 +73,17 @@ def _run_dual(nv, gw, uw, xb):
 # ---- layout -----------------------------------------------------------------
 
 def _layout_numpy(codes, scales, sg, n, k):
-    """The packed layout (version 2), written out from its definition: per
-    super-tile, code entry 32 c + 16 h + j (chunk c = 4 kb + fb) = canonical
-    code bytes of feature 16 fb + j for k = 64 kb + 32 h .. + 31; scale entry
-    16 g + j, byte 4 kb + fb = scale of feature 16 fb + j, group 4 kb + g."""
+    """The packed layout (version 3), written out from its definition: per
+    super-tile, 8 code chunks then one scale chunk of 64 16-byte entries each
+    (entry l of a chunk: lane l = 16 q + j).  Code chunk c, entry l, dword d:
+    canonical code bytes of feature 16 (c // 2) + j for k = 32 (4 (c % 2) + d)
+    + 8 q .. + 7; scale entry l, byte 8 b + t: scale of feature
+    16 (2 (q // 2) + b) + j, group 2 t + (q % 2)."""
     S, T = -(-n // 64), -(-k // 256)
     out = np.zeros(256 + S * T * 9216, np.uint8)
     out[0:4] = np.frombuffer(np.float32(sg).tobytes(), np.uint8)
     out[4:8] = np.frombuffer(np.uint32(0x34465056).tobytes(), np.uint8)
-    out[8:12] = np.frombuffer(np.uint32(2).tobytes(), np.uint8)
+    out[8:12] = np.frombuffer(np.uint32(3).tobytes(), np.uint8)
     out[16:24] = np.frombuffer(np.int64(n).tobytes(), np.uint8)
     out[24:32] = np.frombuffer(np.int64(k).tobytes(), np.uint8)
     cpad = np.zeros((S * 64, T * 128), np.uint8)
@@ -91,18 +93,21 @@ def _layout_numpy(codes, scales, sg, n, k):
     for s in range(S):
         for u in range(T):
             base = 256 + (s * T + u) * 9216
-            for kb in range(4):
-                for fb in range(4):
-                    for h in range(2):
-                        for j in range(16):
-                            e = 32 * (4 * kb + fb) + 16 * h + j
-                            f, c0 = 64 * s + 16 * fb + j, 128 * u + 32 * kb + 16 * h
-                            out[base + 16 * e: base + 16 * e + 16] = cpad[f, c0: c0 + 16]
-                for g in range(4):
+            for c in range(8):
+                for q in range(4):
                     for j in range(16):
-                        e = 512 + 16 * g + j
-                        for fb in range(4):
-                            out[base + 16 * e + 4 * kb + fb] = spad[64 * s + 16 * fb + j, 16 * u + 4 * kb + g]
+                        e = base + 1024 * c + 16 * (16 * q + j)
+                        f = 64 * s + 16 * (c // 2) + j
+                        for d in range(4):
+                            kk = 256 * u + 32 * (4 * (c % 2) + d) + 8 * q
+                            out[e + 4 * d: e + 4 * d + 4] = cpad[f, kk // 2: kk // 2 + 4]
+            for q in range(4):
+                for j in range(16):
+                    e = base + 8192 + 16 * (16 * q + j)
+                    for b in range(2):
+                        for t in range(8):
+                            f = 64 * s + 16 * (2 * (q // 2) + b) + j
+                            out[e + 8 * b + t] = spad[f, 16 * u + 2 * t + q % 2]
     return out
 
 
@@ -225,27 +230,24 @@ def test_dual_random_all_rows(nv, n, k):
 
 
 @pytest.mark.parametrize("n,k", [(130, 4112), (300, 4352), (72, 17408)])
-def test_rows_invariant_within_tier(nv, n, k):
-    """A row's result does not depend on how many rows share the call, within
-    one arithmetic tier: rows 5-16 (fp16 products) and rows 2-4 (block-scaled
-    products) give every row bit-identical fp32 and bf16 outputs whatever the
-    call's row count (the plan, the per-row activation scales, the product
-    rows and every summation order are independent of the row count).  Single
+def test_rows_invariant_1_to_16(nv, n, k):
+    """A row's result does not depend on how many rows share the call: every
+    row count 1..16 gives every row bit-identical fp32 and bf16 outputs (one
+    arithmetic for every row count; the plan, the product positions of a row
+    and every summation order are independent of the row count).  Single
     projection and gate/up pair; shapes with and without split-K pieces."""
     c = workloads.case(n, k, 16, seed=n + 7 * k, dual=True)
     gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
     gw, uw = _pack(nv, gq), _pack(nv, uq)
-    for tier in ((5, 16), (2, 4)):
-        lo, hi = tier
-        y_ref, y16_ref = _run_gemv(nv, gw, c["x"][:hi])
-        o_ref, o16_ref = _run_dual(nv, gw, uw, c["x"][:hi])
-        for rows in range(lo, hi):
-            y, y16 = _run_gemv(nv, gw, c["x"][:rows])
-            o, o16 = _run_dual(nv, gw, uw, c["x"][:rows])
-            assert np.array_equal(y.view(np.uint32), y_ref[:rows].view(np.uint32)), (n, k, rows)
-            assert np.array_equal(y16, y16_ref[:rows]), (n, k, rows)
-            assert np.array_equal(o.view(np.uint32), o_ref[:rows].view(np.uint32)), (n, k, rows)
-            assert np.array_equal(o16, o16_ref[:rows]), (n, k, rows)
+    y_ref, y16_ref = _run_gemv(nv, gw, c["x"])
+    o_ref, o16_ref = _run_dual(nv, gw, uw, c["x"])
+    for rows in range(1, 16):
+        y, y16 = _run_gemv(nv, gw, c["x"][:rows])
+        o, o16 = _run_dual(nv, gw, uw, c["x"][:rows])
+        assert np.array_equal(y.view(np.uint32), y_ref[:rows].view(np.uint32)), (n, k, rows)
+        assert np.array_equal(y16, y16_ref[:rows]), (n, k, rows)
+        assert np.array_equal(o.view(np.uint32), o_ref[:rows].view(np.uint32)), (n, k, rows)
+        assert np.array_equal(o16, o16_ref[:rows]), (n, k, rows)
 
 
 # ---- more than 16 rows: row chunks ----------------------------------------------
@@ -285,15 +287,16 @@ def test_dual_random_many_rows(nv):
 
 
 @pytest.mark.parametrize("n,k", [(130, 4112), (72, 17408)])
-def test_rows_invariant_across_chunks(nv, n, k):
-    """From 5 rows on every row chunk runs on the fp16 products, so a row's
-    result is the same bits in a call of any row count 5..128."""
+def test_rows_invariant_1_to_128(nv, n, k):
+    """Every row count 1..128 (one row chunk up to 16 rows, balanced chunks
+    beyond) gives every row the same bits as the 128-row call, single
+    projection and gate/up pair."""
     c = workloads.case(n, k, 128, seed=n + 11 * k, dual=True)
     gq, uq = oracle.quantize(c["W"]), oracle.quantize(c["W_up"])
     gw, uw = _pack(nv, gq), _pack(nv, uq)
     y_ref, y16_ref = _run_gemv(nv, gw, c["x"])
     o_ref, o16_ref = _run_dual(nv, gw, uw, c["x"])
-    for rows in (5, 16, 17, 37, 64, 100):
+    for rows in range(1, 128):
         y, y16 = _run_gemv(nv, gw, c["x"][:rows])
         o, o16 = _run_dual(nv, gw, uw, c["x"][:rows])
         assert np.array_equal(y.view(np.uint32), y_ref[:rows].view(np.uint32)), (n, k, rows)
@@ -339,19 +342,54 @@ def _wide_x(rng, rows, k, binades):
 
 
 @pytest.mark.parametrize("n,k", [(200, 784), (130, 4112)])
-def test_gemv_wide_range_activations_all_rows(nv, n, k):
-    """Activations spread over 2^-16 .. 2^16 inside every group: the fp8 split
-    is exact only within 13 binades of a group's largest and the fp16 staging
-    within 31 of a row's largest in a super-tile; R14/R15 still hold."""
-    rng = np.random.default_rng(31 * n + k)
+@pytest.mark.parametrize("binades", [16, 60])
+def test_gemv_wide_range_activations_all_rows(nv, n, k, binades):
+    """Activations sign * 2^u, u uniform in [-binades, binades], inside every
+    group: the activations enter the products as stored, so R14/R15 hold at
+    any spread (60 binades: products from about 2^-70 to 2^63, all inside the
+    fp32 range)."""
+    rng = np.random.default_rng(31 * n + k + binades)
     for rows in ALL_ROWS:
         c = workloads.case(n, k, rows, seed=300 * rows + n, outlier_frac=0.01)
         q = oracle.quantize(c["W"])
-        xb = _wide_x(rng, rows, k, 16)
+        xb = _wide_x(rng, rows, k, binades)
         y32, y16 = _run_gemv(nv, _pack(nv, q), xb)
         ref, absd, ref16 = oracle.gemv(*q, xb)
-        st = check.check_gemv(y32, y16, ref, absd, ref16, label="wide gemv %dx%d rows=%d" % (n, k, rows))
-        print("wide gemv %dx%d rows=%d: max err / sum|w*x| = %.3g" % (n, k, rows, st["max_err_over_absdot"]))
+        check.check_gemv(y32, y16, ref, absd, ref16, label="wide(%d) gemv %dx%d rows=%d" % (binades, n, k, rows))
+
+
+def _big_on_zero_code_case(k, rows, g0):
+    """One group g0 of every row: x = 2^16 on a weight whose code is 0, and
+    2^-8 on 15 weights of code +-1 (scale 1, s_g 1); every other k has x = 0.
+    The exact result is 15 * 2^-8 * (+-1 sums), which a path that scales each
+    group's activations by its largest loses entirely."""
+    n = 64
+    codes = np.zeros((n, k // 2), np.uint8)
+    scales = np.zeros((n, k // 16), np.uint8)
+    rng = np.random.default_rng(k + rows + g0)
+    signs = rng.integers(0, 2, (n, 15))
+    nib = np.concatenate([np.zeros((n, 1), np.uint8), np.where(signs == 1, 0xA, 0x2).astype(np.uint8)], axis=1)
+    codes[:, 8 * g0: 8 * g0 + 8] = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    scales[:, g0] = 0x38                                # E4M3 1.0
+    xv = np.zeros((rows, k), np.float32)
+    xv[:, 16 * g0] = 2.0 ** 16
+    xv[:, 16 * g0 + 1: 16 * g0 + 16] = 2.0 ** -8
+    return codes, scales, np.float32(1.0), workloads.bf16_bits(xv)
+
+
+@pytest.mark.parametrize("k,g0", [(16, 0), (5120, 0), (5120, 137), (5120, 319)])
+def test_gemv_large_activation_on_zero_code(nv, k, g0):
+    """The wide-range case that an activation split per group loses: checked
+    exactly (every partial sum is a multiple of 2^-8 below 2^17) at every row
+    count, as a lone group and inside k = 5120."""
+    for rows in ALL_ROWS:
+        codes, scales, sg, xb = _big_on_zero_code_case(k, rows, g0)
+        w = nv.nvfp4_pack(_dev(codes), _dev(scales), float(sg))
+        y32, y16 = _run_gemv(nv, w, xb)
+        ref, absd, ref16 = oracle.gemv(codes, scales, sg, xb)
+        assert np.any(ref != 0)
+        assert np.array_equal(y32.astype(np.float64), ref), (k, g0, rows)
+        assert np.array_equal(y16, ref16), (k, g0, rows)
 
 
 def test_gemv_zero_inputs(nv):
