@@ -84,10 +84,25 @@ __device__ __forceinline__ void stage_g(const uint4 (&xv)[XStageG<ROWS>::XR], ui
 // ws is the lane's scale entry: byte 8 b + ks is the scale of feature
 // 16 (2 (q >> 1) + b) + n, group 2 ks + (q & 1) of the super-tile; lanes q and
 // q ^ 2 need the same 32 scale bytes and hold half of them each.
+// The 16 codes of product (fb, ks) as a bf16 B operand.
+__device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w) {
+    const bf16x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    const bf16x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    const bf16x2_t b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    const bf16x2_t b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+    return bf16x8_t{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
+
+// Software pipeline over the 8 k steps of a super-tile: while the products
+// of step ks run on the matrix core, the vector unit converts the codes of
+// step ks + 1 and scales the results of step ks - 1 into the accumulators
+// (a product's result is read 2 steps of conversions after it was issued,
+// so neither unit waits for the other).
 template <int ROWS>
 __device__ __forceinline__ void core_g(const uint4 (&wc)[kCodeChunks], const uint4 &ws, const uint8_t *xs, int lane,
                                        float (&acc)[4][XStageG<ROWS>::RS][XStageG<ROWS>::NV]) {
     using S = XStageG<ROWS>;
+    constexpr int RS = S::RS, NV = S::NV;
     const int q = lane >> 4, i = lane & 15;
     // the scale bytes of feature blocks 0, 1 (sl[0]) and 2, 3 (sl[1])
     uint32_t sl[2][4];
@@ -99,48 +114,63 @@ __device__ __forceinline__ void core_g(const uint4 (&wc)[kCodeChunks], const uin
     }
     // this lane's A slot: group half and row of the row set
     const int sh = (i >> 2) & 1, sr = 2 * (i & 3) + (i >> 3);
-    int abase[S::RS], astep[S::RS];
+    int abase[RS], astep[RS];
 #pragma unroll
-    for (int rs = 0; rs < S::RS; ++rs) {
+    for (int rs = 0; rs < RS; ++rs) {
         const bool live = sh == (q >> 1) && 8 * rs + sr < ROWS;
         abase[rs] = live ? (8 * rs + sr) * S::ROW_BYTES + 16 * q : S::ZERO_OFF;
         astep[rs] = live ? 64 : 0;
     }
-#pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {   // k steps 2 kp, 2 kp + 1
-        // E4M3 scales of the two k steps, per feature block
-        float sc[2][4];
-#pragma unroll
-        for (int fb = 0; fb < 4; ++fb) {
-            const uint32_t w = sl[fb >> 1][2 * (fb & 1) + (kp >> 1)];
-            const f32x2_t s = (kp & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true)
-                                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
-            sc[0][fb] = s.x;
-            sc[1][fb] = s.y;
+    // E4M3 scale of feature block fb at k step ks
+    auto scale = [&](int fb, int ks) {
+        const uint32_t w = sl[fb >> 1][2 * (fb & 1) + (ks >> 2)];
+        switch (ks & 3) {
+            case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+            case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+            case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+            default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
         }
+    };
+    bf16x8_t B[4], Bn[4];
+    f32x4_t D[4][RS], Dp[4][RS];
+    float sp[4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int ks = 2 * kp + t;
-            bf16x8_t A[S::RS];
+    for (int fb = 0; fb < 4; ++fb) Bn[fb] = codes_bf16(word_of(wc[2 * fb], 0));
 #pragma unroll
-            for (int rs = 0; rs < S::RS; ++rs)
+    for (int ks = 0; ks <= 8; ++ks) {
+        if (ks < 8) {
+            bf16x8_t A[RS];
+#pragma unroll
+            for (int rs = 0; rs < RS; ++rs)
                 A[rs] = *reinterpret_cast<const bf16x8_t *>(xs + abase[rs] + astep[rs] * ks);
 #pragma unroll
-            for (int fb = 0; fb < 4; ++fb) {
-                const uint32_t w = word_of(wc[2 * fb + (ks >> 2)], ks & 3);
-                const bf16x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
-                const bf16x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
-                const bf16x2_t b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
-                const bf16x2_t b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
-                const bf16x8_t B = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+            for (int fb = 0; fb < 4; ++fb) B[fb] = Bn[fb];
 #pragma unroll
-                for (int rs = 0; rs < S::RS; ++rs) {
+            for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+                for (int rs = 0; rs < RS; ++rs) {
                     const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rs], B, zero, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < S::NV; ++v)
-                        acc[fb][rs][v] = __builtin_fmaf(D[v], sc[t][fb], acc[fb][rs][v]);
+                    D[fb][rs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rs], B[fb], zero, 0, 0, 0);
                 }
+            if (ks + 1 < 8) {
+#pragma unroll
+                for (int fb = 0; fb < 4; ++fb) Bn[fb] = codes_bf16(word_of(wc[2 * fb + ((ks + 1) >> 2)], (ks + 1) & 3));
+            }
+        }
+        if (ks > 0) {
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+                for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) acc[fb][rs][v] = __builtin_fmaf(Dp[fb][rs][v], sp[fb], acc[fb][rs][v]);
+        }
+        if (ks < 8) {
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+                sp[fb] = scale(fb, ks);
+#pragma unroll
+                for (int rs = 0; rs < RS; ++rs) Dp[fb][rs] = D[fb][rs];
             }
         }
     }
