@@ -19,14 +19,26 @@ roofline's kernel is its shared launch (bytes and duration per launch).  The
 stand-alone gate/up pair launch (nvfp4_gemv_dual_silu) is timed as well, over
 the 64 layers' pairs launched back to back.
 
-The CPU baseline times the fp64 CPU oracle on layer 0 of the same workload.
+After timing, every row count's workspace wait flag must be clear, and at
+rows 1 and 8 sampled outputs of the timed step's last layer (every call of
+layer 63, 256 features each) are checked against the CPU oracle.
+
+Single projection calls (qkv at 1 row, the gate/up pair at 1 row, down at 8
+rows with 1% outlier groups) are timed one call between two events each,
+rotating over at least 1 GiB of distinct packed weights, and reported as
+median / p10 / p90 beside the streaming-read ceiling for the same bytes.
+
+The CPU baseline times the CPU oracle on layer 0 of the same workload at all
+host threads and at one thread.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -100,7 +112,7 @@ def build_sweep(nv, workloads, torch, dev, layers):
     return mats
 
 
-def make_sequence(nv, torch, dev, workloads, mats, rows):
+def make_sequence(nv, torch, dev, workloads, mats, rows, bufs=None):
     x5120 = workloads.draw_x_device(rows, 5120, 5_000_000 + rows, dev)
     x6144 = workloads.draw_x_device(rows, 6144, 5_000_100 + rows, dev)
     y_qkv = torch.empty((rows, 12288), dtype=torch.bfloat16, device=dev)
@@ -113,6 +125,8 @@ def make_sequence(nv, torch, dev, workloads, mats, rows):
         calls.append((lm["o"], None, x6144, y_o))
         calls.append((lm["gate"], lm["up"], x5120, o_gu))
         calls.append((lm["down"], None, o_gu, y_down))
+    if bufs is not None:
+        bufs.update(x5120=x5120, x6144=x6144, y_qkv=y_qkv, y_o=y_o, o_gu=o_gu, y_down=y_down)
     return nv.Sequence(calls)
 
 
@@ -152,41 +166,237 @@ def time_pair(nv, torch, dev, mats, rows, ws, reps):
     return start.elapsed_time(stop) / reps / len(mats)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(workloads, torch, dev, target_s):
+    """The CPU oracle (fp64 dequantize-then-dot, OpenMP over output features)
+    on layer 0 of the sweep at rows=1: all host threads over the whole layer,
+    and one thread over its qkv projection; GB/s of the same packed bytes."""
     import numpy as np
 
     import oracle
 
     oracle.build(force=False)
     q = {}
-    nbytes = 0
     for pi, (name, n, k) in enumerate(workloads.LAYER_PROJECTIONS):
         W = workloads.draw_weights_device(n, k, workloads.sweep_seed(0, pi), dev).cpu().numpy()
         q[name] = oracle.quantize(W)
-        nbytes += packed_weight_bytes(n, k)
         del W
     rng = np.random.default_rng(0)
     xs = {k: workloads.draw_x(rng, 1, k) for k in (5120, 6144, 17408)}
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
+    layer_bytes = sum(packed_weight_bytes(n, k) for _, n, k in workloads.LAYER_PROJECTIONS)
+    qkv_bytes = packed_weight_bytes(12288, 5120)
+
+    def run(threads, fn, nbytes, budget):
+        oracle.set_num_threads(threads)
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget or el * (passes + 1) / passes > 2.5 * budget:
+                break
+        return nbytes * passes / el / 1e9, passes, el
+
+    def layer():
         oracle.gemv(*q["qkv"], xs[5120])
         oracle.gemv(*q["o"], xs[6144])
         oracle.gemv_dual_silu(q["gate"], q["up"], xs[5120])
         oracle.gemv(*q["down"], xs[17408])
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or el * (passes + 1) / passes > 30.0:
-            break
+
+    all_threads = os.cpu_count() or 1
+    gbs_all, p_all, el_all = run(all_threads, layer, layer_bytes, target_s)
+    gbs_one, p_one, el_one = run(1, lambda: oracle.gemv(*q["qkv"], xs[5120]), qkv_bytes, target_s / 2)
+    oracle.set_num_threads(all_threads)
     return {
-        "value": round(nbytes * passes / el / 1e9, 4),
+        "value": round(gbs_all, 4),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": all_threads,
         "kind": "oracle",
-        "sample": "layer 0 of the decode-step sweep (qkv, o, gate/up pair with SiLU, down), rows=1, "
-                  "fp64 CPU oracle (dequantize then dot), %d pass(es) in %.1f s, %d packed bytes per pass"
-                  % (passes, el, nbytes),
+        "cpu_model": cpu_model(),
+        "sample": "layer 0 of the decode-step sweep (qkv, o, gate/up pair with SiLU, down), rows=1, fp64 CPU "
+                  "oracle (dequantize then dot), %d thread(s), %d pass(es) in %.1f s, %d packed bytes per pass"
+                  % (all_threads, p_all, el_all, layer_bytes),
+        "one_thread": {"value": round(gbs_one, 5), "unit": "GB/s", "cores": 1,
+                       "sample": "qkv projection of layer 0 [12288 x 5120], rows=1, %d pass(es) in %.1f s"
+                                 % (p_one, el_one)},
     }
+
+
+def parity_sample(nv, torch, mats, bufs, rows, nsel=256, seed=7):
+    """Sampled outputs of the last layer of the timed step (every call of
+    layer 63: qkv, o, the gate/up pair, down -- whose activations are the
+    pair's outputs of the same step) against the CPU oracle: the bf16 outputs
+    within 1e-3 * sum|w*x| plus half a bf16 ulp of the oracle's fp64 value, and
+    within one bf16 ulp of its bf16 value wherever |y| >= 2^-12 sum|w*x|."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    lm = mats[-1]
+    rng = np.random.default_rng(seed)
+
+    def host_weight(w):
+        c, s_, g = nv.nvfp4_unpack(w)
+        return c.cpu().numpy(), s_.cpu().numpy(), np.float32(g.item())
+
+    def bits(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    def ordered(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+    def val(b):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    worst = {"max_err_over_absdot": 0.0, "max_bf16_ulp": 0, "outputs": 0, "exempt": 0}
+
+    def compare(out16, ref, absd, ref16):
+        y = val(out16)
+        err = np.abs(y - ref)
+        bound = 1e-3 * absd + np.abs(ref) * 2.0 ** -8
+        if not np.all(err <= bound):
+            raise SystemExit("parity sample failed at rows=%d: max err/bound %.3g" % (rows, (err / bound).max()))
+        enforce = np.abs(ref) >= 2.0 ** -12 * absd
+        dist = np.abs(ordered(out16) - ordered(ref16))
+        if np.any(dist[enforce] > 1):
+            raise SystemExit("parity sample failed at rows=%d: %d bf16 outputs > 1 ulp" % (rows, int(np.sum(dist[enforce] > 1))))
+        worst["max_err_over_absdot"] = max(worst["max_err_over_absdot"],
+                                           float(np.max(err / np.where(absd > 0, absd, 1.0))))
+        worst["max_bf16_ulp"] = max(worst["max_bf16_ulp"], int(dist[enforce].max()) if enforce.any() else 0)
+        worst["outputs"] += int(out16.size)
+        worst["exempt"] += int(np.sum(~enforce))
+
+    x5120, x6144 = bits(bufs["x5120"]), bits(bufs["x6144"])
+    for name, x, yb in (("qkv", x5120, bufs["y_qkv"]), ("o", x6144, bufs["y_o"])):
+        w = host_weight(lm[name])
+        sel = np.sort(rng.choice(lm[name].n, nsel, replace=False))
+        ref, absd, ref16 = oracle.gemv(*w, x, sel=sel)
+        compare(bits(yb)[:, sel], ref, absd, ref16)
+    g, u = host_weight(lm["gate"]), host_weight(lm["up"])
+    sel = np.sort(rng.choice(lm["gate"].n, nsel, replace=False))
+    d = oracle.gemv_dual_silu(g, u, x5120, sel=sel)
+    o16 = bits(bufs["o_gu"])
+    y = val(o16[:, sel])
+    err = np.abs(y - d["o"])
+    from oracle import check
+    bound = check.dual_bound(d) + np.abs(d["o"]) * 2.0 ** -8
+    if not np.all(err <= bound):
+        raise SystemExit("parity sample failed at rows=%d (gate/up pair)" % rows)
+    worst["outputs"] += int(y.size)
+    w = host_weight(lm["down"])
+    sel = np.sort(rng.choice(lm["down"].n, nsel, replace=False))
+    ref, absd, ref16 = oracle.gemv(*w, o16, sel=sel)
+    compare(bits(bufs["y_down"])[:, sel], ref, absd, ref16)
+    worst["max_err_over_absdot"] = float("%.3g" % worst["max_err_over_absdot"])
+    worst["features_per_call"] = nsel
+    worst["layer"] = len(mats) - 1
+    return worst
+
+
+def pctl(vals, p):
+    import numpy as np
+    return float(np.percentile(np.asarray(vals, dtype=np.float64), p))
+
+
+def time_calls(torch, launch, ncalls, warmup=20):
+    """Per-call device time: every call between two events of its own, all
+    enqueued before one synchronization.  Returns the durations in us."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        launch(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncalls)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        launch(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def call_stats(us, nbytes, copies):
+    med = pctl(us, 50)
+    return {"calls": len(us), "copies": copies, "bytes_per_call": nbytes,
+            "bytes_rotated": nbytes * copies,
+            "median_us": round(med, 3), "p10_us": round(pctl(us, 10), 3), "p90_us": round(pctl(us, 90), 3),
+            "GB_per_s_median": round(nbytes / (med * 1e-6) / 1e9, 1),
+            "pct_hbm_peak_median": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+CEILING_BYTES = 1 << 31     # the read-ceiling buffer: 2 GiB, far beyond the 256 MB Infinity Cache
+
+
+def read_ceiling(nv, torch, dev, buf, nbytes, ncalls):
+    """Per-call durations of the streaming-read kernel over nbytes, rotating
+    the start offset through the 2 GiB buffer."""
+    span = (CEILING_BYTES - nbytes) // 4096 * 4096
+    offs = [(i * 1_000_003 * 4096) % max(span, 4096) if span > 0 else 0 for i in range(ncalls + 20)]
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    return time_calls(torch, lambda i: nv.nvfp4_read_ceiling(buf, nbytes, sink, offset=offs[i % len(offs)]),
+                      ncalls)
+
+
+def single_calls(nv, torch, dev, workloads, mats, ceil_buf, ncalls=200):
+    """The single-call configurations, one call between two events each,
+    rotating over >= 1 GiB of distinct packed weights: qkv [12288 x 5120] at
+    1 row (the sweep's 64 qkv weights), the gate/up pair 2 x [17408 x 5120] at
+    1 row (the sweep's 64 pairs), down [5120 x 17408] at 8 rows with 1% of its
+    16-weight groups x50 (22 weights drawn and quantized for this).  Beside
+    each, the read ceiling for the same bytes."""
+    out = {}
+    x1 = workloads.draw_x_device(1, 5120, 6_000_001, dev)
+    y_qkv = torch.empty((1, 12288), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(max(nv.nvfp4_workspace_bytes(12288, 5120, 1), 16), dtype=torch.uint8, device=dev)
+    qkv = [lm["qkv"] for lm in mats]
+    nb = packed_weight_bytes(12288, 5120)
+    us = time_calls(torch, lambda i: nv.nvfp4_gemv(qkv[i % len(qkv)], x1, out=y_qkv, workspace=ws), ncalls)
+    out["qkv_12288x5120_rows1"] = call_stats(us, nb, len(qkv))
+    out["qkv_12288x5120_rows1"]["read_ceiling_median_us"] = round(pctl(read_ceiling(nv, torch, dev, ceil_buf, nb, ncalls), 50), 3)
+
+    o_gu = torch.empty((1, 17408), dtype=torch.bfloat16, device=dev)
+    ws2 = torch.zeros(max(nv.nvfp4_workspace_bytes(17408, 5120, 1, True), 16), dtype=torch.uint8, device=dev)
+    nb2 = 2 * packed_weight_bytes(17408, 5120)
+    us = time_calls(torch, lambda i: nv.nvfp4_gemv_dual_silu(mats[i % len(mats)]["gate"], mats[i % len(mats)]["up"],
+                                                              x1, out=o_gu, workspace=ws2), ncalls)
+    out["gate_up_2x17408x5120_rows1"] = call_stats(us, nb2, len(mats))
+    out["gate_up_2x17408x5120_rows1"]["read_ceiling_median_us"] = round(pctl(read_ceiling(nv, torch, dev, ceil_buf, nb2, ncalls), 50), 3)
+
+    n, k = 5120, 17408
+    ncopies = -(-(1 << 30) // packed_weight_bytes(n, k))
+    qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+    downs = []
+    for c in range(ncopies):
+        g = torch.Generator(device=dev).manual_seed(7_000_000 + c)
+        W = torch.randn((n, k), generator=g, device=dev, dtype=torch.float32).mul_(workloads.WEIGHT_STD)
+        ngroups = n * k // workloads.GROUP
+        idx = torch.randperm(ngroups, generator=g, device=dev)[: round(0.01 * ngroups)]
+        W.view(ngroups, workloads.GROUP)[idx] *= 50.0
+        downs.append(nv.nvfp4_quantize(W, workspace=qws))
+        del W, idx
+    x8 = workloads.draw_x_device(8, k, 6_000_008, dev)
+    y8 = torch.empty((8, n), dtype=torch.bfloat16, device=dev)
+    ws3 = torch.zeros(max(nv.nvfp4_workspace_bytes(n, k, 8), 16), dtype=torch.uint8, device=dev)
+    nb3 = packed_weight_bytes(n, k)
+    us = time_calls(torch, lambda i: nv.nvfp4_gemv(downs[i % ncopies], x8, out=y8, workspace=ws3), ncalls)
+    out["down_5120x17408_rows8_outliers"] = call_stats(us, nb3, ncopies)
+    out["down_5120x17408_rows8_outliers"]["read_ceiling_median_us"] = round(pctl(read_ceiling(nv, torch, dev, ceil_buf, nb3, ncalls), 50), 3)
+    for key, floor in (("qkv_12288x5120_rows1", 5.90), ("gate_up_2x17408x5120_rows1", 16.71),
+                       ("down_5120x17408_rows8_outliers", 8.95)):
+        out[key]["derived_floor_us"] = floor
+        out[key]["pct_of_read_ceiling"] = round(100 * out[key]["read_ceiling_median_us"] / out[key]["median_us"], 1)
+    del downs
+    return out
 
 
 def load_traffic():
@@ -293,75 +503,81 @@ def time_dense(nv, torch, dev, rows_list, reps):
     return out
 
 
+ROTATE_BYTES = 1 << 30   # distinct bytes cycled through by back-to-back timings (>= 4x the 256 MB Infinity Cache)
+
+
+def time_rotating(torch, launch, copies, reps):
+    """Average us per call of `reps` back-to-back calls cycling through
+    `copies` distinct operand sets (launch(i) runs set i % copies)."""
+    stream = torch.cuda.current_stream()
+    for i in range(min(copies, 3)):
+        launch(i)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(reps):
+        launch(i % copies)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e3 / reps
+
+
 def time_mx(nv, torch, dev, rows_list, reps):
     """The MXFP4 projection (nvfp4_mxfp4_gemv) on an lm-head-sized [151936 x
     5120] and a gate-sized [17408 x 5120] matrix: random codes and E8M0 scale
     bytes 118..124 drawn on the device (any bytes are valid MXFP4), back-to-back
-    calls between HIP events; GB/s counts codes + scales once per call."""
+    calls cycling through >= 1 GiB of distinct copies; GB/s counts codes +
+    scales once per call."""
     g = torch.Generator(device=dev).manual_seed(2024)
     out = {}
-    stream = torch.cuda.current_stream()
     for n, k in ((151936, 5120), (17408, 5120)):
-        codes = torch.randint(0, 256, (n, k // 2), generator=g, device=dev, dtype=torch.uint8)
-        scales = torch.randint(118, 125, (n, k // 32), generator=g, device=dev, dtype=torch.uint8)
         wbytes = n * k // 2 + n * k // 32
-        res = {"shape": [n, k], "weight_bytes": wbytes, "by_rows": {}}
+        copies = -(-ROTATE_BYTES // wbytes)
+        cs = [(torch.randint(0, 256, (n, k // 2), generator=g, device=dev, dtype=torch.uint8),
+               torch.randint(118, 125, (n, k // 32), generator=g, device=dev, dtype=torch.uint8))
+              for _ in range(copies)]
+        res = {"shape": [n, k], "weight_bytes": wbytes, "copies": copies, "by_rows": {}}
         for r in rows_list:
             x = torch.randn((r, k), generator=g, device=dev).to(torch.bfloat16)
             y = torch.empty((r, n), dtype=torch.bfloat16, device=dev)
-            for _ in range(3):
-                nv.nvfp4_mxfp4_gemv(codes, scales, x, out=y)
-            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            start.record(stream)
-            for _ in range(reps):
-                nv.nvfp4_mxfp4_gemv(codes, scales, x, out=y)
-            stop.record(stream)
-            torch.cuda.synchronize()
-            us = start.elapsed_time(stop) * 1e3 / reps
+            us = time_rotating(torch, lambda i: nv.nvfp4_mxfp4_gemv(cs[i][0], cs[i][1], x, out=y), copies,
+                               max(reps, 3 * copies))
             gbs = wbytes / (us * 1e-6) / 1e9
             res["by_rows"][str(r)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1),
                                       "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
-            log("mxfp4 %dx%d rows=%d: %.2f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (
-                n, k, r, us, gbs, 100 * gbs / HBM_PEAK_GBS))
+            log("mxfp4 %dx%d rows=%d (%d copies): %.2f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (
+                n, k, r, copies, us, gbs, 100 * gbs / HBM_PEAK_GBS))
         out["%dx%d" % (n, k)] = res
-        del codes, scales
+        del cs
     return out
 
 
 def time_w8(nv, torch, dev, rows_list, reps):
     """The W8G32_F16S projection (nvfp4_w8g32_gemv) on a gate-sized [17408 x
     5120] and a down-sized [5120 x 17408] matrix: random int8 codes and fp16
-    scales 2^-8..2^-6 drawn on the device, back-to-back calls between HIP
-    events; GB/s counts codes + scales once per call."""
+    scales 2^-8..2^-6 drawn on the device, back-to-back calls cycling through
+    >= 1 GiB of distinct copies; GB/s counts codes + scales once per call."""
     g = torch.Generator(device=dev).manual_seed(2025)
     out = {}
-    stream = torch.cuda.current_stream()
     for n, k in ((17408, 5120), (5120, 17408)):
-        codes = torch.randint(-127, 128, (n, k), generator=g, device=dev, dtype=torch.int8)
-        scales = torch.exp2(torch.randint(-8, -5, (n, k // 32), generator=g, device=dev).float()).half()
         wbytes = n * k + n * k // 32 * 2
-        res = {"shape": [n, k], "weight_bytes": wbytes, "by_rows": {}}
+        copies = -(-ROTATE_BYTES // wbytes)
+        cs = [(torch.randint(-127, 128, (n, k), generator=g, device=dev, dtype=torch.int8),
+               torch.exp2(torch.randint(-8, -5, (n, k // 32), generator=g, device=dev).float()).half())
+              for _ in range(copies)]
+        res = {"shape": [n, k], "weight_bytes": wbytes, "copies": copies, "by_rows": {}}
         for r in rows_list:
             x = torch.randn((r, k), generator=g, device=dev).to(torch.bfloat16)
             y = torch.empty((r, n), dtype=torch.bfloat16, device=dev)
-            for _ in range(3):
-                nv.nvfp4_w8g32_gemv(codes, scales, x, out=y)
-            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            start.record(stream)
-            for _ in range(reps):
-                nv.nvfp4_w8g32_gemv(codes, scales, x, out=y)
-            stop.record(stream)
-            torch.cuda.synchronize()
-            us = start.elapsed_time(stop) * 1e3 / reps
+            us = time_rotating(torch, lambda i: nv.nvfp4_w8g32_gemv(cs[i][0], cs[i][1], x, out=y), copies,
+                               max(reps, 3 * copies))
             gbs = wbytes / (us * 1e-6) / 1e9
             res["by_rows"][str(r)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1),
                                       "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
-            log("w8g32 %dx%d rows=%d: %.2f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (
-                n, k, r, us, gbs, 100 * gbs / HBM_PEAK_GBS))
+            log("w8g32 %dx%d rows=%d (%d copies): %.2f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (
+                n, k, r, copies, us, gbs, 100 * gbs / HBM_PEAK_GBS))
         out["%dx%d" % (n, k)] = res
-        del codes, scales
+        del cs
     return out
 
 
@@ -369,30 +585,28 @@ def time_norm(nv, torch, dev, reps):
     """nvfp4_residual_rmsnorm at the 27B model's hidden size (k = 5120): the
     average call at decode row counts (1 and 8: a few tens of KB, bound by
     latency) and GB/s at 4096 rows (reads residual and delta, writes
-    residual_out and x: 8 bytes per element)."""
+    residual_out and x: 8 bytes per element), cycling through >= 1 GiB of
+    distinct buffers."""
     g = torch.Generator(device=dev).manual_seed(99)
     k = 5120
     w = torch.randn((k,), generator=g, device=dev).to(torch.bfloat16)
     out = {"k": k, "by_rows": {}}
-    stream = torch.cuda.current_stream()
     for rows in (1, 8, 4096):
-        r = torch.randn((rows, k), generator=g, device=dev).to(torch.bfloat16)
-        h = torch.randn((rows, k), generator=g, device=dev).to(torch.bfloat16)
-        ro, x = torch.empty_like(r), torch.empty_like(r)
-        for _ in range(3):
-            nv.nvfp4_residual_rmsnorm(r, h, w, residual_out=ro, x=x)
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(reps):
-            nv.nvfp4_residual_rmsnorm(r, h, w, residual_out=ro, x=x)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        us = start.elapsed_time(stop) * 1e3 / reps
+        copies = max(1, -(-ROTATE_BYTES // (rows * k * 8)))
+        copies = min(copies, 64)
+        sets = []
+        for _ in range(copies):
+            r = torch.randn((rows, k), generator=g, device=dev).to(torch.bfloat16)
+            h = torch.randn((rows, k), generator=g, device=dev).to(torch.bfloat16)
+            sets.append((r, h, torch.empty_like(r), torch.empty_like(r)))
+        us = time_rotating(torch, lambda i: nv.nvfp4_residual_rmsnorm(sets[i][0], sets[i][1], w,
+                                                                      residual_out=sets[i][2], x=sets[i][3]),
+                           copies, max(reps, 3 * copies))
         gbs = rows * k * 8 / (us * 1e-6) / 1e9
-        out["by_rows"][str(rows)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1),
+        out["by_rows"][str(rows)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1), "copies": copies,
                                      "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
-        log("residual add + RMSNorm k=%d rows=%d: %.2f us, %.1f GB/s" % (k, rows, us, gbs))
+        log("residual add + RMSNorm k=%d rows=%d (%d copies): %.2f us, %.1f GB/s" % (k, rows, copies, us, gbs))
+        del sets
     return out
 
 
@@ -434,11 +648,20 @@ def main():
         del src, dst
         log("copy calibration: 1 GiB device-to-device copy done")
 
-    seqs = {r: make_sequence(nv, torch, dev, workloads, mats, r) for r in rows_list}
+    bufs = {r: {} for r in rows_list}
+    seqs = {r: make_sequence(nv, torch, dev, workloads, mats, r, bufs[r]) for r in rows_list}
     ws = torch.zeros(max(s.workspace_bytes for s in seqs.values()), dtype=torch.uint8, device=dev)
     by_rows = {}
+    parity = {}
     for r in rows_list:
         ms = time_rows(torch, seqs[r], ws, args.steps, args.warmup)
+        if nv.wait_flag(ws):
+            raise SystemExit("rows=%d: a wait between calls gave up (workspace wait flag set)" % r)
+        if r in (1, 8) and not args.no_cpu_baseline:
+            parity[str(r)] = parity_sample(nv, torch, mats, bufs[r], r)
+            log("rows=%d: parity sample of layer %d: max err/sum|w*x| %.3g, max %d bf16 ulp, %d outputs"
+                % (r, len(mats) - 1, parity[str(r)]["max_err_over_absdot"], parity[str(r)]["max_bf16_ulp"],
+                   parity[str(r)]["outputs"]))
         pair_ms = time_pair(nv, torch, dev, mats, r, ws, max(2, args.steps // 10))
         gbs = step_bytes / (ms * 1e-3) / 1e9
         by_rows[str(r)] = {
@@ -452,6 +675,11 @@ def main():
         log("rows=%d: %.4f ms/step in %d launches, %.1f GB/s (%.1f%% of 8 TB/s); stand-alone gate/up pair "
             "%.2f us" % (r, ms, seqs[r].launches, gbs, 100 * gbs / HBM_PEAK_GBS, pair_ms * 1e3))
 
+    wait_flag = nv.wait_flag(ws)
+    if wait_flag:
+        raise SystemExit("a wait between calls gave up (workspace wait flag set)")
+    del seqs, bufs
+    ceil_buf = torch.zeros(CEILING_BYTES, dtype=torch.uint8, device=dev)
     head = by_rows[str(rows_list[0])]
     # The dominant kernel is the shared launch that runs the step's calls
     # (every byte of the step is read by it): bytes and duration per launch.
@@ -471,6 +699,23 @@ def main():
         "bytes_per_launch": round(launch_bytes),
         "avg_launch_us": round(launch_us, 2),
     }
+    # the streaming-read ceiling for the same bytes per launch (the step's
+    # 1.86 GB launches), rotating through a 2 GiB buffer
+    cl = read_ceiling(nv, torch, dev, ceil_buf, int(launch_bytes) // 16 * 16, 20)
+    ceiling_gbs = launch_bytes / (pctl(cl, 50) * 1e-6) / 1e9
+    roofline["read_ceiling_GB_per_s"] = round(ceiling_gbs, 1)
+    roofline["frac_of_read_ceiling"] = round(achieved / ceiling_gbs, 4)
+    log("read ceiling for %.2f GB launches: %.1f GB/s (%.1f%% of 8 TB/s); the step reaches %.1f%% of it"
+        % (launch_bytes / 1e9, ceiling_gbs, 100 * ceiling_gbs / HBM_PEAK_GBS, 100 * achieved / ceiling_gbs))
+
+    singles = None
+    if args.layers == 64:
+        singles = single_calls(nv, torch, dev, workloads, mats, ceil_buf)
+        for key, v in singles.items():
+            log("%s: median %.2f us (p10 %.2f, p90 %.2f), %.1f GB/s = %.1f%% of 8 TB/s; read ceiling %.2f us; "
+                "floor at 75%%/70%%: %.2f us" % (key, v["median_us"], v["p10_us"], v["p90_us"], v["GB_per_s_median"],
+                                                v["pct_hbm_peak_median"], v["read_ceiling_median_us"],
+                                                v["derived_floor_us"]))
 
     dense = None
     if not args.no_dense:
@@ -489,6 +734,10 @@ def main():
         log("cpu baseline: oracle on layer 0 ...")
         cpu = cpu_baseline(workloads, torch, dev, args.cpu_seconds)
         log("cpu baseline: %.3f GB/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    del mats, ws
+    gc.collect()
+    torch.cuda.synchronize()
 
     line = {
         "metric": METRIC,
@@ -514,6 +763,9 @@ def main():
         },
         "pct_hbm_peak": head["pct_hbm_peak"],
         "by_rows": by_rows,
+        "wait_timeouts": wait_flag,
+        "parity_sample": parity or None,
+        "single_calls": singles,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_lm_head": dense,
@@ -522,6 +774,14 @@ def main():
         "w8g32_f16s": w8,
     }
     print(json.dumps(line), flush=True)
+    # end deterministically: nothing left on the device or in flight when the
+    # interpreter (and any profiler attached to it) shuts down
+    del ceil_buf
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    sys.stdout.flush()
+    sys.stderr.flush()
 
 
 if __name__ == "__main__":

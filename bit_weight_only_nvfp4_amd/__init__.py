@@ -28,6 +28,7 @@ NVFP4_LAYOUT_VERSION = 3
 NVFP4_MAX_ROWS = 128
 NVFP4_OUT_BF16 = 0
 NVFP4_OUT_F32 = 1
+NVFP4_WS_WAIT_FLAG_OFFSET = 65536   # uint32 in a sequence workspace: a wait between calls gave up
 
 STATUS = {
     0: "NVFP4_OK", -1: "NVFP4_E_NULL", -2: "NVFP4_E_SHAPE", -3: "NVFP4_E_ROWS", -4: "NVFP4_E_ALIGN",
@@ -40,7 +41,7 @@ EXPORTS = (
     "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
     "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16", "nvfp4_residual_rmsnorm",
-    "nvfp4_mxfp4_gemv", "nvfp4_w8g32_gemv",
+    "nvfp4_mxfp4_gemv", "nvfp4_w8g32_gemv", "nvfp4_read_ceiling",
 )
 
 
@@ -111,6 +112,7 @@ def lib() -> ctypes.CDLL:
             "nvfp4_w8g32_gemv": ([vp, vp, i64, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
             "nvfp4_residual_rmsnorm": ([vp, vp, vp, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, vp, vp],
                                        ctypes.c_int),
+            "nvfp4_read_ceiling": ([vp, sz, vp, vp], ctypes.c_int),
         }
         for name, (argt, rest) in sig.items():
             f = getattr(L, name)
@@ -367,6 +369,28 @@ def nvfp4_residual_rmsnorm(residual: torch.Tensor, delta: torch.Tensor, weight: 
                                         int(bool(gemma_offset)), _ptr(residual_out), _ptr(x),
                                         _stream(residual.device)))
     return residual_out, x
+
+
+def nvfp4_read_ceiling(buf: torch.Tensor, nbytes: int | None = None, sink: torch.Tensor | None = None,
+                       offset: int = 0) -> torch.Tensor:
+    """Read ``nbytes`` of ``buf`` (a device tensor) from byte ``offset`` once
+    with the projection kernel's launch shape: the streaming-read ceiling.
+    Returns the 256-word sink."""
+    nb = buf.numel() * buf.element_size() - offset if nbytes is None else nbytes
+    if sink is None:
+        sink = torch.empty(256, dtype=torch.int32, device=buf.device)
+    _check("nvfp4_read_ceiling", lib().nvfp4_read_ceiling(buf.data_ptr() + offset, nb, sink.data_ptr(),
+                                                          _stream(buf.device)))
+    return sink
+
+
+def wait_flag(workspace: torch.Tensor) -> int:
+    """The workspace's wait flag (nonzero: a wait between calls of a launch of
+    several calls gave up); synchronizes with the device to read it."""
+    off = NVFP4_WS_WAIT_FLAG_OFFSET
+    if workspace.numel() < off + 4:
+        return 0
+    return int(workspace[off:off + 4].view(torch.int32).item())
 
 
 class Sequence:

@@ -486,6 +486,16 @@ int nvfp4_residual_rmsnorm(const void *residual, const void *delta, const void *
                                                   residual_out, x, static_cast<hipStream_t>(stream)));
 }
 
+int nvfp4_read_ceiling(const void *buf, size_t bytes, void *sink, void *stream) {
+    static const char *fn = "nvfp4_read_ceiling";
+    if (!buf || !sink) return fail(NVFP4_E_NULL, "%s: buf or sink is NULL", fn);
+    if (bytes == 0 || bytes % 16 != 0) return fail(NVFP4_E_SHAPE, "%s: bytes=%zu (need a positive multiple of 16)", fn, bytes);
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(NVFP4_E_ALIGN, "%s: buf must be 16-byte and sink 4-byte aligned", fn);
+    int st = check_device(fn);
+    if (st) return st;
+    return hip_status(fn, launch_read_ceiling(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
                         void *const *events, void *stream) {
     static const char *fn = "nvfp4_gemv_sequence";

@@ -67,6 +67,7 @@ constexpr int64_t kMaxN = (int64_t)1 << 20;
 constexpr size_t kSyncOffset = 32 * 1024;
 constexpr size_t kFlagOffset = 64 * 1024;
 constexpr size_t kPartialOffset = 65 * 1024;
+static_assert(kFlagOffset == NVFP4_WS_WAIT_FLAG_OFFSET, "the wait flag sits where the ABI says");
 
 // Bytes 32..255 of the header are always zero (pack and quantize write them);
 // kernels use them as a 16-byte source of zeros.
@@ -204,6 +205,9 @@ hipError_t launch_w8(const void *codes, const void *scales, int64_t n, int64_t k
 int64_t norm_max_k();
 hipError_t launch_residual_rmsnorm(const void *r, const void *h, const void *w, int64_t k, int rows, float eps,
                                    int gemma_offset, void *r_out, void *x, hipStream_t stream);
+
+// Streaming-read ceiling: read `bytes` (a multiple of 16) once; 256 words to `sink`.
+hipError_t launch_read_ceiling(const void *buf, size_t bytes, void *sink, hipStream_t stream);
 
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
                        int64_t n, int64_t k, void *packed, hipStream_t stream);

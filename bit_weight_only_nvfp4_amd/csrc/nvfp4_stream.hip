@@ -81,7 +81,10 @@ static_assert(sizeof(CallDesc) % 4 == 0, "call descriptors are copied as words")
 constexpr int kSC1 = 16;                          // cache policy: device-coherent access
 constexpr int kDroppedOffset = 0x7fffffff;        // past any buffer: loads read 0, stores are dropped
 constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit data format
-constexpr uint64_t kWaitTicks = 20000000;         // 0.2 s of the 100 MHz real-time clock
+// Polls a wait between calls makes before it gives up (each poll is a round
+// trip to memory, about a microsecond): counted rather than timed, so a
+// dispatch that the scheduler pauses cannot run out of time while paused.
+constexpr unsigned kMaxPolls = 1u << 18;
 
 // Workgroup whose shared range [floor(g*U/G), floor((g+1)*U/G)) holds shared
 // unit v: the largest g with g*U < (v+1)*G, i.e. ((v+1)*G - 1) / U.
@@ -488,8 +491,8 @@ __device__ __forceinline__ bool arrive_piece(const SeqArgs &a, int sh, int np, i
 // workgroup counts itself in one arrival counter once its writes of the call
 // are complete; the workgroup whose count completes epoch e stores e in every
 // workgroup's release word, each in a 128-byte line of its own that only its
-// workgroup polls, and goes on without waiting (returns true).  A wait that
-// exceeds kWaitTicks sets a flag and goes on: it never hangs.
+// workgroup polls, and goes on without waiting (returns true).  A wait of
+// more than kMaxPolls polls sets the wait flag and goes on: it never hangs.
 __device__ __forceinline__ bool arrive_call(const SeqArgs &a, int g, unsigned e, int lane) {
     wait_own_writes();
     const bool last = lane0_add(a.flags + 32, lane) + 1u == e * (unsigned)a.G;
@@ -509,13 +512,12 @@ __device__ __forceinline__ bool arrive_call(const SeqArgs &a, int g, unsigned e,
 // fetch of the next call's first items (a poll's result waits for every load
 // issued before it) 0.4-2.6% slower.
 __device__ __forceinline__ void wait_release(const SeqArgs &a, int g, unsigned e, int lane) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    bool late = false;
-    while (lane0_load(a.sync + g * 32, lane) < e && !late) {
+    unsigned polls = 0;
+    while (lane0_load(a.sync + g * 32, lane) < e && polls < kMaxPolls) {
         __builtin_amdgcn_s_sleep(1);
-        late = __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks;
+        ++polls;
     }
-    if (late) lane0_store(a.flags, 1u, lane);
+    if (polls >= kMaxPolls) lane0_store(a.flags, 1u, lane);
 }
 
 // SEQ: several calls per launch (the cross-call pipeline and the completion

@@ -36,18 +36,27 @@
  *
  * Packed (device-tiled) weight, produced by nvfp4_pack / nvfp4_quantize:
  *   [256-byte header][strip 0: super-tiles 0..T-1][strip 1 ...] ...
- *   strip = 64 output features, super-tile = 64 features x 256 k = 9216 bytes,
- *   an array of 576 entries of 16 bytes (layout version 2):
- *     code entry e = 32 c + 16 h + j (e < 512), chunk c = 4 kb + fb: the 32
- *       codes (canonical nibble order) of feature 64 s + 16 fb + j for
- *       k = 256 u + 64 kb + 32 h .. + 31, i.e. 16 consecutive canonical bytes;
- *     scale entry e = 512 + 16 g + j: byte 4 kb + fb is the E4M3 scale of
- *       feature 64 s + 16 fb + j for group 16 u + 4 kb + g.
- *   Features >= n and k >= k are zero padding.  Each 512-byte code chunk is
- *   the weight operand of one block-scaled matrix-core product (16 features x
- *   64 k); a wave reads it with one aligned 16-byte load per lane.
+ *   strip = 64 output features, super-tile = 64 features x 256 k = 9216 bytes
+ *   (layout version 3): 8 code chunks of 1 KB, then a 1 KB scale chunk, each
+ *   64 entries of 16 bytes (entry l = 16 q + j is what lane l of a wave reads):
+ *     code chunk c, entry l, dword d: the 8 codes (4 canonical bytes) of
+ *       feature 64 s + 16 (c >> 1) + j for k = 256 u + 32 (4 (c & 1) + d) + 8 q
+ *       .. + 7;
+ *     scale chunk, entry l, byte 8 b + t: the E4M3 scale of feature
+ *       64 s + 16 (2 (q >> 1) + b) + j, group 16 u + 2 t + (q & 1).
+ *   Features >= n and k >= k are zero padding.  Each lane's 16 code bytes hold
+ *   the weight operands of four 16x16x32 matrix-core products, and one wave
+ *   instruction reads one whole, aligned 1 KB run of 128-byte lines.
  *   The header holds s_g (float at byte 0), the layout magic and version, n, k.
- *   One wave instruction therefore reads one whole, aligned 1 KB run.
+ *
+ * Arithmetic of the projections (nvfp4_gemv, the pair, nvfp4_gemv_sequence):
+ * every product of a bf16 activation, exactly as stored, and an E2M1 code is
+ * exact; each 16-element group's sum comes from the matrix core in fp32 and is
+ * multiplied by its E4M3 group scale into an fp32 accumulator; s_g multiplies
+ * the fp32 total.  This holds for every finite bf16 activation, subnormals
+ * included (fp32 subnormal products are kept).  A row's result is
+ * bit-identical whatever the number of rows in the call (1..NVFP4_MAX_ROWS)
+ * and run to run.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -116,8 +125,11 @@ int nvfp4_pack(const uint8_t *codes, const uint8_t *scales, float global_scale,
 int nvfp4_unpack(const nvfp4_weight *w, uint8_t *codes, uint8_t *scales,
                  float *global_scale, void *stream);
 
-/* Dequantize to fp32 out[n][k] = fp32(fp32(e2m1 * e4m3) * s_g), using the same
- * device decode routines as the projection kernels.  out 16-byte aligned. */
+/* Dequantize to fp32 out[n][k] = fp32(fp32(e2m1 * e4m3) * s_g) (test and
+ * inspection use).  The codes go through the conversion instruction the
+ * projection kernels use (v_cvt_scalef32_pk_bf16_fp4, exact); the scale and
+ * s_g are applied in fp32 here, while the projections apply the scale to each
+ * group's sum and s_g to the total.  out 16-byte aligned. */
 int nvfp4_dequant(const nvfp4_weight *w, float *out, void *stream);
 
 /* Quantize fp32 weights W[n][k] (device, 16-byte aligned) straight into the
@@ -148,9 +160,7 @@ size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual);
  * run to run.  A kernel computes up to 16 rows; a call of more rows runs as
  * ceil(rows / 16) chunks of balanced row counts, each reading the weights
  * once (the pages' wider row tiers: up to 32 draft and 128 multi-sequence
- * rows).  From 5 rows on, a row's result does not depend on the call's row
- * count (the same holds among 2..4 rows); across those tiers it differs by
- * fp32 rounding only.
+ * rows).  A row's result does not depend on the call's row count.
  * workspace: >= nvfp4_workspace_bytes(n, k, rows, 0) bytes, 16-byte aligned,
  * ZERO-FILLED before its first use.  Its first 65 KiB hold counters at fixed
  * positions and every call returns them to zero, so one workspace serves any
@@ -178,6 +188,14 @@ typedef struct nvfp4_call {
     int rows;                /* 1..NVFP4_MAX_ROWS                                  */
     int out_dtype;           /* NVFP4_OUT_BF16 or NVFP4_OUT_F32                    */
 } nvfp4_call;
+
+/* Byte offset, in a projection workspace, of the uint32 wait flag: a launch
+ * of several calls (nvfp4_gemv_sequence) sets it to nonzero if one of its
+ * waits between calls gave up (after 2^18 polls, about a second; it then goes
+ * on so that no launch can hang, and that launch's results are not
+ * reliable).  Nothing clears it but the caller: read it after a
+ * synchronization to check a run of launches. */
+#define NVFP4_WS_WAIT_FLAG_OFFSET 65536
 
 /* Workspace for nvfp4_gemv_sequence: the largest partial sums any of its
  * calls needs, plus the counters (65 KiB) when ncalls > 1. */
@@ -258,6 +276,14 @@ int nvfp4_residual_rmsnorm(const void *residual, const void *delta, const void *
  * events on the current device (one per call where shared launches are not
  * available); 0 if ncalls <= 0 or calls is NULL. */
 int nvfp4_sequence_launches(const nvfp4_call *calls, int ncalls);
+
+/* Measurement aid, not part of the method: read `bytes` of device memory at
+ * `buf` once with the projection kernel's launch shape (16-byte nontemporal
+ * loads, one 512-thread workgroup per CU) and nothing else -- the streaming
+ * read ceiling the projections are compared with beside the nominal HBM peak.
+ * buf 16-byte aligned, bytes a positive multiple of 16; sink: device, 256
+ * uint32 (4-byte aligned), receives a fold of the bytes read. */
+int nvfp4_read_ceiling(const void *buf, size_t bytes, void *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,8 @@ def _load():
                                        i64, i64, c_u16p, ctypes.c_int, c_i64p, i64,
                                        c_f64p, c_f64p, c_f64p, c_f64p, c_f64p, c_u16p]
     lib.nvo_gemv_dual_silu.restype = ctypes.c_int
+    lib.nvo_set_num_threads.argtypes = [ctypes.c_int]
+    lib.nvo_set_num_threads.restype = None
     lib.nvo_dense_gemv.argtypes = [c_u16p, i64, i64, c_u16p, ctypes.c_int, c_i64p, i64, c_f64p, c_f64p, c_u16p]
     lib.nvo_dense_gemv.restype = None
     lib.nvo_residual_rmsnorm.argtypes = [c_u16p, c_u16p, c_u16p, i64, ctypes.c_int, ctypes.c_double, ctypes.c_int,
@@ -253,6 +255,12 @@ def gemv_dual_silu(gate, up, x_bf16, sel=None):
 
 def num_threads() -> int:
     return int(_load().nvo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's projections use (OpenMP over output features; the
+    results do not depend on it)."""
+    _load().nvo_set_num_threads(int(n))
 
 
 def dense_gemv(W_bf16, x_bf16, sel=None):

@@ -308,6 +308,15 @@ int nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g_
     return 0;
 }
 
+void nvo_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int nvo_num_threads(void)
 {
 #ifdef _OPENMP

@@ -74,6 +74,7 @@ int  nvo_gemv_dual_silu(const uint8_t *g_codes, const uint8_t *g_scales, float g
                         double *o, double *g, double *u, double *abs_g, double *abs_u,
                         uint16_t *o_bf16);
 int  nvo_num_threads(void);
+void nvo_set_num_threads(int n);   /* OpenMP threads of the projections (results do not depend on it) */
 
 /* Dense bf16 projection: W bf16 [n][k], x bf16 [rows][k]; y, |D.x| sums and a
  * bf16 copy of y for the selected features (sel NULL: all), [rows][nsel]. */

@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(nv):
     names = _declared_functions()
-    assert len(names) == 19, names
+    assert len(names) >= 20, names
     L = ctypes.CDLL(nv.LIB_PATH)
     for name in names:
         assert hasattr(L, name), name
@@ -308,3 +308,12 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, nv):
     monkeypatch.setattr(pkg, "LIB_PATH", "/nonexistent/libnvfp4_hip.so")
     with pytest.raises(ImportError):
         pkg.lib()
+
+
+def test_read_ceiling_argument_errors(nv):
+    L = nv.lib()
+    E = {v: k for k, v in nv.STATUS.items()}
+    assert L.nvfp4_read_ceiling(None, 1024, YF, None) == E["NVFP4_E_NULL"]
+    assert L.nvfp4_read_ceiling(FAKE, 0, YF, None) == E["NVFP4_E_SHAPE"]
+    assert L.nvfp4_read_ceiling(FAKE, 1000, YF, None) == E["NVFP4_E_SHAPE"]
+    assert L.nvfp4_read_ceiling(FAKE + 8, 1024, YF, None) == E["NVFP4_E_ALIGN"]
