@@ -41,7 +41,7 @@ EXPORTS = (
     "nvfp4_unpack", "nvfp4_dequant", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize",
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
     "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16", "nvfp4_residual_rmsnorm",
-    "nvfp4_mxfp4_gemv", "nvfp4_w8g32_gemv", "nvfp4_read_ceiling",
+    "nvfp4_mxfp4_gemv", "nvfp4_w8g32_gemv", "nvfp4_read_ceiling", "nvfp4_gemv_noalloc",
 )
 
 
@@ -113,6 +113,7 @@ def lib() -> ctypes.CDLL:
             "nvfp4_residual_rmsnorm": ([vp, vp, vp, i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, vp, vp],
                                        ctypes.c_int),
             "nvfp4_read_ceiling": ([vp, sz, vp, vp], ctypes.c_int),
+            "nvfp4_gemv_noalloc": ([wp, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
         }
         for name, (argt, rest) in sig.items():
             f = getattr(L, name)
@@ -283,6 +284,17 @@ def nvfp4_gemv(w: PackedWeight, x: torch.Tensor, out_dtype=torch.bfloat16, out: 
     _check("nvfp4_gemv", lib().nvfp4_gemv(ctypes.byref(w.desc), _ptr(x), rows, _ptr(out), _OUT[out.dtype],
                                           _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                           _stream(x.device)))
+    return out
+
+
+def nvfp4_gemv_noalloc(w: PackedWeight, x: torch.Tensor, out_dtype=torch.bfloat16,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """nvfp4_gemv with the library's static per-device scratch as its workspace
+    (no device allocation by the library; ``out`` may be given so that nothing
+    is allocated here either)."""
+    x, rows, out = _gemv_common(x, None, out_dtype, out, w.n)
+    _check("nvfp4_gemv_noalloc", lib().nvfp4_gemv_noalloc(ctypes.byref(w.desc), _ptr(x), rows, _ptr(out),
+                                                          _OUT[out.dtype], _stream(x.device)))
     return out
 
 

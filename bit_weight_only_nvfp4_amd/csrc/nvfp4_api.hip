@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "nvfp4_internal.h"
@@ -194,6 +195,41 @@ int check_call(const char *fn, const nvfp4_weight *w, const nvfp4_weight *up, co
     return check_gemv_args(fn, x, rows, y, out_dtype);
 }
 
+// The projection workspace of nvfp4_gemv_noalloc: a file-scope device array,
+// one per device the library runs on, held until the process ends.  It is
+// zero when the code object is loaded, and every launch leaves its counters
+// at zero again (the partial sums are written before they are read), so it
+// never needs clearing.  Host code never passes the array's name to a kernel
+// or a copy (that is a host-side stand-in, not a device address): it uses the
+// device address hipGetSymbolAddress returned for the current device.
+constexpr size_t kScratchBytes = NVFP4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` on device d, set once
+
+// The device address of the current device's scratch array, looked up on the
+// first call on that device (with it current) and kept.
+int scratch_address(const char *fn, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) return fail(NVFP4_E_DEVICE, "%s: no HIP device (%s)", fn, hipGetErrorString(e));
+    if (dev >= kMaxDevices) return fail(NVFP4_E_DEVICE, "%s: device %d beyond the %d this library tracks", fn, dev,
+                                        kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(NVFP4_E_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NVFP4_OK;
+}
+
 int run_one(const char *fn, const nvfp4_weight *w, const nvfp4_weight *up, const void *x, int rows, void *y,
             int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_call(fn, w, up, x, rows, y, out_dtype);
@@ -331,6 +367,31 @@ size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual) {
 int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype, void *workspace,
                size_t workspace_bytes, void *stream) {
     return run_one("nvfp4_gemv", w, nullptr, x, rows, y, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int nvfp4_gemv_noalloc(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype, void *stream) {
+    static const char *fn = "nvfp4_gemv_noalloc";
+    int st = check_call(fn, w, nullptr, x, rows, y, out_dtype);
+    if (st) return st;
+    st = check_self_overlap(fn, w, x, rows, y, out_dtype);
+    if (st) return st;
+    std::vector<StreamCall> sc;
+    add_calls(sc, w, nullptr, x, rows, y, out_dtype);
+    const int nc = (int)sc.size();
+    const size_t need = sequence_workspace_bytes(sc.data(), nc);
+    if (need > kScratchBytes)
+        return fail(NVFP4_E_WORKSPACE,
+                    "%s: this call needs %zu bytes of workspace; the static scratch holds %zu (use nvfp4_gemv "
+                    "with a workspace of nvfp4_workspace_bytes(n, k, rows, 0) bytes)",
+                    fn, need, kScratchBytes);
+    st = check_device(fn);
+    if (st) return st;
+    void *ws = nullptr;
+    st = scratch_address(fn, &ws);
+    if (st) return st;
+    st = check_overlaps(fn, sc.data(), nc, ws, need);
+    if (st) return st;
+    return hip_status(fn, launch_sequence(sc.data(), nc, need ? ws : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const void *x, int rows, void *y,

@@ -169,6 +169,22 @@ size_t nvfp4_workspace_bytes(int64_t n, int64_t k, int rows, int dual);
 int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype,
                void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): nvfp4_gemv
+ * with the workspace taken from a static array inside the library (one per
+ * device, NVFP4_NOALLOC_SCRATCH_BYTES, held until the process ends) instead of
+ * the caller's.  Same arguments, results (bit for bit) and errors as
+ * nvfp4_gemv; it allocates and frees nothing.  The array holds the largest
+ * workspace any valid call needs (at most 255 shared strips of at most 16 rows
+ * in fewer than 768 pieces: under 3.2 MB of partial sums plus 65 KiB of
+ * counters); a call whose workspace would exceed it is refused with
+ * NVFP4_E_WORKSPACE before anything is launched.  Every call on one device shares that device's
+ * array, which keeps the last call's contents: calls that may overlap in time
+ * on one device (different streams without ordering) race and must not be
+ * made.  The array starts at zero and every call leaves its counters at zero. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int nvfp4_gemv_noalloc(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype, void *stream);
+
 /* Fused gate/up pair of the SwiGLU FFN: o = silu(g) * u with
  * g = x W_gate^T, u = x W_up^T (both as in nvfp4_gemv, fp32), silu(g) =
  * g / (1 + exp(-g)), evaluated after the full reduction -- the blueprint
