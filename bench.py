@@ -6,7 +6,7 @@ at one row count: per layer qkv [12288x5120], o [5120x6144], the gate/up pair
 2x[17408x5120] with SiLU*mul, down [5120x17408] (whose input is the pair's
 output), 256 calls, 13,023,313,920 bytes of packed weights (E2M1 codes +
 E4M3 scales, 9/16 byte per weight).  The calls run in order, each after the
-previous one has completed, in shared launches of up to 40 calls.  Weights ~ N(0, 0.02^2) are drawn on the
+previous one has completed, in shared launches of up to 36 calls.  Weights ~ N(0, 0.02^2) are drawn on the
 device from seeded generators and quantized on the device; activations are
 bf16 ~ N(0, 1).  All weights stay resident in HBM (no cache reuse between
 layers: 13 GB >> the 256 MB Infinity Cache).
@@ -22,6 +22,11 @@ the 64 layers' pairs launched back to back.
 After timing, every row count's workspace wait flag must be clear, and at
 rows 1 and 8 sampled outputs of the timed step's last layer (every call of
 layer 63, 256 features each) are checked against the CPU oracle.
+
+The same step with each layer's two residual add + RMSNorm calls (the first
+producing qkv's input from the residual and the previous layer's down output,
+the second the pair's input from the residual and o's output) fused into its
+launches is timed at rows 1 and 8 as well (step_with_norms).
 
 Single projection calls (qkv at 1 row, the gate/up pair at 1 row, down at 8
 rows with 1% outlier groups) are timed one call between two events each,
@@ -112,17 +117,30 @@ def build_sweep(nv, workloads, torch, dev, layers):
     return mats
 
 
-def make_sequence(nv, torch, dev, workloads, mats, rows, bufs=None):
+def make_sequence(nv, torch, dev, workloads, mats, rows, bufs=None, norms=False):
+    """The decode step's calls for every layer: qkv, o, the gate/up pair and
+    down (fed by the pair).  With norms, each layer also runs its two residual
+    add + RMSNorm calls inside the same launches: the first (residual +=
+    previous down output) produces qkv's input, the second (residual += o's
+    output) the pair's."""
     x5120 = workloads.draw_x_device(rows, 5120, 5_000_000 + rows, dev)
     x6144 = workloads.draw_x_device(rows, 6144, 5_000_100 + rows, dev)
     y_qkv = torch.empty((rows, 12288), dtype=torch.bfloat16, device=dev)
-    y_o = torch.empty((rows, 5120), dtype=torch.bfloat16, device=dev)
+    y_o = torch.zeros((rows, 5120), dtype=torch.bfloat16, device=dev)
     o_gu = torch.empty((rows, 17408), dtype=torch.bfloat16, device=dev)
-    y_down = torch.empty((rows, 5120), dtype=torch.bfloat16, device=dev)
+    y_down = torch.zeros((rows, 5120), dtype=torch.bfloat16, device=dev)
     calls = []
-    for lm in mats:
+    if norms:
+        resid = workloads.draw_x_device(rows, 5120, 5_000_200 + rows, dev)
+        g = torch.Generator(device=dev).manual_seed(5_000_300)
+        lns = (torch.randn((len(mats), 2, 5120), generator=g, device=dev) * 0.1).to(torch.bfloat16)
+    for li, lm in enumerate(mats):
+        if norms:
+            calls.append(nv.Norm(resid, y_down, lns[li, 0], x5120, gemma_offset=True))
         calls.append((lm["qkv"], None, x5120, y_qkv))
         calls.append((lm["o"], None, x6144, y_o))
+        if norms:
+            calls.append(nv.Norm(resid, y_o, lns[li, 1], x5120, gemma_offset=True))
         calls.append((lm["gate"], lm["up"], x5120, o_gu))
         calls.append((lm["down"], None, o_gu, y_down))
     if bufs is not None:
@@ -675,6 +693,22 @@ def main():
         log("rows=%d: %.4f ms/step in %d launches, %.1f GB/s (%.1f%% of 8 TB/s); stand-alone gate/up pair "
             "%.2f us" % (r, ms, seqs[r].launches, gbs, 100 * gbs / HBM_PEAK_GBS, pair_ms * 1e3))
 
+    # the same step with each layer's two residual add + RMSNorm calls inside
+    # its launches (the activations of qkv and of the pair made by the step)
+    with_norms = {}
+    for r in [r for r in (1, 8) if r in rows_list]:
+        seq_n = make_sequence(nv, torch, dev, workloads, mats, r, norms=True)
+        ms = time_rows(torch, seq_n, ws, max(5, args.steps // 2), min(args.warmup, 3))
+        if nv.wait_flag(ws):
+            raise SystemExit("rows=%d with norms: a wait between calls gave up" % r)
+        base = by_rows[str(r)]["ms_per_step"]
+        with_norms[str(r)] = {"ms_per_step": round(ms, 4), "launches_per_step": seq_n.launches,
+                              "calls_per_step": seq_n.n, "added_ms_vs_projections_only": round(ms - base, 4),
+                              "added_us_per_norm": round((ms - base) * 1e3 / (2 * args.layers), 3)}
+        log("rows=%d with %d fused residual add + RMSNorm calls: %.4f ms/step in %d launches (+%.3f us per norm)"
+            % (r, 2 * args.layers, ms, seq_n.launches, (ms - base) * 1e3 / (2 * args.layers)))
+        del seq_n
+
     wait_flag = nv.wait_flag(ws)
     if wait_flag:
         raise SystemExit("a wait between calls gave up (workspace wait flag set)")
@@ -770,6 +804,7 @@ def main():
         "cpu_baseline": cpu,
         "dense_lm_head": dense,
         "residual_rmsnorm": norm,
+        "step_with_norms": with_norms or None,
         "mxfp4": mx,
         "w8g32_f16s": w8,
     }

@@ -9,7 +9,8 @@ Entry points (same names as the C ABI):
   nvfp4_packed_bytes, nvfp4_pack, nvfp4_unpack, nvfp4_dequant,
   nvfp4_quantize_workspace_bytes, nvfp4_quantize,
   nvfp4_workspace_bytes, nvfp4_gemv, nvfp4_gemv_dual_silu,
-  nvfp4_sequence_workspace_bytes, nvfp4_gemv_sequence, nvfp4_sequence_launches,
+  nvfp4_sequence_workspace_bytes, nvfp4_gemv_sequence, nvfp4_sequence_launches
+  (projections, gate/up pairs and residual add + RMSNorm calls: Sequence, Norm),
   nvfp4_abi_version, nvfp4_strerror, nvfp4_last_error.
 """
 from __future__ import annotations
@@ -25,6 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4_hip.so")
 
 NVFP4_LAYOUT_MAGIC = 0x34465056
 NVFP4_LAYOUT_VERSION = 3
+NVFP4_ABI_VERSION = 2
 NVFP4_MAX_ROWS = 128
 NVFP4_OUT_BF16 = 0
 NVFP4_OUT_F32 = 1
@@ -55,6 +57,18 @@ class nvfp4_weight(ctypes.Structure):
     ]
 
 
+class nvfp4_norm(ctypes.Structure):
+    _fields_ = [
+        ("residual", ctypes.c_void_p),
+        ("delta", ctypes.c_void_p),
+        ("weight", ctypes.c_void_p),
+        ("residual_out", ctypes.c_void_p),
+        ("k", ctypes.c_int64),
+        ("eps", ctypes.c_float),
+        ("gemma_offset", ctypes.c_int),
+    ]
+
+
 class nvfp4_call(ctypes.Structure):
     _fields_ = [
         ("w", ctypes.POINTER(nvfp4_weight)),
@@ -63,6 +77,7 @@ class nvfp4_call(ctypes.Structure):
         ("y", ctypes.c_void_p),
         ("rows", ctypes.c_int),
         ("out_dtype", ctypes.c_int),
+        ("norm", ctypes.POINTER(nvfp4_norm)),
     ]
 
 
@@ -405,13 +420,35 @@ def wait_flag(workspace: torch.Tensor) -> int:
     return int(workspace[off:off + 4].view(torch.int32).item())
 
 
+class Norm:
+    """A residual add + RMSNorm call of a Sequence: residual_out = bf16(residual
+    + delta), x = RMSNorm(residual_out) * w' (w' = weight, or 1 + weight with
+    the Gemma offset); residual_out defaults to residual (updated in place).
+    All bf16 device tensors: residual, delta, residual_out, x [rows, k];
+    weight [k]."""
+
+    def __init__(self, residual: torch.Tensor, delta: torch.Tensor, weight: torch.Tensor, x: torch.Tensor,
+                 residual_out: torch.Tensor | None = None, eps: float = 1e-6, gemma_offset: bool = False):
+        self.residual, self.delta, self.weight, self.x = residual, delta, weight, x
+        self.residual_out = residual if residual_out is None else residual_out
+        for name in ("residual", "delta", "weight", "x", "residual_out"):
+            t = getattr(self, name)
+            if t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise TypeError("%s must be a contiguous bfloat16 tensor" % name)
+        self.desc = nvfp4_norm(residual.data_ptr(), delta.data_ptr(), weight.data_ptr(),
+                               self.residual_out.data_ptr(), residual.shape[-1], float(eps),
+                               int(bool(gemma_offset)))
+
+
 class Sequence:
-    """A prepared list of projection calls (the projections of a decode step),
-    built once and enqueued with one native call each time it runs.
+    """A prepared list of calls (the projections of a decode step, and the
+    residual add + RMSNorm between them), built once and enqueued with one
+    native call each time it runs.
 
     ``calls``: iterable of (weight, up_or_None, x, y) with x bf16 [rows, k] and y
-    [rows, n] (bf16 or fp32) device tensors; a call may take an earlier call's y
-    as its x.
+    [rows, n] (bf16 or fp32) device tensors, or Norm objects; a call may take
+    an earlier call's y as its x (a Norm: its x as a projection's x, its
+    residual_out as a later Norm's residual, a projection's y as its delta).
     """
 
     def __init__(self, calls):
@@ -419,16 +456,27 @@ class Sequence:
         self._keep = []
         self.n = len(calls)
         self._arr = (nvfp4_call * max(self.n, 1))()
-        for i, (w, up, x, y) in enumerate(calls):
+        for i, item in enumerate(calls):
+            c = self._arr[i]
+            if isinstance(item, Norm):
+                c.w = c.up = None
+                c.x = None
+                c.y = item.x.data_ptr()
+                c.rows = item.residual.shape[0]
+                c.out_dtype = NVFP4_OUT_BF16
+                c.norm = ctypes.pointer(item.desc)
+                self._keep.append((None, None, item.residual, item))
+                continue
+            w, up, x, y = item
             if x.dtype != torch.bfloat16 or y.dtype not in _OUT:
                 raise TypeError("call %d: x must be bfloat16 and y bfloat16 or float32" % i)
-            c = self._arr[i]
             c.w = ctypes.pointer(w.desc)
             c.up = ctypes.pointer(up.desc) if up is not None else None
             c.x = x.data_ptr()
             c.y = y.data_ptr()
             c.rows = x.shape[0]
             c.out_dtype = _OUT[y.dtype]
+            c.norm = None
             self._keep.append((w, up, x, y))
         self.workspace_bytes = int(lib().nvfp4_sequence_workspace_bytes(self._arr, self.n))
         # kernel launches of one launch() without events

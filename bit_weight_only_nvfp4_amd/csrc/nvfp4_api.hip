@@ -110,21 +110,36 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 size_t x_bytes(const StreamCall &c) { return (size_t)c.plan.rows * c.plan.k * 2; }
 size_t y_bytes(const StreamCall &c) { return (size_t)c.plan.rows * c.plan.n * (c.out_f32 ? 4 : 2); }
-size_t w_bytes(const StreamCall &c) { return nvfp4_packed_bytes(c.plan.n, c.plan.k); }
+// the bytes a call reads from w0 and w1 (a norm call: delta and weight)
+size_t w_bytes(const StreamCall &c) {
+    return c.norm ? (size_t)c.plan.rows * c.plan.k * 2 : nvfp4_packed_bytes(c.plan.n, c.plan.k);
+}
+size_t w1_bytes(const StreamCall &c) {
+    return c.norm ? (size_t)c.plan.k * 2 : (c.w1 ? nvfp4_packed_bytes(c.plan.n, c.plan.k) : 0);
+}
 
 // A call's outputs may not overlap its own activations, the workspace or any
-// weight of the launch (weights are read ahead across calls).
+// weight of the launch (weights are read ahead across calls).  A norm call's
+// delta is read as an activation, after the calls before it have finished, so
+// an earlier call may write it; its residual_out may be its own residual, and
+// a later call may read it (a norm's residual, a projection's x).
 int check_overlaps(const char *fn, const StreamCall *calls, int ncalls, const void *workspace, size_t ws_bytes) {
     for (int i = 0; i < ncalls; ++i) {
         const StreamCall &c = calls[i];
-        if (overlap(c.y, y_bytes(c), c.x, x_bytes(c)))
+        const size_t yb = y_bytes(c), rb = c.norm ? x_bytes(c) : 0;
+        if (overlap(c.y, yb, c.x, x_bytes(c)))
             return fail(NVFP4_E_OVERLAP, "%s: call %d: y overlaps its x", fn, i);
-        if (overlap(c.y, y_bytes(c), workspace, ws_bytes))
-            return fail(NVFP4_E_OVERLAP, "%s: call %d: y overlaps the workspace", fn, i);
+        if (overlap(c.y, yb, workspace, ws_bytes) || overlap(c.aux, rb, workspace, ws_bytes))
+            return fail(NVFP4_E_OVERLAP, "%s: call %d: an output overlaps the workspace", fn, i);
         for (int j = 0; j < ncalls; ++j) {
             const StreamCall &o = calls[j];
-            if (overlap(c.y, y_bytes(c), o.w0, w_bytes(o)) || (o.w1 && overlap(c.y, y_bytes(c), o.w1, w_bytes(o))))
+            const bool w0 = !o.norm;   // a norm's w0 is its delta
+            if ((w0 && overlap(c.y, yb, o.w0, w_bytes(o))) || (o.w1 && overlap(c.y, yb, o.w1, w1_bytes(o))))
                 return fail(NVFP4_E_OVERLAP, "%s: call %d: y overlaps the weight of call %d", fn, i, j);
+            if ((w0 && overlap(c.aux, rb, o.w0, w_bytes(o))) || (o.w1 && overlap(c.aux, rb, o.w1, w1_bytes(o))))
+                return fail(NVFP4_E_OVERLAP, "%s: call %d: residual_out overlaps the weight of call %d", fn, i, j);
+            if (j != i && overlap(c.aux, rb, o.y, y_bytes(o)))
+                return fail(NVFP4_E_OVERLAP, "%s: call %d: residual_out overlaps the y of call %d", fn, i, j);
         }
     }
     return NVFP4_OK;
@@ -227,6 +242,43 @@ int scratch_address(const char *fn, void **out) {
         g_scratch_ptr[dev] = p;
     }
     *out = g_scratch_ptr[dev];
+    return NVFP4_OK;
+}
+
+// Validate a residual add + RMSNorm call of a sequence and append it.
+int add_norm_call(const char *fn, const nvfp4_call &c, std::vector<StreamCall> &out) {
+    const nvfp4_norm *nm = c.norm;
+    if (c.w || c.up || c.x) return fail(NVFP4_E_NULL, "%s: a norm call must have w, up and x NULL", fn);
+    if (!nm->residual || !nm->delta || !nm->weight || !nm->residual_out || !c.y)
+        return fail(NVFP4_E_NULL, "%s: a norm buffer or y is NULL", fn);
+    if (nm->k < 16 || nm->k % 16 != 0 || nm->k > norm_max_k())
+        return fail(NVFP4_E_SHAPE, "%s: k=%lld (need a positive multiple of 16, at most %lld)", fn,
+                    (long long)nm->k, (long long)norm_max_k());
+    if (c.rows < 1 || c.rows > NVFP4_MAX_ROWS)
+        return fail(NVFP4_E_ROWS, "%s: rows=%d outside 1..%d", fn, c.rows, NVFP4_MAX_ROWS);
+    if (c.out_dtype != NVFP4_OUT_BF16) return fail(NVFP4_E_DTYPE, "%s: a norm call writes bf16", fn);
+    if (!(nm->eps >= 0.0f) || nm->eps > 3.0e38f) return fail(NVFP4_E_SHAPE, "%s: eps must be finite and >= 0", fn);
+    for (const void *p : {nm->residual, nm->delta, nm->weight, (const void *)nm->residual_out, (const void *)c.y})
+        if (!aligned(p, 16)) return fail(NVFP4_E_ALIGN, "%s: every norm buffer must be 16-byte aligned", fn);
+    const size_t rb = (size_t)c.rows * nm->k * 2, wb = (size_t)nm->k * 2;
+    if (nm->residual_out != nm->residual && overlap(nm->residual_out, rb, nm->residual, rb))
+        return fail(NVFP4_E_OVERLAP, "%s: residual_out overlaps residual without being it", fn);
+    if (overlap(nm->residual_out, rb, nm->delta, rb) || overlap(nm->residual_out, rb, nm->weight, wb))
+        return fail(NVFP4_E_OVERLAP, "%s: residual_out overlaps delta or weight", fn);
+    if (overlap(c.y, rb, nm->residual, rb) || overlap(c.y, rb, nm->delta, rb) || overlap(c.y, rb, nm->weight, wb) ||
+        overlap(c.y, rb, nm->residual_out, rb))
+        return fail(NVFP4_E_OVERLAP, "%s: y overlaps another norm buffer", fn);
+    StreamCall s{};
+    s.plan = make_norm_plan(nm->k, c.rows);
+    s.w0 = nm->delta;
+    s.w1 = nm->weight;
+    s.x = nm->residual;
+    s.y = c.y;
+    s.out_f32 = 0;
+    s.norm = nm->gemma_offset ? 2 : 1;
+    s.aux = nm->residual_out;
+    s.eps = nm->eps;
+    out.push_back(s);
     return NVFP4_OK;
 }
 
@@ -406,6 +458,10 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls) {
     sc.reserve(ncalls);
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
+        if (c.norm) {
+            sc.push_back(StreamCall{});   // no partial sums; counts as a call of the launch
+            continue;
+        }
         if (!c.w || !valid_shape(c.w->n, c.w->k) || c.rows < 1 || c.rows > NVFP4_MAX_ROWS) continue;
         add_plans(sc, c.w->n, c.w->k, c.rows, c.up != nullptr);
     }
@@ -419,6 +475,12 @@ int nvfp4_sequence_launches(const nvfp4_call *calls, int ncalls) {
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
         if (c.rows < 1 || c.rows > NVFP4_MAX_ROWS) continue;
+        if (c.norm) {
+            StreamCall s{};
+            s.plan = make_norm_plan(16, c.rows);
+            sc.push_back(s);
+            continue;
+        }
         for (int j = 0; j < num_chunks(c.rows); ++j) {
             int r0, nr;
             chunk_of(c.rows, j, r0, nr);
@@ -569,11 +631,16 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
     for (int i = 0; i < ncalls; ++i) {
         const nvfp4_call &c = calls[i];
         snprintf(name, sizeof name, "%s call %d", fn, i);
+        first[i] = (int)sc.size();
+        if (c.norm) {
+            int st = add_norm_call(name, c, sc);
+            if (st) return st;
+            continue;
+        }
         int st = check_call(name, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
         if (st) return st;
         st = check_self_overlap(name, c.w, c.x, c.rows, c.y, c.out_dtype);
         if (st) return st;
-        first[i] = (int)sc.size();
         add_calls(sc, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
     }
     first[ncalls] = (int)sc.size();

@@ -173,7 +173,17 @@ struct StreamCall {
     const void *w0, *w1, *x;
     void *y;
     int out_f32;
+    // a residual add + RMSNorm call when norm != 0 (1, or 2 with the Gemma
+    // offset): x = residual, w0 = delta, w1 = weight, y = normalized output,
+    // aux = residual_out; plan.rows rows of plan.k values, no tiles
+    int norm;
+    const void *aux;
+    float eps;
 };
+
+// The plan of a residual add + RMSNorm call of a sequence: rows workgroups,
+// one row each, no tiles and no workspace.
+StreamPlan make_norm_plan(int64_t k, int rows);
 
 StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual);
 size_t stream_lds_bytes(int krows, int waves);

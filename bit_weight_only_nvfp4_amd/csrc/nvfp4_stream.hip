@@ -48,23 +48,38 @@ namespace {
 using namespace core;
 
 // One call of a launch.
+// A residual add + RMSNorm call (kNorm) reuses the fields: x = residual,
+// w0 = delta, w1 = the norm weight (bf16 [k]), y = the normalized output,
+// aux = residual_out, n = k = the row length, eps; it has no tiles (waves 0).
 struct CallDesc {
     const uint8_t *w0;    // packed weight (gate of the pair)
     const uint8_t *w1;    // packed up weight of a pair; w0 otherwise
     const uint16_t *x;    // [rows][k] bf16
     void *y;              // [rows][n]
+    void *aux;            // norm: residual_out
     int n, k, T;
     int G, F, R;          // workgroups taking part, owned strips each, shared strips
-    int max_pieces;
+    union {
+        int max_pieces;   // pieces a shared strip is cut into, at most
+        float eps;        // norm: added to the mean square
+    };
     int waves;            // waves taking part
     int flags;            // kPair | kOutF32 | kReloadX
     int rows;             // the call's rows (the kernel's ROWS may be more: those rows read and write nothing)
 };
-constexpr int kPair = 1, kOutF32 = 2;
+constexpr int kPair = 1, kOutF32 = 2, kNorm = 8, kGemma = 16;
 // x is written by the call before this one in the same launch: the activations
 // of a super-tile fetched before the call started are fetched again.
 constexpr int kReloadX = 4;
-constexpr int kSeqMax = 40;   // calls per launch (the kernel arguments stay below 4 KB)
+constexpr int kSeqMax = 36;
+
+// 16 zero bytes for the dummy loads of a norm call (a packed weight's header
+// holds its own: a norm's buffers may be shorter than a header)
+__device__ __align__(16) uint8_t g_zero16[16];
+
+__device__ __forceinline__ const uint8_t *zero_of(const CallDesc &d) {
+    return (d.flags & kNorm) ? g_zero16 : d.w0 + kHeaderZeroOffset;
+}   // calls per launch (the kernel arguments stay below 4 KB)
 
 struct SeqArgs {
     CallDesc call[kSeqMax];
@@ -520,6 +535,104 @@ __device__ __forceinline__ void wait_release(const SeqArgs &a, int g, unsigned e
     if (polls >= kMaxPolls) lane0_store(a.flags, 1u, lane);
 }
 
+// Residual add + RMSNorm of one row, by every wave of workgroup `row`: v =
+// bf16(residual + delta) is stored as residual_out, then x = bf16(v * inv *
+// w') with inv = 1 / sqrt(mean(v^2) + eps) and w' = w or 1 + w, fp32
+// arithmetic.  The sum of squares takes the order of the stand-alone norm
+// kernel (its thread t of 256 sums chunks of 8 values t, t + 256, ... in
+// order; a butterfly per wave of 64; the 4 waves' sums in order): waves 0-3
+// here are its waves (with fewer waves, each takes several in turn), so the
+// two give the same bits.  Chunks go 4 per thread at a time, all loads in
+// flight together; up to 8192 values the whole row is one such block and v
+// stays in registers, past it the second pass reads v back from residual_out
+// (the thread's own writes, after waiting for them), which is also correct
+// when residual_out is the residual itself.  Every wave waits for its writes
+// before the workgroup goes on: wave 0 then counts the call done.
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+__device__ __forceinline__ void norm_row(const CallDesc &d, int row, int wave, int nwb, int lane, float *s_ss) {
+    const int k = d.n;
+    const uint32_t rb = (uint32_t)k * 2;
+    const size_t row0 = (size_t)row * k;
+    const __amdgpu_buffer_rsrc_t rr = rsrc(d.x + row0, rb);
+    const __amdgpu_buffer_rsrc_t hr = rsrc(reinterpret_cast<const uint16_t *>(d.w0) + row0, rb);
+    const __amdgpu_buffer_rsrc_t wr = rsrc(d.w1, rb);
+    const __amdgpu_buffer_rsrc_t orr = rsrc(static_cast<uint16_t *>(d.aux) + row0, rb);
+    const __amdgpu_buffer_rsrc_t xr = rsrc(static_cast<uint16_t *>(d.y) + row0, rb);
+    constexpr int kBlock = 4 * 256 * 8;   // values per block: 4 chunks of 8 per thread
+    const bool keep = k <= kBlock && nwb >= 4;   // v of the one block stays in registers
+    const bool gemma = d.flags & kGemma;
+    u32x4_t vk[4], wk[4];
+    for (int vw = wave; vw < 4; vw += nwb) {
+        const int t = 64 * vw + lane;
+        float ss = 0.0f;
+        for (int c0 = 0; c0 < k; c0 += kBlock) {   // past the row: loads read 0, stores are dropped
+            u32x4_t rv[4], hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = c0 * 2 + (t + 256 * i) * 16;
+                rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kSC1);
+                hv[i] = __builtin_amdgcn_raw_buffer_load_b128(hr, off, 0, kSC1);
+                if (keep) wk[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = c0 * 2 + (t + 256 * i) * 16;
+                u32x4_t v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = f32_to_bf16_rne(bf_lo(rv[i][e]) + bf_lo(hv[i][e]));
+                    const uint32_t hi = f32_to_bf16_rne(bf_hi(rv[i][e]) + bf_hi(hv[i][e]));
+                    v[e] = lo | (hi << 16);
+                    const float fl = bf_lo(v[e]), fh = bf_hi(v[e]);
+                    ss = __builtin_fmaf(fl, fl, ss);
+                    ss = __builtin_fmaf(fh, fh, ss);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(v, orr, off, 0, kSC1);
+                vk[i] = v;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+        if (lane == 0) s_ss[vw] = ss;
+    }
+    __syncthreads();
+    const float tot = ((s_ss[0] + s_ss[1]) + s_ss[2]) + s_ss[3];
+    const float inv = 1.0f / __builtin_sqrtf(tot / (float)k + d.eps);
+    if (!keep) wait_own_writes();
+    for (int vw = wave; vw < 4; vw += nwb) {
+        const int t = 64 * vw + lane;
+        for (int c0 = 0; c0 < k; c0 += kBlock) {
+            u32x4_t v[4], wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = c0 * 2 + (t + 256 * i) * 16;
+                v[i] = keep ? vk[i] : __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, kSC1);
+                wv[i] = keep ? wk[i] : __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = c0 * 2 + (t + 256 * i) * 16;
+                u32x4_t xv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float wl = bf_lo(wv[i][e]), wh = bf_hi(wv[i][e]);
+                    if (gemma) {
+                        wl += 1.0f;
+                        wh += 1.0f;
+                    }
+                    xv[e] = (uint32_t)f32_to_bf16_rne(bf_lo(v[i][e]) * inv * wl) |
+                            ((uint32_t)f32_to_bf16_rne(bf_hi(v[i][e]) * inv * wh) << 16);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(xv, xr, off, 0, kSC1);
+            }
+        }
+    }
+    wait_own_writes();
+    __syncthreads();
+}
+
 // SEQ: several calls per launch (the cross-call pipeline and the completion
 // counts); without it the launch runs call 0 alone.
 template <int ROWS, bool SEQ>
@@ -560,6 +673,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     // time; from LDS it is a few cycles.  The words are wave-uniform.
     __shared__ CallDesc s_calls[SEQ ? kSeqMax : 1];
     __shared__ unsigned s_fin;   // shared strips this workgroup completes (bits 0, 1)
+    __shared__ float s_ss[4];    // a norm call's sums of squares, by wave of the stand-alone kernel
     constexpr int kDescWords = sizeof(CallDesc) / 4;
     if (SEQ) {
         const uint32_t *src = reinterpret_cast<const uint32_t *>(a.call);
@@ -600,7 +714,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         const bool live = k < ncalls;
         p.d = desc(live ? k : ncalls - 1);
         const CallDesc &d = p.d;
-        p.q = make_geometry(d, live ? g : kMaxWorkgroups);
+        p.q = make_geometry(d, live && !(d.flags & kNorm) ? g : kMaxWorkgroups);
         const Geometry &q = p.q;
         p.nw = sw < d.waves && sw < q.total ? (q.total - sw + d.waves - 1) / d.waves : 0;
         p.fetch = p.nw > 0;
@@ -649,7 +763,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         Cursor c0 = cursor_at(cur.d, cur.q, g, 0);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            load_tile<ROWS, true>(first_item(cur, c0, i, true), cur.d.w0 + kHeaderZeroOffset, lane, b[i]);
+            load_tile<ROWS, true>(first_item(cur, c0, i, true), zero_of(cur.d), lane, b[i]);
     }
     for (int c = 0; c < ncalls; ++c) {
         const CallDesc d = cur.d;
@@ -658,7 +772,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         const bool has_next = SEQ && c + 1 < ncalls;
         const bool pair = d.flags & kPair;
         const int nwc = d.waves;
-        const uint8_t *zero = d.w0 + kHeaderZeroOffset;
+        const uint8_t *zero = zero_of(d);
         const __amdgpu_buffer_rsrc_t xr = x_rsrc(d);
         const __amdgpu_buffer_rsrc_t yr = output_rsrc(d);
         const float sg[2] = {cur.sg[0], cur.sg[1]};
@@ -672,7 +786,10 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         // stream, sets their length (measured 1-2% faster on a decode step; at
         // 4-8 rows, with more arithmetic per byte, 4-6% slower).
         constexpr bool kLateFetch = ROWS <= 2;
-        const bool nreal = !kLateFetch && nxt.fetch && wave != 0;
+        // A workgroup normalizing a row (a norm call) fetches the next call's
+        // first items only after it: its loads would return behind them.
+        const bool norm_here = (d.flags & kNorm) && g < d.rows;
+        const bool nreal = !kLateFetch && nxt.fetch && wave != 0 && !norm_here;
         const Cursor nc0 = cursor_at(nxt.d, nxt.q, g, 0);
 
         int pub[2] = {0, 0};   // pieces of shared strips fs, fs + 1 stored here
@@ -747,6 +864,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
         }
+        if (norm_here) norm_row(d, g, wave, nwb, lane, s_ss);
         // Pieces of shared strips: wave 0 counts them; where this workgroup's
         // count completes a strip, it is summed either by wave 0 alone or by
         // every wave, some rows each, into LDS (`red`, free once wave 0 has
@@ -807,7 +925,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
         if (wave == 0 && has_next) released = arrive_call(a, g, (unsigned)(c + 1), lane);
         if (has_next) {
             if (kLateFetch) __syncthreads();   // wave 0 has counted the call done
-            if ((kLateFetch || wave == 0) && nxt.fetch) {
+            if ((kLateFetch || wave == 0 || norm_here) && nxt.fetch) {
                 // wave 0's writes are complete: its loads in flight delay only its polls
                 Cursor nc = nc0;
 #pragma unroll
@@ -891,6 +1009,28 @@ bool cooperative_ok() {
         state.store(s, std::memory_order_release);
     }
     return s == 1;
+}
+
+StreamPlan make_norm_plan(int64_t k, int rows) {
+    StreamPlan pl{};
+    pl.n = k;
+    pl.k = k;
+    pl.rows = rows;
+    // the kernel of the row chunks a projection of as many rows runs as, so
+    // that the norm shares their launch
+    const int chunks = (rows + kKernelMaxRows - 1) / kKernelMaxRows;
+    pl.krows = kernel_rows((rows + chunks - 1) / chunks);
+    pl.nmat = 1;
+    pl.strips = 0;
+    pl.supers = 1;
+    pl.G = rows;      // workgroup r normalizes row r
+    pl.F = 0;
+    pl.R = 0;
+    pl.waves = 0;     // no tiles
+    pl.max_pieces = 1;
+    pl.partial_bytes = 0;
+    pl.lds_bytes = stream_lds_bytes(pl.krows, 1);
+    return pl;
 }
 
 StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
@@ -1014,10 +1154,19 @@ hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace,
             d.waves = pl.waves;
             d.flags = (pl.nmat == 2 ? kPair : 0) | (sc.out_f32 ? kOutF32 : 0);
             d.rows = pl.rows;
+            d.aux = nullptr;
+            if (sc.norm) {
+                d.flags = kNorm | (sc.norm == 2 ? kGemma : 0);
+                d.aux = const_cast<void *>(sc.aux);
+                d.eps = sc.eps;
+            }
             if (i > i0) {
                 const StreamCall &p = calls[i - 1];
                 const size_t ybytes = (size_t)p.plan.rows * p.plan.n * (p.out_f32 ? 4 : 2);
-                if (ranges_overlap(sc.x, (size_t)pl.rows * pl.k * 2, p.y, ybytes)) d.flags |= kReloadX;
+                const size_t xbytes = (size_t)pl.rows * pl.k * 2;
+                if (ranges_overlap(sc.x, xbytes, p.y, ybytes) ||
+                    (p.norm && ranges_overlap(sc.x, xbytes, p.aux, (size_t)p.plan.rows * p.plan.k * 2)))
+                    d.flags |= kReloadX;
             }
             if (pl.G > G) G = pl.G;
             if (pl.waves > waves) waves = pl.waves;

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 #define NVFP4_LAYOUT_MAGIC 0x34465056u /* "VPF4" */
 #define NVFP4_LAYOUT_VERSION 3u
 #define NVFP4_MAX_ROWS 128
@@ -195,7 +195,26 @@ int nvfp4_gemv_dual_silu(const nvfp4_weight *gate, const nvfp4_weight *up, const
                          int rows, void *y, int out_dtype, void *workspace,
                          size_t workspace_bytes, void *stream);
 
-/* One projection (up == NULL) or gate/up pair (up != NULL) of a sequence. */
+/* Residual add + RMSNorm inside a sequence (the blueprint page's
+ * norm::residual_add_rms_norm between a decoder's projections): the same
+ * operation as nvfp4_residual_rmsnorm, run by the sequence's own launch between
+ * two of its calls instead of as a launch of its own. */
+typedef struct nvfp4_norm {
+    const void *residual;    /* device bf16 [rows][k], 16-byte aligned                   */
+    const void *delta;       /* device bf16 [rows][k], 16-byte aligned                   */
+    const void *weight;      /* device bf16 [k], 16-byte aligned                         */
+    void *residual_out;      /* device bf16 [rows][k], 16-byte aligned; may be residual  */
+    int64_t k;               /* positive multiple of 16, at most 65536                   */
+    float eps;               /* finite, >= 0                                             */
+    int gemma_offset;        /* nonzero: w' = 1 + weight                                 */
+} nvfp4_norm;
+
+/* One call of a sequence: a projection (norm == NULL, up == NULL), a gate/up
+ * pair (norm == NULL, up != NULL), or a residual add + RMSNorm (norm != NULL;
+ * then w, up and x must be NULL, y receives the normalized rows -- bf16
+ * [rows][norm->k], 16-byte aligned, out_dtype NVFP4_OUT_BF16 -- and a later
+ * call may take y as its x and norm->residual_out as a later norm's
+ * residual). */
 typedef struct nvfp4_call {
     const nvfp4_weight *w;   /* the projection's weight; the gate weight of a pair */
     const nvfp4_weight *up;  /* NULL, or the pair's up weight (same n, k as w)     */
@@ -203,6 +222,7 @@ typedef struct nvfp4_call {
     void *y;                 /* device [rows][n], bf16 or fp32 per out_dtype       */
     int rows;                /* 1..NVFP4_MAX_ROWS                                  */
     int out_dtype;           /* NVFP4_OUT_BF16 or NVFP4_OUT_F32                    */
+    const nvfp4_norm *norm;  /* NULL, or the residual add + RMSNorm this call is   */
 } nvfp4_call;
 
 /* Byte offset, in a projection workspace, of the uint32 wait flag: a launch
@@ -223,12 +243,17 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
  * computing exactly what nvfp4_gemv / nvfp4_gemv_dual_silu would (bit for
  * bit), sharing the one workspace.  The pages drive a decode step of several
  * hundred launches as one captured graph (kern README, "decode" programs; the
- * NVFP4 blueprint's 755 launches per step); here runs of up to 40 consecutive
+ * NVFP4 blueprint's 755 launches per step); here runs of up to 36 consecutive
  * calls with the same row count share one cooperative launch whose
  * workgroups finish each call before any starts computing the next (the next
  * call's first weight tiles are fetched meanwhile), so a call may read the y
  * of an earlier call as its x.  No call's y may overlap any call's weight,
  * its own x or the workspace (NVFP4_E_OVERLAP).
+ * Residual add + RMSNorm calls (norm != NULL) run inside the same launch, one
+ * workgroup per row, with the arithmetic and summation order of
+ * nvfp4_residual_rmsnorm: both outputs are bit-identical to it.  A norm's
+ * delta may be an earlier call's y; its outputs may not overlap any weight or
+ * the workspace, and its residual_out no other call's y.
  * events: NULL, or 2*ncalls hipEvent_t handles (entries may be NULL); with
  * events every call gets a launch of its own, events[2i] is recorded on
  * `stream` right before call i and events[2i+1] right after it, for

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(nv):
 
 
 def test_version_and_strerror(nv):
-    assert nv.nvfp4_abi_version() == 1
+    assert nv.nvfp4_abi_version() == nv.NVFP4_ABI_VERSION == 2
     for code in nv.STATUS:
         assert nv.nvfp4_strerror(code) != "unknown status"
     assert nv.nvfp4_strerror(-99) == "unknown status"
@@ -207,6 +207,117 @@ def test_sequence_argument_errors(nv):
     assert 2 <= L.nvfp4_sequence_launches(arr, 1) <= 3
     arr[0].rows = 1
     assert L.nvfp4_gemv_sequence(None, 3, None, 0, None, None) == E["NVFP4_E_NULL"]
+
+
+def _norm_sequence(nv, rows=1, k=512):
+    """[residual add + RMSNorm, projection reading its x, projection writing
+    the next norm's delta, residual add + RMSNorm]: the four calls of half a
+    decode layer, at fake addresses."""
+    keep = []
+    w = _weight(nv, 256, k)                                   # [FAKE, FAKE + 73984)
+    wo = _weight(nv, k, 256, data=FAKE + 0x100000)
+    keep += [w, wo]
+    norms = []
+    for i in range(2):
+        nm = nv.nvfp4_norm()
+        nm.residual = nm.residual_out = XF + 0x400000         # updated in place by both
+        nm.delta = YF + 0x300000                              # the second: written by call 2
+        nm.weight = FAKE + 0x800000 + i * 0x10000
+        nm.k, nm.eps, nm.gemma_offset = k, 1e-6, i
+        norms.append(nm)
+    arr = (nv.nvfp4_call * 4)()
+    for c, nm in ((arr[0], norms[0]), (arr[3], norms[1])):
+        c.norm = ctypes.pointer(nm)
+        c.y, c.rows, c.out_dtype = YF + 0x500000, rows, 0
+    arr[1].w, arr[1].x, arr[1].y = ctypes.pointer(w), YF + 0x500000, YF + 0x600000
+    arr[2].w, arr[2].x, arr[2].y = ctypes.pointer(wo), YF + 0x600000, YF + 0x300000
+    for c in (arr[1], arr[2]):
+        c.rows, c.out_dtype = rows, 0
+    return arr, norms, keep
+
+
+def test_sequence_norm_call_errors(nv):
+    """Residual add + RMSNorm calls inside a sequence: the checks of
+    nvfp4_residual_rmsnorm, plus the sequence's own (a norm's delta may be an
+    earlier call's output; its outputs may not overlap any weight)."""
+    E = {v: k for k, v in nv.STATUS.items()}
+    L = nv.lib()
+    arr, norms, keep = _norm_sequence(nv)
+    need = L.nvfp4_sequence_workspace_bytes(arr, 4)
+    assert need == 65 * 1024 and L.nvfp4_sequence_workspace_bytes(arr, 1) == 0
+    assert 1 <= L.nvfp4_sequence_launches(arr, 4) <= 4
+
+    def run():
+        return L.nvfp4_gemv_sequence(arr, 4, WF, need, None, None)
+
+    def expect(status, text):
+        assert run() == E[status], nv.nvfp4_last_error()
+        assert text in nv.nvfp4_last_error(), nv.nvfp4_last_error()
+
+    if torch.cuda.device_count() == 0:
+        assert run() == E["NVFP4_E_DEVICE"]      # every check passed
+    arr[0].w = arr[1].w
+    expect("NVFP4_E_NULL", "call 0")
+    arr[0].w = None
+    norms[1].residual = None
+    expect("NVFP4_E_NULL", "call 3")
+    norms[1].residual = XF + 0x400000
+    norms[0].k = 24
+    expect("NVFP4_E_SHAPE", "call 0")
+    norms[0].k = 65536 + 16
+    expect("NVFP4_E_SHAPE", "call 0")
+    norms[0].k = 512
+    arr[3].rows = 129
+    expect("NVFP4_E_ROWS", "call 3")
+    arr[3].rows = 1
+    arr[3].out_dtype = 1
+    expect("NVFP4_E_DTYPE", "call 3")
+    arr[3].out_dtype = 0
+    norms[1].eps = float("nan")
+    expect("NVFP4_E_SHAPE", "call 3")
+    norms[1].eps = 1e-6
+    norms[0].delta = YF + 0x300000 + 8
+    expect("NVFP4_E_ALIGN", "call 0")
+    norms[0].delta = YF + 0x300000
+    norms[0].residual_out = XF + 0x400000 + 512              # partly over its residual
+    expect("NVFP4_E_OVERLAP", "call 0")
+    norms[0].residual_out = YF + 0x300000                    # over its delta
+    expect("NVFP4_E_OVERLAP", "call 0")
+    norms[0].residual_out = FAKE + 0x100000 + 4096           # over call 2's weight
+    expect("NVFP4_E_OVERLAP", "call 2")
+    norms[0].residual_out = YF + 0x600000                    # over call 1's y
+    expect("NVFP4_E_OVERLAP", "call 1")
+    norms[0].residual_out = FAKE + 0x800000 + 0x10000        # over the other norm's weight
+    expect("NVFP4_E_OVERLAP", "call 3")
+    norms[0].residual_out = XF + 0x400000
+    arr[3].y = FAKE + 0x800000                               # its y over the first norm's weight
+    expect("NVFP4_E_OVERLAP", "weight of call 0")
+    arr[3].y = XF + 0x400000                                 # its y over its residual
+    expect("NVFP4_E_OVERLAP", "call 3")
+    arr[3].y = YF + 0x500000
+    arr[2].y = FAKE + 0x800000 + 0x10000                     # a projection's y over a norm weight
+    expect("NVFP4_E_OVERLAP", "weight of call 3")
+    arr[2].y = YF + 0x300000
+    arr[2].y = WF + 64                                       # over the workspace
+    expect("NVFP4_E_OVERLAP", "workspace")
+    arr[2].y = YF + 0x300000
+    if torch.cuda.device_count() == 0:
+        assert run() == E["NVFP4_E_DEVICE"]
+    del keep
+
+
+def test_sequence_norm_launch_grouping(nv):
+    """A norm call runs in the launch of the projections of its row count
+    (rows past 16: the kernel of their row chunks)."""
+    L = nv.lib()
+    for rows in (1, 5, 8, 24, 40):
+        arr, norms, keep = _norm_sequence(nv, rows=rows)
+        alone = L.nvfp4_sequence_launches(arr, 1)
+        assert alone == 1
+        chunks = -(-rows // 16)
+        # per call: one launch per row chunk of a projection, one for a norm
+        assert L.nvfp4_sequence_launches(arr, 4) <= 2 * chunks + 2
+        del keep
 
 
 def _dense(nv, W=FAKE, n=256, k=512, x=XF, rows=1, y=YF, dtype=0):
