@@ -44,6 +44,7 @@ EXPORTS = (
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
     "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16", "nvfp4_residual_rmsnorm",
     "nvfp4_mxfp4_gemv", "nvfp4_w8g32_gemv", "nvfp4_read_ceiling", "nvfp4_gemv_noalloc",
+    "nvfp4_sequence_plan_bytes", "nvfp4_sequence_plan", "nvfp4_sequence_plan_launch",
 )
 
 
@@ -129,6 +130,9 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_int),
             "nvfp4_read_ceiling": ([vp, sz, vp, vp], ctypes.c_int),
             "nvfp4_gemv_noalloc": ([wp, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
+            "nvfp4_sequence_plan_bytes": ([ctypes.POINTER(nvfp4_call), ctypes.c_int], sz),
+            "nvfp4_sequence_plan": ([ctypes.POINTER(nvfp4_call), ctypes.c_int, vp, sz], ctypes.c_int),
+            "nvfp4_sequence_plan_launch": ([vp, vp, sz, vp], ctypes.c_int),
         }
         for name, (argt, rest) in sig.items():
             f = getattr(L, name)
@@ -470,6 +474,10 @@ class Sequence:
             w, up, x, y = item
             if x.dtype != torch.bfloat16 or y.dtype not in _OUT:
                 raise TypeError("call %d: x must be bfloat16 and y bfloat16 or float32" % i)
+            if x.dim() != 2 or x.shape[1] != w.k or tuple(y.shape) != (x.shape[0], w.n):
+                raise ValueError("call %d: x must be [rows, %d] and y [rows, %d]" % (i, w.k, w.n))
+            if not (x.is_contiguous() and y.is_contiguous()):
+                raise ValueError("call %d: x and y must be contiguous" % i)
             c.w = ctypes.pointer(w.desc)
             c.up = ctypes.pointer(up.desc) if up is not None else None
             c.x = x.data_ptr()
@@ -481,6 +489,14 @@ class Sequence:
         self.workspace_bytes = int(lib().nvfp4_sequence_workspace_bytes(self._arr, self.n))
         # kernel launches of one launch() without events
         self.launches = int(lib().nvfp4_sequence_launches(self._arr, self.n))
+        # validated once: launch() enqueues the plan (nvfp4_sequence_plan_launch)
+        self._plan = None
+        if self.n:
+            nb = int(lib().nvfp4_sequence_plan_bytes(self._arr, self.n))   # 0: a call is invalid
+            self._plan = (ctypes.c_uint64 * (-(-nb // 8) + 2))()
+            base = ctypes.addressof(self._plan)
+            self._plan_ptr = base + (-base % 16)
+            _check("nvfp4_sequence_plan", lib().nvfp4_sequence_plan(self._arr, self.n, self._plan_ptr, nb))
 
     def launch(self, workspace: torch.Tensor | None = None, events=None, stream=None):
         """Enqueue every call on ``stream`` (default: the current stream).
@@ -495,9 +511,12 @@ class Sequence:
                 raise ValueError("events must hold 2 entries per call")
             ev = (ctypes.c_void_p * (2 * self.n))(*[e if e else None for e in events])
         st = stream if stream is not None else _stream(dev)
-        _check("nvfp4_gemv_sequence",
-               lib().nvfp4_gemv_sequence(self._arr, self.n, _ptr(workspace),
-                                         0 if workspace is None else workspace.numel(), ev, st))
+        wsb = 0 if workspace is None else workspace.numel()
+        if ev is None and self._plan is not None:
+            _check("nvfp4_sequence_plan_launch",
+                   lib().nvfp4_sequence_plan_launch(self._plan_ptr, _ptr(workspace), wsb, st))
+            return
+        _check("nvfp4_gemv_sequence", lib().nvfp4_gemv_sequence(self._arr, self.n, _ptr(workspace), wsb, ev, st))
 
 
 def nvfp4_sequence_workspace_bytes(calls) -> int:

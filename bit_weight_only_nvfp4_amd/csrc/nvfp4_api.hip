@@ -282,6 +282,63 @@ int add_norm_call(const char *fn, const nvfp4_call &c, std::vector<StreamCall> &
     return NVFP4_OK;
 }
 
+// Validate every call of a sequence and turn it into the calls one launch
+// runs (a projection of more than kKernelMaxRows rows: one per row chunk);
+// call i runs as out[first[i] .. first[i + 1]).
+int build_sequence(const char *fn, const nvfp4_call *calls, int ncalls, std::vector<StreamCall> &out,
+                   std::vector<int> &first) {
+    if (!calls) return fail(NVFP4_E_NULL, "%s: calls is NULL", fn);
+    char name[64];
+    out.clear();
+    first.assign((size_t)ncalls + 1, 0);
+    for (int i = 0; i < ncalls; ++i) {
+        const nvfp4_call &c = calls[i];
+        snprintf(name, sizeof name, "%s call %d", fn, i);
+        first[i] = (int)out.size();
+        if (c.norm) {
+            int st = add_norm_call(name, c, out);
+            if (st) return st;
+            continue;
+        }
+        int st = check_call(name, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
+        if (st) return st;
+        st = check_self_overlap(name, c.w, c.x, c.rows, c.y, c.out_dtype);
+        if (st) return st;
+        add_calls(out, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
+    }
+    first[ncalls] = (int)out.size();
+    return NVFP4_OK;
+}
+
+// A sequence plan (nvfp4_sequence_plan): header, launch records, then the
+// byte ranges of every output (checked against the workspace at launch).
+constexpr uint32_t kPlanMagic = 0x50535650;   // "PVSP"
+struct PlanHeader {
+    uint32_t magic, abi;
+    size_t bytes, workspace_bytes;
+    int device, nrec, nout, pad;
+};
+struct OutRange {
+    uintptr_t p;
+    size_t n;
+};
+struct PlanLayout {
+    size_t rec_off, out_off, total;
+};
+size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
+PlanLayout plan_layout_of(int nrec, int nout) {
+    PlanLayout L;
+    L.rec_off = round16(sizeof(PlanHeader));
+    L.out_off = round16(L.rec_off + (size_t)nrec * launch_rec_bytes());
+    L.total = L.out_off + (size_t)nout * sizeof(OutRange);
+    return L;
+}
+PlanLayout plan_layout(const std::vector<StreamCall> &sc) {
+    int nout = 0;
+    for (const StreamCall &c : sc) nout += c.norm ? 2 : 1;
+    return plan_layout_of(sequence_launches(sc.data(), (int)sc.size()), nout);
+}
+
 int run_one(const char *fn, const nvfp4_weight *w, const nvfp4_weight *up, const void *x, int rows, void *y,
             int out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_call(fn, w, up, x, rows, y, out_dtype);
@@ -624,28 +681,12 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
     static const char *fn = "nvfp4_gemv_sequence";
     if (ncalls < 0) return fail(NVFP4_E_SHAPE, "%s: ncalls=%d", fn, ncalls);
     if (ncalls == 0) return ok();
-    if (!calls) return fail(NVFP4_E_NULL, "%s: calls is NULL", fn);
-    char name[64];
     std::vector<StreamCall> sc;
-    std::vector<int> first((size_t)ncalls + 1);   // call i runs as sc[first[i] .. first[i + 1])
-    for (int i = 0; i < ncalls; ++i) {
-        const nvfp4_call &c = calls[i];
-        snprintf(name, sizeof name, "%s call %d", fn, i);
-        first[i] = (int)sc.size();
-        if (c.norm) {
-            int st = add_norm_call(name, c, sc);
-            if (st) return st;
-            continue;
-        }
-        int st = check_call(name, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
-        if (st) return st;
-        st = check_self_overlap(name, c.w, c.x, c.rows, c.y, c.out_dtype);
-        if (st) return st;
-        add_calls(sc, c.w, c.up, c.x, c.rows, c.y, c.out_dtype);
-    }
-    first[ncalls] = (int)sc.size();
+    std::vector<int> first;   // call i runs as sc[first[i] .. first[i + 1])
+    int st = build_sequence(fn, calls, ncalls, sc, first);
+    if (st) return st;
     const int nsc = (int)sc.size();
-    int st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(sc.data(), nsc));
+    st = check_workspace(fn, workspace, workspace_bytes, sequence_workspace_bytes(sc.data(), nsc));
     if (st) return st;
     st = check_overlaps(fn, sc.data(), nsc, workspace, workspace_bytes);
     if (st) return st;
@@ -670,6 +711,76 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
         }
     }
     return ok();
+}
+
+size_t nvfp4_sequence_plan_bytes(const nvfp4_call *calls, int ncalls) {
+    static const char *fn = "nvfp4_sequence_plan_bytes";
+    if (ncalls <= 0 || !calls) return 0;
+    std::vector<StreamCall> sc;
+    std::vector<int> first;
+    if (build_sequence(fn, calls, ncalls, sc, first)) return 0;
+    return plan_layout(sc).total;
+}
+
+int nvfp4_sequence_plan(const nvfp4_call *calls, int ncalls, void *plan, size_t plan_bytes) {
+    static const char *fn = "nvfp4_sequence_plan";
+    if (ncalls <= 0) return fail(NVFP4_E_SHAPE, "%s: ncalls=%d (need at least one call)", fn, ncalls);
+    if (!plan) return fail(NVFP4_E_NULL, "%s: plan is NULL", fn);
+    if (!aligned(plan, 16)) return fail(NVFP4_E_ALIGN, "%s: plan is not 16-byte aligned", fn);
+    std::vector<StreamCall> sc;
+    std::vector<int> first;
+    int st = build_sequence(fn, calls, ncalls, sc, first);
+    if (st) return st;
+    const int nsc = (int)sc.size();
+    // the plan's outputs against any workspace are checked at launch; here
+    // every other overlap rule (no workspace yet)
+    st = check_overlaps(fn, sc.data(), nsc, nullptr, 0);
+    if (st) return st;
+    const PlanLayout L = plan_layout(sc);
+    if (plan_bytes < L.total)
+        return fail(NVFP4_E_WORKSPACE, "%s: plan has %zu bytes, %zu needed", fn, plan_bytes, L.total);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    uint8_t *base = static_cast<uint8_t *>(plan);
+    PlanHeader h{};
+    h.magic = kPlanMagic;
+    h.abi = NVFP4_ABI_VERSION;
+    h.bytes = L.total;
+    h.workspace_bytes = sequence_workspace_bytes(sc.data(), nsc);
+    h.device = dev;
+    h.nrec = build_launches(sc.data(), nsc, base + L.rec_off);
+    h.nout = 0;
+    OutRange *outs = reinterpret_cast<OutRange *>(base + L.out_off);
+    for (const StreamCall &c : sc) {
+        outs[h.nout++] = OutRange{reinterpret_cast<uintptr_t>(c.y), y_bytes(c)};
+        if (c.norm) outs[h.nout++] = OutRange{reinterpret_cast<uintptr_t>(c.aux), x_bytes(c)};
+    }
+    *reinterpret_cast<PlanHeader *>(base) = h;
+    return ok();
+}
+
+int nvfp4_sequence_plan_launch(const void *plan, void *workspace, size_t workspace_bytes, void *stream) {
+    static const char *fn = "nvfp4_sequence_plan_launch";
+    if (!plan) return fail(NVFP4_E_NULL, "%s: plan is NULL", fn);
+    if (!aligned(plan, 16)) return fail(NVFP4_E_ALIGN, "%s: plan is not 16-byte aligned", fn);
+    const uint8_t *base = static_cast<const uint8_t *>(plan);
+    const PlanHeader &h = *reinterpret_cast<const PlanHeader *>(base);
+    if (h.magic != kPlanMagic || h.abi != NVFP4_ABI_VERSION)
+        return fail(NVFP4_E_LAYOUT, "%s: not a plan written by nvfp4_sequence_plan of this library", fn);
+    int st = check_workspace(fn, workspace, workspace_bytes, h.workspace_bytes);
+    if (st) return st;
+    const PlanLayout L = plan_layout_of(h.nrec, h.nout);
+    const OutRange *outs = reinterpret_cast<const OutRange *>(base + L.out_off);
+    for (int i = 0; i < h.nout; ++i)
+        if (overlap(reinterpret_cast<const void *>(outs[i].p), outs[i].n, workspace, workspace_bytes))
+            return fail(NVFP4_E_OVERLAP, "%s: an output of the plan overlaps the workspace", fn);
+    st = check_device(fn);
+    if (st) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != h.device)
+        return fail(NVFP4_E_DEVICE, "%s: the plan was made on device %d, the current device is %d", fn, h.device,
+                    dev);
+    return hip_status(fn, launch_recs(base + L.rec_off, h.nrec, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

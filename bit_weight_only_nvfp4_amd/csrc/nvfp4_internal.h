@@ -197,6 +197,12 @@ bool cooperative_ok();
 hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace, hipStream_t stream);
 // Launches launch_sequence makes for these calls.
 int sequence_launches(const StreamCall *calls, int ncalls);
+// The same in two steps: build_launches writes the launches of these calls
+// (sequence_launches of them, launch_rec_bytes() each, 8-byte aligned) into
+// recs and returns their count; launch_recs enqueues them with a workspace.
+size_t launch_rec_bytes();
+int build_launches(const StreamCall *calls, int ncalls, void *recs);
+hipError_t launch_recs(const void *recs, int nrec, void *workspace, hipStream_t stream);
 
 // Dense bf16 projection (rows <= kKernelMaxRows): y[r][j] = sum_k W[j][k] x[r][k].
 hipError_t launch_dense(const void *w, int64_t n, int64_t k, const void *x, int rows, void *y, int out_f32,

@@ -40,6 +40,7 @@
 // [g*RT/G, (g+1)*RT/G), cut at strip boundaries into pieces.
 #include <atomic>
 #include <type_traits>
+#include <vector>
 
 #include "nvfp4_core.h"
 
@@ -1123,18 +1124,26 @@ int sequence_launches(const StreamCall *calls, int ncalls) {
     return n;
 }
 
-hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace, hipStream_t stream) {
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
+// One launch of a sequence, complete but for the workspace pointers.
+struct LaunchRec {
+    int krows, waves;
+    size_t lds;
+    SeqArgs args;
+};
+
+size_t launch_rec_bytes() { return sizeof(LaunchRec); }
+
+int build_launches(const StreamCall *calls, int ncalls, void *recs) {
+    LaunchRec *out = static_cast<LaunchRec *>(recs);
     const bool shared = ncalls > 1 && cooperative_ok();
-    for (int i0 = 0; i0 < ncalls;) {
+    int nrec = 0;
+    for (int i0 = 0; i0 < ncalls; ++nrec) {
         const int i1 = launch_end(calls, ncalls, i0, shared);
+        LaunchRec &r = out[nrec];
+        r = LaunchRec{};
         const int krows = calls[i0].plan.krows;
-        SeqArgs a{};
+        SeqArgs &a = r.args;
         a.ncalls = i1 - i0;
-        a.counters = reinterpret_cast<unsigned *>(ws);
-        a.sync = ws ? reinterpret_cast<unsigned *>(ws + kSyncOffset) : nullptr;
-        a.flags = ws ? reinterpret_cast<unsigned *>(ws + kFlagOffset) : nullptr;
-        a.partial = ws ? reinterpret_cast<float *>(ws + kPartialOffset) : nullptr;
         int G = 1, waves = 1;
         for (int i = i0; i < i1; ++i) {
             const StreamCall &sc = calls[i];
@@ -1172,11 +1181,33 @@ hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace,
             if (pl.waves > waves) waves = pl.waves;
         }
         a.G = G;
-        hipError_t e = launch_args(krows, a, waves, stream_lds_bytes(krows, waves), stream);
-        if (e != hipSuccess) return e;
+        r.krows = krows;
+        r.waves = waves;
+        r.lds = stream_lds_bytes(krows, waves);
         i0 = i1;
     }
+    return nrec;
+}
+
+hipError_t launch_recs(const void *recs, int nrec, void *workspace, hipStream_t stream) {
+    const LaunchRec *in = static_cast<const LaunchRec *>(recs);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    for (int i = 0; i < nrec; ++i) {
+        SeqArgs a = in[i].args;
+        a.counters = reinterpret_cast<unsigned *>(ws);
+        a.sync = ws ? reinterpret_cast<unsigned *>(ws + kSyncOffset) : nullptr;
+        a.flags = ws ? reinterpret_cast<unsigned *>(ws + kFlagOffset) : nullptr;
+        a.partial = ws ? reinterpret_cast<float *>(ws + kPartialOffset) : nullptr;
+        hipError_t e = launch_args(in[i].krows, a, in[i].waves, in[i].lds, stream);
+        if (e != hipSuccess) return e;
+    }
     return hipSuccess;
+}
+
+hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace, hipStream_t stream) {
+    std::vector<LaunchRec> recs((size_t)sequence_launches(calls, ncalls));
+    const int nrec = build_launches(calls, ncalls, recs.data());
+    return launch_recs(recs.data(), nrec, workspace, stream);
 }
 
 }  // namespace nvfp4

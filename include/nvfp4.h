@@ -261,6 +261,24 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
                         void *const *events, void *stream);
 
+/* A call list validated once and kept, for a decode step launched many times
+ * (the pages capture a step once and replay it: kern README, "Layout").
+ * nvfp4_sequence_plan_bytes: host bytes of the plan of these calls, 0 if a
+ * call is invalid (nvfp4_last_error says which).  nvfp4_sequence_plan:
+ * validates the calls exactly as nvfp4_gemv_sequence does (but for the
+ * workspace) and writes the plan -- the kernel launches with every argument
+ * but the workspace -- into `plan`: caller-owned host memory, 16-byte aligned,
+ * at least nvfp4_sequence_plan_bytes long (NVFP4_E_WORKSPACE otherwise).  The
+ * plan holds the calls' device pointers: their buffers must stay allocated
+ * and the plan unchanged while it is used, on the device current when it was
+ * made.  nvfp4_sequence_plan_launch: enqueues the plan's launches on `stream`
+ * -- the same work as nvfp4_gemv_sequence with no events, bit for bit --
+ * after checking only the plan's header, the workspace (size, alignment, no
+ * overlap with any output) and the device: O(ncalls) host work. */
+size_t nvfp4_sequence_plan_bytes(const nvfp4_call *calls, int ncalls);
+int nvfp4_sequence_plan(const nvfp4_call *calls, int ncalls, void *plan, size_t plan_bytes);
+int nvfp4_sequence_plan_launch(const void *plan, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Dense bf16 projection, for the projection whose weights stay bf16: the lm
  * head (the Qwen3.8-27B-NVFP4 blueprint page, "Precision" table, bf16 x bf16
  * nodes; its kernel table names the step gemv::dense_gemv_bf16).

@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 double   nvo_e2m1_value(unsigned code);
-unsigned nvo_e2m1_encode(float v);
+unsigned nvo_e2m1_encode(float v);   /* v not NaN (the quantizer rejects non-finite weights first) */
 float    nvo_e4m3_value(unsigned byte);
 unsigned nvo_e4m3_encode(float v);
 double   nvo_bf16_value(uint16_t h);

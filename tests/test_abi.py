@@ -320,6 +320,59 @@ def test_sequence_norm_launch_grouping(nv):
         del keep
 
 
+def test_sequence_plan_errors(nv):
+    """nvfp4_sequence_plan validates once what nvfp4_gemv_sequence validates
+    each time; nvfp4_sequence_plan_launch checks the header, the workspace
+    and the device only."""
+    E = {v: k for k, v in nv.STATUS.items()}
+    L = nv.lib()
+    arr, norms, keep = _norm_sequence(nv)
+    nb = L.nvfp4_sequence_plan_bytes(arr, 4)
+    assert nb > 0 and nb % 8 == 0
+    buf = (ctypes.c_uint64 * (nb // 8 + 4))()
+    base = ctypes.addressof(buf)
+    plan = base + (-base % 16)
+    assert L.nvfp4_sequence_plan(arr, 4, plan, nb - 8) == E["NVFP4_E_WORKSPACE"]
+    assert L.nvfp4_sequence_plan(arr, 4, plan + 8, nb) == E["NVFP4_E_ALIGN"]
+    assert L.nvfp4_sequence_plan(arr, 4, None, nb) == E["NVFP4_E_NULL"]
+    assert L.nvfp4_sequence_plan(arr, 0, plan, nb) == E["NVFP4_E_SHAPE"]
+    assert L.nvfp4_sequence_plan(arr, 4, plan, nb) == 0
+    need = L.nvfp4_sequence_workspace_bytes(arr, 4)
+    assert L.nvfp4_sequence_plan_launch(plan, WF, need - 16, None) == E["NVFP4_E_WORKSPACE"]
+    assert L.nvfp4_sequence_plan_launch(plan, WF + 4, need, None) == E["NVFP4_E_ALIGN"]
+    assert L.nvfp4_sequence_plan_launch(plan, YF + 0x600000 - 64, need, None) == E["NVFP4_E_OVERLAP"]
+    assert L.nvfp4_sequence_plan_launch(plan, XF + 0x400000, need, None) == E["NVFP4_E_OVERLAP"]  # residual_out
+    if torch.cuda.device_count() == 0:
+        assert L.nvfp4_sequence_plan_launch(plan, WF, need, None) == E["NVFP4_E_DEVICE"]
+    assert L.nvfp4_sequence_plan_launch(plan + 16, WF, need, None) == E["NVFP4_E_LAYOUT"]
+    assert L.nvfp4_sequence_plan_launch(None, WF, need, None) == E["NVFP4_E_NULL"]
+    # invalid calls: no size, and the plan call names the call
+    arr[2].rows = 0
+    assert L.nvfp4_sequence_plan_bytes(arr, 4) == 0
+    assert "call 2" in nv.nvfp4_last_error()
+    assert L.nvfp4_sequence_plan(arr, 4, plan, nb) == E["NVFP4_E_ROWS"]
+    arr[2].rows = 1
+    arr[2].y = FAKE + 0x800000                               # over a norm weight: found at plan time
+    assert L.nvfp4_sequence_plan(arr, 4, plan, nb) == E["NVFP4_E_OVERLAP"]
+    arr[2].y = YF + 0x300000
+    # the Python Sequence validates at construction
+    del keep
+
+
+def test_sequence_object_validates_once(nv):
+    w = _weight(nv, 256, 512)
+    x = torch.empty((1, 512), dtype=torch.bfloat16)
+    y = torch.empty((1, 300), dtype=torch.bfloat16)
+    pw = nv.PackedWeight(torch.empty(0, dtype=torch.uint8), w)
+    with pytest.raises(ValueError):
+        nv.Sequence([(pw, None, x, y)])                     # y is not [1, 256]
+    x0 = torch.empty((0, 512), dtype=torch.bfloat16)
+    y0 = torch.empty((0, 256), dtype=torch.bfloat16)
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.Sequence([(pw, None, x0, y0), (pw, None, x0, y0)])
+    assert "call 0" in str(e.value)   # empty tensors: a NULL x
+
+
 def _dense(nv, W=FAKE, n=256, k=512, x=XF, rows=1, y=YF, dtype=0):
     return nv.lib().nvfp4_dense_gemv_bf16(W, n, k, x, rows, y, dtype, None)
 
