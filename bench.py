@@ -56,7 +56,7 @@ HBM_PEAK_GBS = 8000.0
 PAIR_NAME = "gate"
 KERNEL_SOURCES = ("bit_weight_only_nvfp4_amd/csrc/nvfp4_stream.hip", "bit_weight_only_nvfp4_amd/csrc/nvfp4_core.h",
                   "bit_weight_only_nvfp4_amd/csrc/nvfp4_internal.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_rows1_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -86,10 +86,14 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the lm-head, RMSNorm, MXFP4 and W8G32_F16S timings")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LAUNCHES_PER_STEP"),
-                    help="write the rows=1 decode-step kernel's HBM traffic per launch from two rocprofv3 "
-                         "--pmc counter collections (FETCH_SIZE, WRITE_SIZE) of a --copy-calibration run of "
-                         "the 64-layer sweep, then exit")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the decode step alone, for profiling: no stand-alone pair, norm-step, read-ceiling, "
+                         "single-call or format timings (their launches would mix with the step's in a profile)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("RDREQ_CSV", "WRITE_CSV", "LAUNCHES_PER_STEP"),
+                    help="write the decode-step kernels' HBM traffic per launch from two rocprofv3 --pmc counter "
+                         "collections (TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_64B_sum "
+                         "TCC_EA0_RDREQ_32B_sum; WRITE_SIZE) of a --copy-calibration run of the 64-layer sweep, "
+                         "then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (known bytes) to scale PMC byte counters")
     return ap.parse_args()
@@ -417,10 +421,10 @@ def single_calls(nv, torch, dev, workloads, mats, ceil_buf, ncalls=200):
     return out
 
 
-def load_traffic():
-    """HBM bytes per launch of the rows=1 decode-step kernel (64-layer sweep)
-    from the committed PMC summary, or None when it is missing or the kernel
-    source changed since."""
+def load_traffic(rows):
+    """HBM bytes per launch of the decode-step kernel at `rows` (64-layer
+    sweep) from the committed PMC summary, or None when it is missing or the
+    kernel source changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -428,59 +432,53 @@ def load_traffic():
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t.get("by_rows", {}).get(str(rows), {}).get("bytes_per_launch")
 
 
-STEP_KERNEL_TAG = "seq_kernel<1, true>"     # rows=1 shared-launch kernel of the decode step
 COPY_BYTES = 1 << 30                         # --copy-calibration copies this many bytes
 
 
-def summarize_pmc(fetch_csv, write_csv, launches_per_step):
-    """HBM bytes per launch of the rows=1 decode-step kernel from rocprofv3
-    counter collections.  FETCH_SIZE and WRITE_SIZE are reported in KiB per
-    dispatch; each is scaled by what the same counter reads for the 1 GiB
-    device copy of the same run (known bytes)."""
+def summarize_pmc(rdreq_csv, write_csv, launches_per_step):
+    """HBM bytes per launch of the decode-step kernels (seq_kernel<R, true>)
+    from two rocprofv3 counter collections of a --copy-calibration run: read
+    bytes from the L2-to-memory read requests by size (TCC_EA0_RDREQ_128B /
+    _64B / _32B, x 128 / 64 / 32 bytes), write bytes from WRITE_SIZE (KiB).
+    Both are checked against the 1 GiB device copy of the same run (known
+    bytes), and scaled by it.  FETCH_SIZE is not used: its expression counts
+    a 128-byte read request as 64 bytes on this GPU (it reads half the copy's
+    bytes), while the 128-byte request count gives the copy's size exactly."""
     import csv
 
-    def per_kernel(path):
+    def dispatches(path):
         out = {}
         for r in csv.DictReader(open(path)):
-            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return out
+            d = out.setdefault(r["Dispatch_Id"], {"kernel": r["Kernel_Name"]})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+        return list(out.values())
 
-    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
+    rd, wr = dispatches(rdreq_csv), dispatches(write_csv)
 
-    def pick(table, pred):
-        keys = [k for k in table if pred(k)]
-        if not keys:
-            raise SystemExit("no matching kernel in the counter file")
-        vals = [v for k in keys for v in table[k]]
-        return sum(vals) / len(vals), len(vals), keys[0]
+    def read_bytes(d):
+        return (128 * d["TCC_EA0_RDREQ_128B_sum"] + 64 * d["TCC_EA0_RDREQ_64B_sum"]
+                + 32 * d["TCC_EA0_RDREQ_32B_sum"])
 
-    pair = lambda k: STEP_KERNEL_TAG in k
-    # the 1 GiB device copy of --copy-calibration (the runtime's copy kernel)
-    copy_f = max(v for k, vals in f.items() if "copyBuffer" in k for v in vals)
-    copy_w = max(v for k, vals in w.items() if "copyBuffer" in k for v in vals)
-    fetch_factor = COPY_BYTES / (copy_f * 1024.0)
-    write_factor = COPY_BYTES / (copy_w * 1024.0)
-    pf, n_f, name = pick(f, pair)
-    pw, n_w, _ = pick(w, pair)
-    fetch_bytes = pf * 1024.0 * fetch_factor
-    write_bytes = pw * 1024.0 * write_factor
-    t = {
-        "kernel": name,
-        "kernel_source_hash": kernel_source_hash(),
-        "dispatches": [n_f, n_w],
-        "fetch_kib_per_dispatch": round(pf, 1),
-        "write_kib_per_dispatch": round(pw, 1),
-        "copy_fetch_kib": round(copy_f, 1),
-        "copy_write_kib": round(copy_w, 1),
-        "fetch_factor": round(fetch_factor, 4),
-        "write_factor": round(write_factor, 4),
-        "launches_per_step": launches_per_step,
-        "algorithmic_bytes_per_launch": STEP_BYTES_64 // launches_per_step,
-        "bytes_per_launch": int(round(fetch_bytes + write_bytes)),
-    }
+    copy_r = max(read_bytes(d) for d in rd if "copyBuffer" in d["kernel"])
+    copy_w = max(d["WRITE_SIZE"] for d in wr if "copyBuffer" in d["kernel"]) * 1024.0
+    read_factor, write_factor = COPY_BYTES / copy_r, COPY_BYTES / copy_w
+    t = {"kernel_source_hash": kernel_source_hash(), "copy_read_bytes": int(copy_r), "copy_write_bytes": int(copy_w),
+         "read_factor": round(read_factor, 4), "write_factor": round(write_factor, 4),
+         "launches_per_step": launches_per_step, "algorithmic_bytes_per_launch": STEP_BYTES_64 // launches_per_step,
+         "by_rows": {}}
+    for rows in (1, 2, 4, 8, 16):
+        tag = "seq_kernel<%d, true>" % rows
+        r = [read_bytes(d) for d in rd if tag in d["kernel"]]
+        w = [d["WRITE_SIZE"] * 1024.0 for d in wr if tag in d["kernel"]]
+        if not r or not w:
+            continue
+        rb, wb = sum(r) / len(r) * read_factor, sum(w) / len(w) * write_factor
+        t["by_rows"][str(rows)] = {"dispatches": [len(r), len(w)], "read_bytes_per_launch": int(round(rb)),
+                                   "write_bytes_per_launch": int(round(wb)), "bytes_per_launch": int(round(rb + wb)),
+                                   "ratio_to_algorithmic": round((rb + wb) / (STEP_BYTES_64 / launches_per_step), 4)}
     with open(TRAFFIC_FILE, "w") as fo:
         json.dump(t, fo, indent=1)
     print(json.dumps(t))
@@ -680,23 +678,24 @@ def main():
             log("rows=%d: parity sample of layer %d: max err/sum|w*x| %.3g, max %d bf16 ulp, %d outputs"
                 % (r, len(mats) - 1, parity[str(r)]["max_err_over_absdot"], parity[str(r)]["max_bf16_ulp"],
                    parity[str(r)]["outputs"]))
-        pair_ms = time_pair(nv, torch, dev, mats, r, ws, max(2, args.steps // 10))
+        pair_ms = None if args.step_only else time_pair(nv, torch, dev, mats, r, ws, max(2, args.steps // 10))
         gbs = step_bytes / (ms * 1e-3) / 1e9
         by_rows[str(r)] = {
             "ms_per_step": round(ms, 4),
             "launches_per_step": seqs[r].launches,
             "GB_per_s": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-            "gate_up_pair_us": round(pair_ms * 1e3, 3),
-            "gate_up_pair_GB_per_s": round(pair_bytes / (pair_ms * 1e-3) / 1e9, 1),
+            "gate_up_pair_us": None if pair_ms is None else round(pair_ms * 1e3, 3),
+            "gate_up_pair_GB_per_s": None if pair_ms is None else round(pair_bytes / (pair_ms * 1e-3) / 1e9, 1),
         }
-        log("rows=%d: %.4f ms/step in %d launches, %.1f GB/s (%.1f%% of 8 TB/s); stand-alone gate/up pair "
-            "%.2f us" % (r, ms, seqs[r].launches, gbs, 100 * gbs / HBM_PEAK_GBS, pair_ms * 1e3))
+        log("rows=%d: %.4f ms/step in %d launches, %.1f GB/s (%.1f%% of 8 TB/s)%s"
+            % (r, ms, seqs[r].launches, gbs, 100 * gbs / HBM_PEAK_GBS,
+               "" if pair_ms is None else "; stand-alone gate/up pair %.2f us" % (pair_ms * 1e3)))
 
     # the same step with each layer's two residual add + RMSNorm calls inside
     # its launches (the activations of qkv and of the pair made by the step)
     with_norms = {}
-    for r in [r for r in (1, 8) if r in rows_list]:
+    for r in [r for r in (1, 8) if r in rows_list and not args.step_only]:
         seq_n = make_sequence(nv, torch, dev, workloads, mats, r, norms=True)
         ms = time_rows(torch, seq_n, ws, max(5, args.steps // 2), min(args.warmup, 3))
         if nv.wait_flag(ws):
@@ -713,7 +712,7 @@ def main():
     if wait_flag:
         raise SystemExit("a wait between calls gave up (workspace wait flag set)")
     del seqs, bufs
-    ceil_buf = torch.zeros(CEILING_BYTES, dtype=torch.uint8, device=dev)
+    ceil_buf = None if args.step_only else torch.zeros(CEILING_BYTES, dtype=torch.uint8, device=dev)
     head = by_rows[str(rows_list[0])]
     # The dominant kernel is the shared launch that runs the step's calls
     # (every byte of the step is read by it): bytes and duration per launch.
@@ -729,21 +728,22 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": load_traffic() if args.layers == 64 and rows_list[0] == 1 else None,
+        "traffic": load_traffic(rows_list[0]) if args.layers == 64 else None,
         "bytes_per_launch": round(launch_bytes),
         "avg_launch_us": round(launch_us, 2),
     }
     # the streaming-read ceiling for the same bytes per launch (the step's
     # 1.86 GB launches), rotating through a 2 GiB buffer
-    cl = read_ceiling(nv, torch, dev, ceil_buf, int(launch_bytes) // 16 * 16, 20)
-    ceiling_gbs = launch_bytes / (pctl(cl, 50) * 1e-6) / 1e9
-    roofline["read_ceiling_GB_per_s"] = round(ceiling_gbs, 1)
-    roofline["frac_of_read_ceiling"] = round(achieved / ceiling_gbs, 4)
-    log("read ceiling for %.2f GB launches: %.1f GB/s (%.1f%% of 8 TB/s); the step reaches %.1f%% of it"
-        % (launch_bytes / 1e9, ceiling_gbs, 100 * ceiling_gbs / HBM_PEAK_GBS, 100 * achieved / ceiling_gbs))
+    if not args.step_only:
+        cl = read_ceiling(nv, torch, dev, ceil_buf, int(launch_bytes) // 16 * 16, 20)
+        ceiling_gbs = launch_bytes / (pctl(cl, 50) * 1e-6) / 1e9
+        roofline["read_ceiling_GB_per_s"] = round(ceiling_gbs, 1)
+        roofline["frac_of_read_ceiling"] = round(achieved / ceiling_gbs, 4)
+        log("read ceiling for %.2f GB launches: %.1f GB/s (%.1f%% of 8 TB/s); the step reaches %.1f%% of it"
+            % (launch_bytes / 1e9, ceiling_gbs, 100 * ceiling_gbs / HBM_PEAK_GBS, 100 * achieved / ceiling_gbs))
 
     singles = None
-    if args.layers == 64:
+    if args.layers == 64 and not args.step_only:
         singles = single_calls(nv, torch, dev, workloads, mats, ceil_buf)
         for key, v in singles.items():
             log("%s: median %.2f us (p10 %.2f, p90 %.2f), %.1f GB/s = %.1f%% of 8 TB/s; read ceiling %.2f us; "
@@ -752,15 +752,16 @@ def main():
                                                 v["derived_floor_us"]))
 
     dense = None
-    if not args.no_dense:
+    skip_formats = args.no_dense or args.step_only
+    if not skip_formats:
         dense = time_dense(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
                            max(5, args.steps // 5))
 
-    norm = None if args.no_dense else time_norm(nv, torch, dev, max(10, args.steps // 2))
+    norm = None if skip_formats else time_norm(nv, torch, dev, max(10, args.steps // 2))
     # calls of 25-150 us: enough back-to-back calls that launch start-up is a small share
-    mx = None if args.no_dense else time_mx(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
+    mx = None if skip_formats else time_mx(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
                                             max(50, args.steps))
-    w8 = None if args.no_dense else time_w8(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
+    w8 = None if skip_formats else time_w8(nv, torch, dev, [r for r in (1, 8) if r in rows_list] or [rows_list[0]],
                                             max(50, args.steps))
 
     cpu = None
