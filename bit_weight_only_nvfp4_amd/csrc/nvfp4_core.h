@@ -131,6 +131,38 @@ __device__ __forceinline__ void core_g(const uint4 (&wc)[kCodeChunks], const uin
             default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
         }
     };
+    if constexpr (RS >= 2) {
+        // Two or more row sets: the products of a k step are already 8 or more
+        // in flight, enough to cover the matrix core's latency without the
+        // pipeline, whose second set of results would not fit in registers.
+        // Same products, same multiply-adds in the same order per accumulator.
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            bf16x8_t A[RS], B[4];
+#pragma unroll
+            for (int rs = 0; rs < RS; ++rs)
+                A[rs] = *reinterpret_cast<const bf16x8_t *>(xs + abase[rs] + astep[rs] * ks);
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) B[fb] = codes_bf16(word_of(wc[2 * fb + (ks >> 2)], ks & 3));
+            f32x4_t D[4][RS];
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+                for (int rs = 0; rs < RS; ++rs) {
+                    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    D[fb][rs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rs], B[fb], zero, 0, 0, 0);
+                }
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+                const float sc = scale(fb, ks);
+#pragma unroll
+                for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) acc[fb][rs][v] = __builtin_fmaf(D[fb][rs][v], sc, acc[fb][rs][v]);
+            }
+        }
+        return;
+    }
     bf16x8_t B[4], Bn[4];
     f32x4_t D[4][RS], Dp[4][RS];
     float sp[4];

@@ -544,14 +544,18 @@ __device__ __forceinline__ void wait_release(const SeqArgs &a, int g, unsigned e
 // order; a butterfly per wave of 64; the 4 waves' sums in order): waves 0-3
 // here are its waves (with fewer waves, each takes several in turn), so the
 // two give the same bits.  Chunks go 4 per thread at a time, all loads in
-// flight together; up to 8192 values the whole row is one such block and v
-// stays in registers, past it the second pass reads v back from residual_out
-// (the thread's own writes, after waiting for them), which is also correct
-// when residual_out is the residual itself.  Every wave waits for its writes
+// flight together; up to 8192 values the whole row is one such block and
+// (in kernels of up to 8 rows) v stays in registers, otherwise the second
+// pass reads v back from residual_out (the thread's own writes, after
+// waiting for them), which is also correct when residual_out is the residual
+// itself.  Every wave waits for its writes
 // before the workgroup goes on: wave 0 then counts the call done.
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 
+// KEEP: the row may stay in registers (kernels of up to 8 rows; beside the
+// 12- and 16-row kernels' registers it would spill).
+template <bool KEEP>
 __device__ __forceinline__ void norm_row(const CallDesc &d, int row, int wave, int nwb, int lane, float *s_ss) {
     const int k = d.n;
     const uint32_t rb = (uint32_t)k * 2;
@@ -562,7 +566,7 @@ __device__ __forceinline__ void norm_row(const CallDesc &d, int row, int wave, i
     const __amdgpu_buffer_rsrc_t orr = rsrc(static_cast<uint16_t *>(d.aux) + row0, rb);
     const __amdgpu_buffer_rsrc_t xr = rsrc(static_cast<uint16_t *>(d.y) + row0, rb);
     constexpr int kBlock = 4 * 256 * 8;   // values per block: 4 chunks of 8 per thread
-    const bool keep = k <= kBlock && nwb >= 4;   // v of the one block stays in registers
+    const bool keep = KEEP && k <= kBlock && nwb >= 4;   // v of the one block stays in registers
     const bool gemma = d.flags & kGemma;
     u32x4_t vk[4], wk[4];
     for (int vw = wave; vw < 4; vw += nwb) {
@@ -865,7 +869,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
             finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
             cc = cursor_at(d, q, g, cc.k + 1);
         }
-        if (norm_here) norm_row(d, g, wave, nwb, lane, s_ss);
+        if (norm_here) norm_row<(ROWS <= 8)>(d, g, wave, nwb, lane, s_ss);
         // Pieces of shared strips: wave 0 counts them; where this workgroup's
         // count completes a strip, it is summed either by wave 0 alone or by
         // every wave, some rows each, into LDS (`red`, free once wave 0 has
