@@ -72,7 +72,10 @@ constexpr int kPair = 1, kOutF32 = 2, kNorm = 8, kGemma = 16;
 // x is written by the call before this one in the same launch: the activations
 // of a super-tile fetched before the call started are fetched again.
 constexpr int kReloadX = 4;
-constexpr int kSeqMax = 36;
+// Calls per launch: a decode step's 256 projection calls in one launch.  The
+// call table travels in the kernel arguments (80 bytes a call, 20 KB here) and
+// is copied into LDS once per workgroup.
+constexpr int kSeqMax = 256;
 
 // 16 zero bytes for the dummy loads of a norm call (a packed weight's header
 // holds its own: a norm's buffers may be shorter than a header)
@@ -80,10 +83,10 @@ __device__ __align__(16) uint8_t g_zero16[16];
 
 __device__ __forceinline__ const uint8_t *zero_of(const CallDesc &d) {
     return (d.flags & kNorm) ? g_zero16 : d.w0 + kHeaderZeroOffset;
-}   // calls per launch (the kernel arguments stay below 4 KB)
+}
 
-struct SeqArgs {
-    CallDesc call[kSeqMax];
+// What every call of a launch shares: the workspace regions and the grid.
+struct LaunchShared {
     float *partial;       // [R][max_pieces][nmat][rows][64] of the call running
     unsigned *counters;   // arrival count of shared strip sh at word 32 sh (one 128-byte line each)
     unsigned *sync;       // word 32 g: the last call workgroup g may go past (one 128-byte line each)
@@ -91,7 +94,15 @@ struct SeqArgs {
     int ncalls;
     int G;                // workgroups of the launch
 };
-static_assert(sizeof(SeqArgs) <= 3072, "kernel arguments must stay small");
+// Kernel arguments: the shared part and a table of N calls (N = 1 for a
+// launch of one call, so that it copies no more than it needs).
+template <int N>
+struct KernelArgs {
+    LaunchShared s;
+    CallDesc call[N];
+};
+using SeqArgs = KernelArgs<kSeqMax>;
+static_assert(sizeof(SeqArgs) <= 24 * 1024, "kernel arguments of a launch (measured to work up to 32 KB)");
 static_assert(sizeof(CallDesc) % 4 == 0, "call descriptors are copied as words");
 
 constexpr int kSC1 = 16;                          // cache policy: device-coherent access
@@ -305,7 +316,7 @@ template <int ROWS>
 using Acc = float[2][4][core::XStageG<ROWS>::RS][core::XStageG<ROWS>::NV];
 
 template <int ROWS>
-__device__ __forceinline__ void finish_segment(const SeqArgs &a, const CallDesc &d, const Geometry &q, int g,
+__device__ __forceinline__ void finish_segment(const LaunchShared &a, const CallDesc &d, const Geometry &q, int g,
                                                int k, float *red, const float (&sg)[2],
                                                __amdgpu_buffer_rsrc_t yr, int wave, int sw, int nwc, int lane,
                                                Acc<ROWS> &acc, int (&pub)[2]) {
@@ -394,7 +405,7 @@ __host__ __device__ constexpr int final_sum_qb() {
 // Wave 0: sum the pieces of shared strip sh for every row at once, QB pieces
 // per round, and write its outputs.
 template <int ROWS, int NM>
-__device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, int sh, int np,
+__device__ __forceinline__ void final_sum(const LaunchShared &a, const CallDesc &d, int sh, int np,
                                           const float (&sg)[2], __amdgpu_buffer_rsrc_t yr, int lane) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     constexpr int QB = final_sum_qb<ROWS, NM>();
@@ -432,7 +443,7 @@ __device__ __forceinline__ void final_sum(const SeqArgs &a, const CallDesc &d, i
 // w + nwb, ..., each in rounds of 32 / NM pieces, into fs[m][r][lane] (LDS)
 // for wave 0 to write.  The order of every sum is the one above.
 template <int ROWS, int NM>
-__device__ __forceinline__ void sum_pieces(const SeqArgs &a, const CallDesc &d, int sh, int np, int wave, int nwb,
+__device__ __forceinline__ void sum_pieces(const LaunchShared &a, const CallDesc &d, int sh, int np, int wave, int nwb,
                                            int lane, float *fs) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     constexpr int QB = 32 / NM;
@@ -496,7 +507,7 @@ __device__ __forceinline__ void lane0_store(unsigned *p, unsigned v, int lane) {
 // Wave 0: count this workgroup's piece of shared strip sh; true for the
 // workgroup whose count completes it, which clears the counter and sums the
 // strip.
-__device__ __forceinline__ bool arrive_piece(const SeqArgs &a, int sh, int np, int lane) {
+__device__ __forceinline__ bool arrive_piece(const LaunchShared &a, int sh, int np, int lane) {
     unsigned *cnt = a.counters + sh * 32;
     if (lane0_add(cnt, lane) != (unsigned)(np - 1)) return false;
     lane0_store(cnt, 0u, lane);
@@ -509,7 +520,7 @@ __device__ __forceinline__ bool arrive_piece(const SeqArgs &a, int sh, int np, i
 // workgroup's release word, each in a 128-byte line of its own that only its
 // workgroup polls, and goes on without waiting (returns true).  A wait of
 // more than kMaxPolls polls sets the wait flag and goes on: it never hangs.
-__device__ __forceinline__ bool arrive_call(const SeqArgs &a, int g, unsigned e, int lane) {
+__device__ __forceinline__ bool arrive_call(const LaunchShared &a, int g, unsigned e, int lane) {
     wait_own_writes();
     const bool last = lane0_add(a.flags + 32, lane) + 1u == e * (unsigned)a.G;
     if (last) {
@@ -527,7 +538,7 @@ __device__ __forceinline__ bool arrive_call(const SeqArgs &a, int g, unsigned e,
 // polling that often slow the weight stream), and polling before wave 0's
 // fetch of the next call's first items (a poll's result waits for every load
 // issued before it) 0.4-2.6% slower.
-__device__ __forceinline__ void wait_release(const SeqArgs &a, int g, unsigned e, int lane) {
+__device__ __forceinline__ void wait_release(const LaunchShared &a, int g, unsigned e, int lane) {
     unsigned polls = 0;
     while (lane0_load(a.sync + g * 32, lane) < e && polls < kMaxPolls) {
         __builtin_amdgcn_s_sleep(1);
@@ -641,7 +652,8 @@ __device__ __forceinline__ void norm_row(const CallDesc &d, int row, int wave, i
 // SEQ: several calls per launch (the cross-call pipeline and the completion
 // counts); without it the launch runs call 0 alone.
 template <int ROWS, bool SEQ>
-__global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqArgs a) {
+__global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(KernelArgs<SEQ ? kSeqMax : 1> args) {
+    const LaunchShared &a = args.s;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index is uniform across the wave; saying so keeps every loop and
@@ -681,13 +693,13 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
     __shared__ float s_ss[4];    // a norm call's sums of squares, by wave of the stand-alone kernel
     constexpr int kDescWords = sizeof(CallDesc) / 4;
     if (SEQ) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.call);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(args.call);
         uint32_t *dst = reinterpret_cast<uint32_t *>(s_calls);
         for (int i = tid; i < a.ncalls * kDescWords; i += blockDim.x) dst[i] = src[i];
         __syncthreads();
     }
     auto desc = [&](int c) {
-        if (!SEQ) return a.call[0];
+        if (!SEQ) return args.call[0];
         CallDesc v;
         const uint32_t *p = reinterpret_cast<const uint32_t *>(&s_calls[c]);
         uint32_t *o = reinterpret_cast<uint32_t *>(&v);
@@ -957,37 +969,45 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(SeqA
 }
 
 template <int ROWS, bool SEQ>
-hipError_t launch_kernel(const SeqArgs &args, int waves, size_t lds, hipStream_t stream) {
+hipError_t launch_kernel(const LaunchShared &sh, const CallDesc *calls, int waves, size_t lds, hipStream_t stream) {
     const void *fn = reinterpret_cast<const void *>(&seq_kernel<ROWS, SEQ>);
-    // dynamic LDS beyond the default limit needs the attribute, set once per instantiation
+    // dynamic LDS beyond the default limit needs the attribute, set once per
+    // instantiation: what the CU's 160 KB leave beside the kernel's static LDS
+    // (the call table of a sequence kernel)
     static std::atomic<int> lds_set{0};
     if (lds_set.load(std::memory_order_acquire) == 0) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 152 * 1024);
+        hipFuncAttributes attr{};
+        hipError_t e = hipFuncGetAttributes(&attr, fn);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(160 * 1024 - attr.sharedSizeBytes));
         if (e != hipSuccess) return e;
         lds_set.store(1, std::memory_order_release);
     }
-    SeqArgs a = args;
+    KernelArgs<SEQ ? kSeqMax : 1> a;   // the table past ncalls is never read
+    a.s = sh;
+    for (int i = 0; i < (SEQ ? sh.ncalls : 1); ++i) a.call[i] = calls[i];
     void *kargs[] = {&a};
-    const dim3 grid((unsigned)a.G), block((unsigned)(64 * waves));
+    const dim3 grid((unsigned)a.s.G), block((unsigned)(64 * waves));
     // workgroups that wait for each other must all be resident: a cooperative launch
     if (SEQ) return hipLaunchCooperativeKernel(fn, grid, block, kargs, (unsigned)lds, stream);
     return hipLaunchKernel(fn, grid, block, kargs, lds, stream);
 }
 
 template <int ROWS>
-hipError_t launch_rows(const SeqArgs &a, int waves, size_t lds, hipStream_t s) {
-    return a.ncalls > 1 ? launch_kernel<ROWS, true>(a, waves, lds, s) : launch_kernel<ROWS, false>(a, waves, lds, s);
+hipError_t launch_rows(const LaunchShared &a, const CallDesc *c, int waves, size_t lds, hipStream_t s) {
+    return a.ncalls > 1 ? launch_kernel<ROWS, true>(a, c, waves, lds, s) : launch_kernel<ROWS, false>(a, c, waves, lds, s);
 }
 
-hipError_t launch_args(int krows, const SeqArgs &a, int waves, size_t lds, hipStream_t s) {
+hipError_t launch_args(int krows, const LaunchShared &a, const CallDesc *c, int waves, size_t lds, hipStream_t s) {
     switch (krows) {
-        case 1: return launch_rows<1>(a, waves, lds, s);
-        case 2: return launch_rows<2>(a, waves, lds, s);
-        case 4: return launch_rows<4>(a, waves, lds, s);
-        case 6: return launch_rows<6>(a, waves, lds, s);
-        case 8: return launch_rows<8>(a, waves, lds, s);
-        case 12: return launch_rows<12>(a, waves, lds, s);
-        case 16: return launch_rows<16>(a, waves, lds, s);
+        case 1: return launch_rows<1>(a, c, waves, lds, s);
+        case 2: return launch_rows<2>(a, c, waves, lds, s);
+        case 4: return launch_rows<4>(a, c, waves, lds, s);
+        case 6: return launch_rows<6>(a, c, waves, lds, s);
+        case 8: return launch_rows<8>(a, c, waves, lds, s);
+        case 12: return launch_rows<12>(a, c, waves, lds, s);
+        case 16: return launch_rows<16>(a, c, waves, lds, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1132,7 +1152,8 @@ int sequence_launches(const StreamCall *calls, int ncalls) {
 struct LaunchRec {
     int krows, waves;
     size_t lds;
-    SeqArgs args;
+    LaunchShared s;           // workspace pointers set at launch
+    CallDesc call[kSeqMax];   // the first s.ncalls are the launch's calls
 };
 
 size_t launch_rec_bytes() { return sizeof(LaunchRec); }
@@ -1144,15 +1165,15 @@ int build_launches(const StreamCall *calls, int ncalls, void *recs) {
     for (int i0 = 0; i0 < ncalls; ++nrec) {
         const int i1 = launch_end(calls, ncalls, i0, shared);
         LaunchRec &r = out[nrec];
-        r = LaunchRec{};
+        r.s = LaunchShared{};
         const int krows = calls[i0].plan.krows;
-        SeqArgs &a = r.args;
-        a.ncalls = i1 - i0;
+        r.s.ncalls = i1 - i0;
         int G = 1, waves = 1;
         for (int i = i0; i < i1; ++i) {
             const StreamCall &sc = calls[i];
             const StreamPlan &pl = sc.plan;
-            CallDesc &d = a.call[i - i0];
+            CallDesc &d = r.call[i - i0];
+            d = CallDesc{};
             d.w0 = static_cast<const uint8_t *>(sc.w0);
             d.w1 = static_cast<const uint8_t *>(sc.w1 ? sc.w1 : sc.w0);
             d.x = static_cast<const uint16_t *>(sc.x);
@@ -1184,7 +1205,7 @@ int build_launches(const StreamCall *calls, int ncalls, void *recs) {
             if (pl.G > G) G = pl.G;
             if (pl.waves > waves) waves = pl.waves;
         }
-        a.G = G;
+        r.s.G = G;
         r.krows = krows;
         r.waves = waves;
         r.lds = stream_lds_bytes(krows, waves);
@@ -1197,12 +1218,12 @@ hipError_t launch_recs(const void *recs, int nrec, void *workspace, hipStream_t 
     const LaunchRec *in = static_cast<const LaunchRec *>(recs);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     for (int i = 0; i < nrec; ++i) {
-        SeqArgs a = in[i].args;
+        LaunchShared a = in[i].s;
         a.counters = reinterpret_cast<unsigned *>(ws);
         a.sync = ws ? reinterpret_cast<unsigned *>(ws + kSyncOffset) : nullptr;
         a.flags = ws ? reinterpret_cast<unsigned *>(ws + kFlagOffset) : nullptr;
         a.partial = ws ? reinterpret_cast<float *>(ws + kPartialOffset) : nullptr;
-        hipError_t e = launch_args(in[i].krows, a, in[i].waves, in[i].lds, stream);
+        hipError_t e = launch_args(in[i].krows, a, in[i].call, in[i].waves, in[i].lds, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

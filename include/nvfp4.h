@@ -243,7 +243,7 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
  * computing exactly what nvfp4_gemv / nvfp4_gemv_dual_silu would (bit for
  * bit), sharing the one workspace.  The pages drive a decode step of several
  * hundred launches as one captured graph (kern README, "decode" programs; the
- * NVFP4 blueprint's 755 launches per step); here runs of up to 36 consecutive
+ * NVFP4 blueprint's 755 launches per step); here runs of up to 256 consecutive
  * calls with the same row count share one cooperative launch whose
  * workgroups finish each call before any starts computing the next (the next
  * call's first weight tiles are fetched meanwhile), so a call may read the y
