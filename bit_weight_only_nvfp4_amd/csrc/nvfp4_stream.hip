@@ -355,6 +355,28 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
 #pragma unroll
                 for (int v = 0; v < XS::NV; ++v) acc[m][fb][rs][v] = 0.0f;
     __syncthreads();
+    // The slots of a row are summed in position order.  From 4 rows on the
+    // rows are spread over the waves (row r by wave r mod the waves), each
+    // sum stored over slot 0's entry, and wave 0 reads the sums after one
+    // more barrier: it writes every output, and summing every row's slots
+    // alone made the other waves wait for it at the next segment (16% of a
+    // long 8-row call).  Same order, same sums.
+    constexpr bool kSpread = ROWS >= 4;
+    const int nwb = blockDim.x >> 6;
+    if (kSpread) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r)
+                if ((m == 0 || pair) && r % nwb == wave) {
+                    float t = red[(m * RR + r) * kStripN + lane];
+#pragma unroll
+                    for (int w = 1; w < kMaxWavesPerWg; ++w)
+                        if (w < nwc) t += red[((w * 2 + m) * RR + r) * kStripN + lane];
+                    red[(m * RR + r) * kStripN + lane] = t;
+                }
+        __syncthreads();
+    }
     if (wave != 0) return;
     float v[2][ROWS];
 #pragma unroll
@@ -364,9 +386,11 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
             float t = 0.0f;
             if (m == 0 || pair) {
                 t = red[(m * RR + r) * kStripN + lane];
+                if (!kSpread) {
 #pragma unroll
-                for (int w = 1; w < kMaxWavesPerWg; ++w)
-                    if (w < nwc) t += red[((w * 2 + m) * RR + r) * kStripN + lane];
+                    for (int w = 1; w < kMaxWavesPerWg; ++w)
+                        if (w < nwc) t += red[((w * 2 + m) * RR + r) * kStripN + lane];
+                }
             }
             v[m][r] = t;
         }
