@@ -415,6 +415,16 @@ def nvfp4_read_ceiling(buf: torch.Tensor, nbytes: int | None = None, sink: torch
     return sink
 
 
+NVFP4_WS_STATE_BYTES = 161 << 10   # counters and wait words at the start of a workspace
+
+
+def counters_clear(workspace: torch.Tensor) -> bool:
+    """Whether the workspace's counters and wait words (its first
+    NVFP4_WS_STATE_BYTES) are all zero, as every launch leaves them.
+    Synchronizes with the device."""
+    return not bool(workspace[:NVFP4_WS_STATE_BYTES].any())
+
+
 def wait_flag(workspace: torch.Tensor) -> int:
     """The workspace's wait flag (nonzero: a wait between calls of a launch of
     several calls gave up); synchronizes with the device to read it."""

@@ -54,20 +54,33 @@ __host__ __device__ inline int scale_byte_offset(int f, int gt) {
 // call's shape, so partial sums of one call can never land where another
 // call's counters are: a zero-filled workspace stays valid for calls of any
 // shape, since every launch returns its counters to zero.
-//   [0, 32 KiB): split-K arrival counters, one per 128-byte line for each of
-//                up to 256 shared strips (a call has fewer shared strips
-//                than workgroups);
+//   [0, 32 KiB): split-K arrival counters of region 0, one per 128-byte line
+//                for each of up to 256 shared strips (a call has fewer shared
+//                strips than workgroups);
 //   [32 KiB, 64 KiB): one 128-byte line per workgroup of a multi-call launch:
-//                word 0 = the last call it may go past;
+//                word 0 = the last wait it may go past;
 //   [64 KiB, 65 KiB): word 0 = set when a wait between calls timed out,
-//                word 32 = arrivals between calls, word 64 = workgroups
-//                done with the launch (one 128-byte line each);
-//   [65 KiB, ...): fp32 partial sums of the call running.
+//                word 32 = arrivals at waits, word 64 = workgroups done with
+//                the launch (one 128-byte line each);
+//   [65 KiB, 161 KiB): the split-K counters of regions 1, 2, 3;
+//   [161 KiB, ...): fp32 partial sums, region 0 first, then (in a launch of
+//                several calls) regions 1, 2, 3, each P bytes rounded up to 256.
+// A launch of several calls runs consecutive calls that do not depend on each
+// other without a wait between them, so up to kRegions calls are in flight
+// at once, each with counters and partial sums of its own (its region).
 constexpr int64_t kMaxN = (int64_t)1 << 20;
 constexpr size_t kSyncOffset = 32 * 1024;
 constexpr size_t kFlagOffset = 64 * 1024;
-constexpr size_t kPartialOffset = 65 * 1024;
+constexpr size_t kCounterBytes = 32 * 1024;
+constexpr size_t kCounterTailOffset = 65 * 1024;
+constexpr int kRegions = 4;
+constexpr size_t kPartialOffset = kCounterTailOffset + (kRegions - 1) * kCounterBytes;
 static_assert(kFlagOffset == NVFP4_WS_WAIT_FLAG_OFFSET, "the wait flag sits where the ABI says");
+static_assert(kPartialOffset == NVFP4_WS_STATE_BYTES, "the state every launch leaves at zero, as the ABI says");
+constexpr size_t round_partial(size_t p) { return (p + 255) & ~(size_t)255; }
+// Workspace bytes of a launch of several calls whose largest partial sums
+// take `partial` bytes.
+constexpr size_t sequence_workspace(size_t partial) { return kPartialOffset + kRegions * round_partial(partial); }
 
 // Bytes 32..255 of the header are always zero (pack and quantize write them);
 // kernels use them as a 16-byte source of zeros.

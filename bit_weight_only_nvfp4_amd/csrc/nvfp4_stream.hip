@@ -69,6 +69,12 @@ struct CallDesc {
     int rows;             // the call's rows (the kernel's ROWS may be more: those rows read and write nothing)
 };
 constexpr int kPair = 1, kOutF32 = 2, kNorm = 8, kGemma = 16;
+// The call waits for every earlier call of the launch to complete before it
+// starts (it reads or overwrites what one of them writes or reads); without
+// it the call starts as soon as this workgroup is done with the call before.
+constexpr int kWaitBefore = 32;
+// Bits 8..9: the call's workspace region (counters and partial sums).
+constexpr int kRegionShift = 8;
 // x is written by the call before this one in the same launch: the activations
 // of a super-tile fetched before the call started are fetched again.
 constexpr int kReloadX = 4;
@@ -86,11 +92,15 @@ __device__ __forceinline__ const uint8_t *zero_of(const CallDesc &d) {
 }
 
 // What every call of a launch shares: the workspace regions and the grid.
+// In the kernel, partial and counters are those of the call running (its
+// region); in the arguments, region 0's.
 struct LaunchShared {
     float *partial;       // [R][max_pieces][nmat][rows][64] of the call running
     unsigned *counters;   // arrival count of shared strip sh at word 32 sh (one 128-byte line each)
-    unsigned *sync;       // word 32 g: the last call workgroup g may go past (one 128-byte line each)
+    unsigned *sync;       // word 32 g: the last wait workgroup g may go past (one 128-byte line each)
     unsigned *flags;      // word 0: a wait between calls timed out; 32: arrivals; 64: workgroups exited
+    unsigned *counters_tail;   // the counters of regions 1..
+    int pstride;          // floats from one region's partial sums to the next
     int ncalls;
     int G;                // workgroups of the launch
 };
@@ -677,7 +687,7 @@ __device__ __forceinline__ void norm_row(const CallDesc &d, int row, int wave, i
 // counts); without it the launch runs call 0 alone.
 template <int ROWS, bool SEQ>
 __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(KernelArgs<SEQ ? kSeqMax : 1> args) {
-    const LaunchShared &a = args.s;
+    LaunchShared a = args.s;   // partial and counters: the running call's region
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index is uniform across the wave; saying so keeps every loop and
@@ -806,11 +816,19 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         for (int i = 0; i < NB; ++i)
             load_tile<ROWS, true>(first_item(cur, c0, i, true), zero_of(cur.d), lane, b[i]);
     }
+    unsigned waits = 0;   // waits between calls passed so far
     for (int c = 0; c < ncalls; ++c) {
         const CallDesc d = cur.d;
         const Geometry q = cur.q;
         const int nw = cur.nw;
         const bool has_next = SEQ && c + 1 < ncalls;
+        // the next call waits for this one (and every other before it)
+        const bool wait_next = has_next && (nxt.d.flags & kWaitBefore);
+        if (SEQ) {
+            const int reg = (d.flags >> kRegionShift) & (kRegions - 1);
+            a.partial = args.s.partial + (size_t)reg * args.s.pstride;
+            a.counters = reg ? args.s.counters_tail + (reg - 1) * (int)(kCounterBytes / 4) : args.s.counters;
+        }
         const bool pair = d.flags & kPair;
         const int nwc = d.waves;
         const uint8_t *zero = zero_of(d);
@@ -963,7 +981,8 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
                 }
             }
         }
-        if (wave == 0 && has_next) released = arrive_call(a, g, (unsigned)(c + 1), lane);
+        if (wait_next) ++waits;
+        if (wave == 0 && wait_next) released = arrive_call(a, g, waits, lane);
         if (has_next) {
             if (kLateFetch) __syncthreads();   // wave 0 has counted the call done
             if ((kLateFetch || wave == 0 || norm_here) && nxt.fetch) {
@@ -975,7 +994,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
             // the call after next, prepared while the workgroups finish this one
             cur = nxt;
             nxt = prepare(c + 2);
-            if (wave == 0 && !released) wait_release(a, g, (unsigned)(c + 1), lane);
+            if (wave == 0 && wait_next && !released) wait_release(a, g, waits, lane);
             __syncthreads();   // the next call starts in every wave
         }
     }
@@ -1148,8 +1167,10 @@ size_t sequence_workspace_bytes(const StreamCall *calls, int ncalls) {
     size_t partial = 0;
     for (int i = 0; i < ncalls; ++i)
         if (calls[i].plan.partial_bytes > partial) partial = calls[i].plan.partial_bytes;
-    // several calls in one launch keep their waits in the sync region
-    if (ncalls > 1 || partial > 0) return kPartialOffset + partial;
+    // several calls in one launch keep their waits in the sync region and
+    // may run in up to kRegions regions at once
+    if (ncalls > 1) return sequence_workspace(partial);
+    if (partial > 0) return kPartialOffset + partial;
     return 0;
 }
 
@@ -1176,23 +1197,78 @@ int sequence_launches(const StreamCall *calls, int ncalls) {
 struct LaunchRec {
     int krows, waves;
     size_t lds;
+    size_t partial_bytes;     // a region's partial sums (the list's largest)
     LaunchShared s;           // workspace pointers set at launch
     CallDesc call[kSeqMax];   // the first s.ncalls are the launch's calls
 };
 
 size_t launch_rec_bytes() { return sizeof(LaunchRec); }
 
+namespace {
+// The bytes a call reads (weights, activations; a norm call: delta, norm
+// weight, residual) and writes (outputs; a norm call: x and residual_out).
+struct Span {
+    const void *p;
+    size_t n;
+};
+int reads_of(const StreamCall &c, Span (&s)[3]) {
+    const size_t xb = (size_t)c.plan.rows * c.plan.k * 2;
+    if (c.norm) {
+        s[0] = {c.w0, xb};
+        s[1] = {c.w1, (size_t)c.plan.k * 2};
+    } else {
+        s[0] = {c.w0, nvfp4_packed_bytes(c.plan.n, c.plan.k)};
+        s[1] = {c.w1, c.w1 ? nvfp4_packed_bytes(c.plan.n, c.plan.k) : 0};
+    }
+    s[2] = {c.x, xb};
+    return 3;
+}
+int writes_of(const StreamCall &c, Span (&s)[2]) {
+    s[0] = {c.y, (size_t)c.plan.rows * c.plan.n * (c.out_f32 ? 4 : 2)};
+    s[1] = {c.aux, c.norm ? (size_t)c.plan.rows * c.plan.k * 2 : 0};
+    return 2;
+}
+bool spans_overlap(const Span *a, int na, const Span *b, int nb) {
+    for (int i = 0; i < na; ++i)
+        for (int j = 0; j < nb; ++j)
+            if (a[i].n && b[j].n && ranges_overlap(a[i].p, a[i].n, b[j].p, b[j].n)) return true;
+    return false;
+}
+// Call i must wait for call j (earlier in the launch): it reads what j
+// writes, or writes what j reads or writes.
+bool depends(const StreamCall &j, const StreamCall &i) {
+    Span rj[3], wj[2], ri[3], wi[2];
+    reads_of(j, rj);
+    writes_of(j, wj);
+    reads_of(i, ri);
+    writes_of(i, wi);
+    return spans_overlap(wj, 2, ri, 3) || spans_overlap(rj, 3, wi, 2) || spans_overlap(wj, 2, wi, 2);
+}
+}  // namespace
+
+// Calls of a launch run as runs of mutually independent calls: a call waits
+// (kWaitBefore) for every earlier call when it depends on a call of the
+// current run, or when the run already holds kRegions calls; the calls of a
+// run take workspace regions 0, 1, ... in order.  A call that waits has its
+// first tiles fetched during the run before, so it fetches their activations
+// again when a call of that run writes them (kReloadX).
 int build_launches(const StreamCall *calls, int ncalls, void *recs) {
     LaunchRec *out = static_cast<LaunchRec *>(recs);
     const bool shared = ncalls > 1 && cooperative_ok();
+    size_t partial = 0;   // the largest partial sums of the list: a region's size
+    for (int i = 0; i < ncalls; ++i)
+        if (calls[i].plan.partial_bytes > partial) partial = calls[i].plan.partial_bytes;
     int nrec = 0;
     for (int i0 = 0; i0 < ncalls; ++nrec) {
         const int i1 = launch_end(calls, ncalls, i0, shared);
         LaunchRec &r = out[nrec];
         r.s = LaunchShared{};
+        r.s.pstride = (int)(round_partial(partial) / sizeof(float));
+        r.partial_bytes = partial;
         const int krows = calls[i0].plan.krows;
         r.s.ncalls = i1 - i0;
         int G = 1, waves = 1;
+        int run = i0, prev_run = i0;   // first call of the current run and of the run before
         for (int i = i0; i < i1; ++i) {
             const StreamCall &sc = calls[i];
             const StreamPlan &pl = sc.plan;
@@ -1219,13 +1295,21 @@ int build_launches(const StreamCall *calls, int ncalls, void *recs) {
                 d.eps = sc.eps;
             }
             if (i > i0) {
-                const StreamCall &p = calls[i - 1];
-                const size_t ybytes = (size_t)p.plan.rows * p.plan.n * (p.out_f32 ? 4 : 2);
-                const size_t xbytes = (size_t)pl.rows * pl.k * 2;
-                if (ranges_overlap(sc.x, xbytes, p.y, ybytes) ||
-                    (p.norm && ranges_overlap(sc.x, xbytes, p.aux, (size_t)p.plan.rows * p.plan.k * 2)))
-                    d.flags |= kReloadX;
+                bool wait = i - run >= kRegions;
+                for (int j = run; j < i && !wait; ++j) wait = depends(calls[j], sc);
+                if (wait) {
+                    prev_run = run;
+                    run = i;
+                    d.flags |= kWaitBefore;
+                    const Span xs[1] = {{sc.x, (size_t)pl.rows * pl.k * 2}};
+                    for (int j = prev_run; j < i; ++j) {
+                        Span wj[2];
+                        writes_of(calls[j], wj);
+                        if (spans_overlap(wj, 2, xs, 1)) d.flags |= kReloadX;
+                    }
+                }
             }
+            d.flags |= (i - run) << kRegionShift;
             if (pl.G > G) G = pl.G;
             if (pl.waves > waves) waves = pl.waves;
         }
@@ -1247,6 +1331,7 @@ hipError_t launch_recs(const void *recs, int nrec, void *workspace, hipStream_t 
         a.sync = ws ? reinterpret_cast<unsigned *>(ws + kSyncOffset) : nullptr;
         a.flags = ws ? reinterpret_cast<unsigned *>(ws + kFlagOffset) : nullptr;
         a.partial = ws ? reinterpret_cast<float *>(ws + kPartialOffset) : nullptr;
+        a.counters_tail = ws ? reinterpret_cast<unsigned *>(ws + kCounterTailOffset) : nullptr;
         hipError_t e = launch_args(in[i].krows, a, in[i].call, in[i].waves, in[i].lds, stream);
         if (e != hipSuccess) return e;
     }

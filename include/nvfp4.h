@@ -176,13 +176,14 @@ int nvfp4_gemv(const nvfp4_weight *w, const void *x, int rows, void *y, int out_
  * the caller's.  Same arguments, results (bit for bit) and errors as
  * nvfp4_gemv; it allocates and frees nothing.  The array holds the largest
  * workspace any valid call needs (at most 255 shared strips of at most 16 rows
- * in fewer than 768 pieces: under 3.2 MB of partial sums plus 65 KiB of
- * counters); a call whose workspace would exceed it is refused with
+ * in fewer than 768 pieces: under 3.2 MB of partial sums per region, four
+ * regions for a call of more than 16 rows, plus 161 KiB of counters); a call
+ * whose workspace would exceed it is refused with
  * NVFP4_E_WORKSPACE before anything is launched.  Every call on one device shares that device's
  * array, which keeps the last call's contents: calls that may overlap in time
  * on one device (different streams without ordering) race and must not be
  * made.  The array starts at zero and every call leaves its counters at zero. */
-#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 int nvfp4_gemv_noalloc(const nvfp4_weight *w, const void *x, int rows, void *y, int out_dtype, void *stream);
 
 /* Fused gate/up pair of the SwiGLU FFN: o = silu(g) * u with
@@ -233,8 +234,16 @@ typedef struct nvfp4_call {
  * synchronization to check a run of launches. */
 #define NVFP4_WS_WAIT_FLAG_OFFSET 65536
 
-/* Workspace for nvfp4_gemv_sequence: the largest partial sums any of its
- * calls needs, plus the counters (65 KiB) when ncalls > 1. */
+/* The first NVFP4_WS_STATE_BYTES of a projection workspace hold counters and
+ * wait words that every launch leaves at zero (the wait flag aside); the
+ * partial sums follow. */
+#define NVFP4_WS_STATE_BYTES ((size_t)161 << 10)
+
+/* Workspace for nvfp4_gemv_sequence: for one call what nvfp4_gemv needs;
+ * for several, NVFP4_WS_STATE_BYTES + 4 x the largest partial sums any of its
+ * calls needs (rounded up to 256 bytes): up to four consecutive calls that do
+ * not depend on each other run at once, each with counters and partial sums
+ * of its own. */
 size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
 
 /* Enqueue a whole decode step's projections with one host call: every call is
@@ -244,11 +253,15 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
  * bit), sharing the one workspace.  The pages drive a decode step of several
  * hundred launches as one captured graph (kern README, "decode" programs; the
  * NVFP4 blueprint's 755 launches per step); here runs of up to 256 consecutive
- * calls with the same row count share one cooperative launch whose
- * workgroups finish each call before any starts computing the next (the next
- * call's first weight tiles are fetched meanwhile), so a call may read the y
- * of an earlier call as its x.  No call's y may overlap any call's weight,
- * its own x or the workspace (NVFP4_E_OVERLAP).
+ * calls with the same row count share one cooperative launch.  A call that
+ * reads what an earlier call of the launch writes, or writes what one reads or
+ * writes (by address ranges), starts only after every workgroup has finished
+ * every earlier call (a wait); calls that depend on none of the calls since
+ * the last wait run without one, up to four at a time (a call's next weight
+ * tiles are fetched across either).  So a call may read the y of an earlier
+ * call as its x, and the results are those of the calls made one by one.
+ * No call's y may overlap any call's weight, its own x or the workspace
+ * (NVFP4_E_OVERLAP).
  * Residual add + RMSNorm calls (norm != NULL) run inside the same launch, one
  * workgroup per row, with the arithmetic and summation order of
  * nvfp4_residual_rmsnorm: both outputs are bit-identical to it.  A norm's

@@ -64,17 +64,21 @@ def test_workspace_bytes(nv):
     assert w1 > 0 and w1 == nv.nvfp4_workspace_bytes(5120, 17408, 1)
     assert nv.nvfp4_workspace_bytes(5120, 17408, 8) > w1
     assert nv.nvfp4_workspace_bytes(17408, 5120, 1, dual=True) > nv.nvfp4_workspace_bytes(17408, 5120, 1) > 0
-    # more than 16 rows run as row chunks, whose waits need the counters (65 KiB)
+    # more than 16 rows run as row chunks, whose launch needs the counters and waits
     assert nv.nvfp4_workspace_bytes(256, 512, 16) == 0
-    assert nv.nvfp4_workspace_bytes(256, 512, 17) == 65 * 1024
-    assert nv.nvfp4_workspace_bytes(256, 512, 128) == 65 * 1024
-    assert nv.nvfp4_workspace_bytes(5120, 17408, 128) == nv.nvfp4_workspace_bytes(5120, 17408, 16)
+    assert nv.nvfp4_workspace_bytes(256, 512, 17) == SEQ_WS
+    assert nv.nvfp4_workspace_bytes(256, 512, 128) == SEQ_WS
+    # row chunks run as calls of a sequence: 4 regions of the largest partial sums
+    p16 = nv.nvfp4_workspace_bytes(5120, 17408, 16) - SEQ_WS
+    assert nv.nvfp4_workspace_bytes(5120, 17408, 128) == SEQ_WS + 4 * (-(-p16 // 256) * 256)
     for bad in [(256, 512, 0), (256, 512, 129), (0, 512, 1), (256, 24, 1)]:
         assert nv.nvfp4_workspace_bytes(*bad) == 0
     assert nv.nvfp4_quantize_workspace_bytes(256, 512) > 0
     assert nv.nvfp4_quantize_workspace_bytes(256, 20) == 0
 
 
+# a sequence workspace with no partial sums: the counters and waits
+SEQ_WS = 161 * 1024
 FAKE = 0x10000      # 64 KiB-aligned addresses that are never dereferenced:
 XF = 0x1000000      # weights at FAKE, activations at XF, outputs at YF,
 YF = 0x2000000      # workspaces at WF (16 MiB apart: no two overlap)
@@ -191,19 +195,20 @@ def test_sequence_argument_errors(nv):
     big = _weight(nv, 5120, 17408)
     arr[1].w = ctypes.pointer(big)
     need = L.nvfp4_sequence_workspace_bytes(arr, 3)
-    # the largest partial sums (rows 8 of the 5120 x 17408 call) plus the counters
-    assert need == nv.nvfp4_workspace_bytes(5120, 17408, 8)
+    # 4 regions of the largest partial sums (rows 8 of the 5120 x 17408 call) plus the counters
+    p8 = nv.nvfp4_workspace_bytes(5120, 17408, 8) - SEQ_WS
+    assert need == SEQ_WS + 4 * (-(-p8 // 256) * 256)
     assert L.nvfp4_gemv_sequence(arr, 3, WF, need - 16, None, None) == E["NVFP4_E_WORKSPACE"]
     # several calls always need the counters, split-K or not
     arr[1].w = ctypes.pointer(good)
-    assert L.nvfp4_sequence_workspace_bytes(arr, 3) == 65 * 1024
+    assert L.nvfp4_sequence_workspace_bytes(arr, 3) == SEQ_WS
     assert L.nvfp4_sequence_workspace_bytes(arr, 1) == 0
     assert L.nvfp4_sequence_launches(arr, 0) == 0 and L.nvfp4_sequence_launches(None, 3) == 0
     assert 1 <= L.nvfp4_sequence_launches(arr, 3) <= 3
     # a call of 40 rows runs as three row chunks (14, 13, 13): one call alone
     # needs the counters, and up to three launches
     arr[0].rows = 40
-    assert L.nvfp4_sequence_workspace_bytes(arr, 1) == 65 * 1024
+    assert L.nvfp4_sequence_workspace_bytes(arr, 1) == SEQ_WS
     assert 2 <= L.nvfp4_sequence_launches(arr, 1) <= 3
     arr[0].rows = 1
     assert L.nvfp4_gemv_sequence(None, 3, None, 0, None, None) == E["NVFP4_E_NULL"]
@@ -244,7 +249,7 @@ def test_sequence_norm_call_errors(nv):
     L = nv.lib()
     arr, norms, keep = _norm_sequence(nv)
     need = L.nvfp4_sequence_workspace_bytes(arr, 4)
-    assert need == 65 * 1024 and L.nvfp4_sequence_workspace_bytes(arr, 1) == 0
+    assert need == SEQ_WS and L.nvfp4_sequence_workspace_bytes(arr, 1) == 0
     assert 1 <= L.nvfp4_sequence_launches(arr, 4) <= 4
 
     def run():

@@ -325,7 +325,7 @@ def test_sequence_with_many_row_calls(nv):
         y2.zero_()
         seq.launch(ws, events=events)
         torch.cuda.synchronize()
-        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+        assert nv.counters_clear(ws), "counters not returned to zero"
         a1 = nv.nvfp4_gemv(w1, x1)
         a2 = nv.nvfp4_gemv(w2, a1, out_dtype=torch.float32)
         torch.cuda.synchronize()
@@ -588,7 +588,7 @@ def test_sequence_matches_individual_calls(nv):
         seq.launch(ws)
         torch.cuda.synchronize()
         fused = [o.clone() for o in (outs[0], outs[1], pair16, outs[3])]
-        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+        assert nv.counters_clear(ws), "counters not returned to zero"
         for o in (outs[0], outs[1], pair16, outs[3]):
             o.zero_()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -610,7 +610,7 @@ def test_sequence_matches_individual_calls(nv):
         for a, t, b in zip(fused, timed, (outs[0], outs[1], pair16, outs[3])):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rows
             assert torch.equal(t.view(torch.uint8), b.view(torch.uint8)), rows
-        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+        assert nv.counters_clear(ws), "counters not returned to zero"
 
 
 def test_sequence_mixed_rows(nv):
@@ -632,7 +632,7 @@ def test_sequence_mixed_rows(nv):
         alone = nv.nvfp4_gemv(w[i], xs[(r, ks[i])], out_dtype=torch.float32, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(alone.view(torch.int32), outs[j].view(torch.int32)), (j, i, r)
-    assert not bool(ws[:65 * 1024].any())
+    assert nv.counters_clear(ws)
 
 
 def test_sequence_full_size_decode_step(nv):
@@ -672,7 +672,7 @@ def test_sequence_full_size_decode_step(nv):
         ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device=dev)
         seq.launch(ws)
         torch.cuda.synchronize()
-        assert not bool(ws[:65 * 1024].any()), "counters not returned to zero"
+        assert nv.counters_clear(ws), "counters not returned to zero"
         alone = nv.nvfp4_gemv(last["down"][0], o_gu, out_dtype=torch.float32, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(alone.view(torch.int32), y_down.view(torch.int32))
