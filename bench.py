@@ -5,8 +5,10 @@ One step = the weight-only NVFP4 projections of a 64-layer 27B-class decoder
 at one row count: per layer qkv [12288x5120], o [5120x6144], the gate/up pair
 2x[17408x5120] with SiLU*mul, down [5120x17408] (whose input is the pair's
 output), 256 calls, 13,023,313,920 bytes of packed weights (E2M1 codes +
-E4M3 scales, 9/16 byte per weight).  The calls run in order, each after the
-previous one has completed, in shared launches of up to 36 calls.  Weights ~ N(0, 0.02^2) are drawn on the
+E4M3 scales, 9/16 byte per weight), in one shared launch.  The calls compute
+what they would one by one; a call waits for the calls before it where it
+depends on one (down reads the pair's output; the next pair overwrites the
+buffer down reads): two waits per layer.  Weights ~ N(0, 0.02^2) are drawn on the
 device from seeded generators and quantized on the device; activations are
 bf16 ~ N(0, 1).  All weights stay resident in HBM (no cache reuse between
 layers: 13 GB >> the 256 MB Infinity Cache).
@@ -683,6 +685,7 @@ def main():
         by_rows[str(r)] = {
             "ms_per_step": round(ms, 4),
             "launches_per_step": seqs[r].launches,
+            "waits_per_step": seqs[r].waits,
             "GB_per_s": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "gate_up_pair_us": None if pair_ms is None else round(pair_ms * 1e3, 3),
@@ -702,6 +705,7 @@ def main():
             raise SystemExit("rows=%d with norms: a wait between calls gave up" % r)
         base = by_rows[str(r)]["ms_per_step"]
         with_norms[str(r)] = {"ms_per_step": round(ms, 4), "launches_per_step": seq_n.launches,
+                              "waits_per_step": seq_n.waits,
                               "calls_per_step": seq_n.n, "added_ms_vs_projections_only": round(ms - base, 4),
                               "added_us_per_norm": round((ms - base) * 1e3 / (2 * args.layers), 3)}
         log("rows=%d with %d fused residual add + RMSNorm calls: %.4f ms/step in %d launches (+%.3f us per norm)"

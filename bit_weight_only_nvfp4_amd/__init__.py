@@ -44,7 +44,7 @@ EXPORTS = (
     "nvfp4_workspace_bytes", "nvfp4_gemv", "nvfp4_gemv_dual_silu", "nvfp4_sequence_workspace_bytes",
     "nvfp4_gemv_sequence", "nvfp4_sequence_launches", "nvfp4_dense_gemv_bf16", "nvfp4_residual_rmsnorm",
     "nvfp4_mxfp4_gemv", "nvfp4_w8g32_gemv", "nvfp4_read_ceiling", "nvfp4_gemv_noalloc",
-    "nvfp4_sequence_plan_bytes", "nvfp4_sequence_plan", "nvfp4_sequence_plan_launch",
+    "nvfp4_sequence_plan_bytes", "nvfp4_sequence_plan", "nvfp4_sequence_plan_launch", "nvfp4_sequence_waits",
 )
 
 
@@ -130,6 +130,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_int),
             "nvfp4_read_ceiling": ([vp, sz, vp, vp], ctypes.c_int),
             "nvfp4_gemv_noalloc": ([wp, vp, ctypes.c_int, vp, ctypes.c_int, vp], ctypes.c_int),
+            "nvfp4_sequence_waits": ([ctypes.POINTER(nvfp4_call), ctypes.c_int], ctypes.c_int),
             "nvfp4_sequence_plan_bytes": ([ctypes.POINTER(nvfp4_call), ctypes.c_int], sz),
             "nvfp4_sequence_plan": ([ctypes.POINTER(nvfp4_call), ctypes.c_int, vp, sz], ctypes.c_int),
             "nvfp4_sequence_plan_launch": ([vp, vp, sz, vp], ctypes.c_int),
@@ -497,8 +498,10 @@ class Sequence:
             c.norm = None
             self._keep.append((w, up, x, y))
         self.workspace_bytes = int(lib().nvfp4_sequence_workspace_bytes(self._arr, self.n))
-        # kernel launches of one launch() without events
+        # kernel launches of one launch() without events, and the waits
+        # between calls inside them (on a device with cooperative launches)
         self.launches = int(lib().nvfp4_sequence_launches(self._arr, self.n))
+        self.waits = int(lib().nvfp4_sequence_waits(self._arr, self.n)) if self.n else 0
         # validated once: launch() enqueues the plan (nvfp4_sequence_plan_launch)
         self._plan = None
         if self.n:

@@ -713,6 +713,19 @@ int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, si
     return ok();
 }
 
+int nvfp4_sequence_waits(const nvfp4_call *calls, int ncalls) {
+    static const char *fn = "nvfp4_sequence_waits";
+    if (ncalls < 0) return fail(NVFP4_E_SHAPE, "%s: ncalls=%d", fn, ncalls);
+    if (ncalls == 0) return 0;
+    std::vector<StreamCall> sc;
+    std::vector<int> first;
+    int st = build_sequence(fn, calls, ncalls, sc, first);
+    if (st) return st;
+    st = check_overlaps(fn, sc.data(), (int)sc.size(), nullptr, 0);
+    if (st) return st;
+    return sequence_waits(sc.data(), (int)sc.size());
+}
+
 size_t nvfp4_sequence_plan_bytes(const nvfp4_call *calls, int ncalls) {
     static const char *fn = "nvfp4_sequence_plan_bytes";
     if (ncalls <= 0 || !calls) return 0;

@@ -210,6 +210,9 @@ bool cooperative_ok();
 hipError_t launch_sequence(const StreamCall *calls, int ncalls, void *workspace, hipStream_t stream);
 // Launches launch_sequence makes for these calls.
 int sequence_launches(const StreamCall *calls, int ncalls);
+// Waits between calls those launches make where every run of calls of one
+// row count shares a launch (a device with cooperative launches).
+int sequence_waits(const StreamCall *calls, int ncalls);
 // The same in two steps: build_launches writes the launches of these calls
 // (sequence_launches of them, launch_rec_bytes() each, 8-byte aligned) into
 // recs and returns their count; launch_recs enqueues them with a workspace.

@@ -1244,7 +1244,44 @@ bool depends(const StreamCall &j, const StreamCall &i) {
     writes_of(i, wi);
     return spans_overlap(wj, 2, ri, 3) || spans_overlap(rj, 3, wi, 2) || spans_overlap(wj, 2, wi, 2);
 }
+
+// The wait, region and reload flags of the calls [i0, i1) of one launch.
+void mark_runs(const StreamCall *calls, int i0, int i1, int *flags) {
+    int run = i0, prev_run = i0;   // first call of the current run and of the run before
+    for (int i = i0; i < i1; ++i) {
+        const StreamCall &sc = calls[i];
+        int f = 0;
+        if (i > i0) {
+            bool wait = i - run >= kRegions;
+            for (int j = run; j < i && !wait; ++j) wait = depends(calls[j], sc);
+            if (wait) {
+                prev_run = run;
+                run = i;
+                f |= kWaitBefore;
+                const Span xs[1] = {{sc.x, (size_t)sc.plan.rows * sc.plan.k * 2}};
+                for (int j = prev_run; j < i; ++j) {
+                    Span wj[2];
+                    writes_of(calls[j], wj);
+                    if (spans_overlap(wj, 2, xs, 1)) f |= kReloadX;
+                }
+            }
+        }
+        flags[i - i0] = f | ((i - run) << kRegionShift);
+    }
+}
 }  // namespace
+
+int sequence_waits(const StreamCall *calls, int ncalls) {
+    std::vector<int> flags((size_t)ncalls);
+    int waits = 0;
+    for (int i0 = 0; i0 < ncalls;) {
+        const int i1 = launch_end(calls, ncalls, i0, ncalls > 1);
+        mark_runs(calls, i0, i1, flags.data());
+        for (int i = 0; i < i1 - i0; ++i) waits += (flags[i] & kWaitBefore) ? 1 : 0;
+        i0 = i1;
+    }
+    return waits;
+}
 
 // Calls of a launch run as runs of mutually independent calls: a call waits
 // (kWaitBefore) for every earlier call when it depends on a call of the
@@ -1268,7 +1305,8 @@ int build_launches(const StreamCall *calls, int ncalls, void *recs) {
         const int krows = calls[i0].plan.krows;
         r.s.ncalls = i1 - i0;
         int G = 1, waves = 1;
-        int run = i0, prev_run = i0;   // first call of the current run and of the run before
+        int marks[kSeqMax];
+        mark_runs(calls, i0, i1, marks);
         for (int i = i0; i < i1; ++i) {
             const StreamCall &sc = calls[i];
             const StreamPlan &pl = sc.plan;
@@ -1294,22 +1332,7 @@ int build_launches(const StreamCall *calls, int ncalls, void *recs) {
                 d.aux = const_cast<void *>(sc.aux);
                 d.eps = sc.eps;
             }
-            if (i > i0) {
-                bool wait = i - run >= kRegions;
-                for (int j = run; j < i && !wait; ++j) wait = depends(calls[j], sc);
-                if (wait) {
-                    prev_run = run;
-                    run = i;
-                    d.flags |= kWaitBefore;
-                    const Span xs[1] = {{sc.x, (size_t)pl.rows * pl.k * 2}};
-                    for (int j = prev_run; j < i; ++j) {
-                        Span wj[2];
-                        writes_of(calls[j], wj);
-                        if (spans_overlap(wj, 2, xs, 1)) d.flags |= kReloadX;
-                    }
-                }
-            }
-            d.flags |= (i - run) << kRegionShift;
+            d.flags |= marks[i - i0];
             if (pl.G > G) G = pl.G;
             if (pl.waves > waves) waves = pl.waves;
         }

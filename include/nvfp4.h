@@ -274,6 +274,14 @@ size_t nvfp4_sequence_workspace_bytes(const nvfp4_call *calls, int ncalls);
 int nvfp4_gemv_sequence(const nvfp4_call *calls, int ncalls, void *workspace, size_t workspace_bytes,
                         void *const *events, void *stream);
 
+/* Waits between calls the launches of nvfp4_gemv_sequence make for these
+ * calls on a device with cooperative launches (calls of one row count share
+ * a launch): the calls that depend on an earlier call of their launch, plus
+ * one for every fifth call of a run of independent ones.  The calls are
+ * validated as nvfp4_gemv_sequence validates them (but for the workspace);
+ * a negative NVFP4_E_* status if one is invalid. */
+int nvfp4_sequence_waits(const nvfp4_call *calls, int ncalls);
+
 /* A call list validated once and kept, for a decode step launched many times
  * (the pages capture a step once and replay it: kern README, "Layout").
  * nvfp4_sequence_plan_bytes: host bytes of the plan of these calls, 0 if a

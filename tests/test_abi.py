@@ -378,6 +378,72 @@ def test_sequence_object_validates_once(nv):
     assert "call 0" in str(e.value)   # empty tensors: a NULL x
 
 
+def test_sequence_waits(nv):
+    """Where a launch of several calls waits between them (the host's reading
+    of the calls' address ranges): a call waits when it reads what a call
+    since the last wait writes, or writes what one reads or writes, and after
+    every 4 calls run without one."""
+    L = nv.lib()
+    MB = 0x100000
+    keep = []
+
+    def w(n, k, i):
+        wt = _weight(nv, n, k, data=0x100000000 + i * 0x10000000)
+        keep.append(wt)
+        return ctypes.pointer(wt)
+
+    def proj(wp, x, y, up=None, rows=1):
+        c = nv.nvfp4_call()
+        c.w, c.up, c.x, c.y, c.rows, c.out_dtype = wp, up, x, y, rows, 0
+        return c
+
+    def norm(resid, delta, weight, xout, k=512, rows=1):
+        nm = nv.nvfp4_norm(resid, delta, weight, resid, k, 1e-6, 1)
+        keep.append(nm)
+        c = nv.nvfp4_call()
+        c.norm, c.y, c.rows, c.out_dtype = ctypes.pointer(nm), xout, rows, 0
+        return c
+
+    def waits(calls):
+        arr = (nv.nvfp4_call * len(calls))(*calls)
+        return L.nvfp4_sequence_waits(arr, len(calls))
+
+    X1, X2, Yq, Yo, H, Yd = (XF + i * 16 * MB for i in range(6))
+    # the benchmark's step: qkv and o read fixed x, the pair too, down reads the pair's output
+    step = []
+    for l in range(3):
+        step += [proj(w(768, 512, 5 * l), X1, Yq), proj(w(512, 384, 5 * l + 1), X2, Yo),
+                 proj(w(1024, 512, 5 * l + 2), X1, H, up=w(1024, 512, 5 * l + 3)),
+                 proj(w(512, 1024, 5 * l + 4), H, Yd)]
+    # layer 0: down waits (reads H); later layers: the pair waits too (overwrites what down read)
+    assert waits(step) == 1 + 2 + 2
+    # independent calls: a wait after every run of 4
+    ind = [proj(w(256, 512, 100 + i), XF + i * MB, 0x40000000 + i * MB) for i in range(9)]
+    assert waits(ind) == 2
+    # a chain: each reads the previous output
+    chain = [proj(w(512, 512, 200 + i), XF + i * 16 * MB, XF + (i + 1) * 16 * MB) for i in range(5)]
+    assert waits(chain) == 4
+    # two writers of one buffer
+    assert waits([proj(w(256, 512, 300), X1, Yq), proj(w(256, 512, 301), X2, Yq)]) == 1
+    # a decoder layer with norms: norm, qkv, o, norm, pair, down -- qkv waits for the
+    # norm's x, the second norm for o's output, the pair for its x, down for the
+    # pair's output, the next layer's first norm for down's output: o alone runs
+    # beside qkv
+    R, XN, A = XF + 7 * 16 * MB, XF + 8 * 16 * MB, XF + 9 * 16 * MB
+    ln = [0x100000000 + (400 + i) * 0x10000000 for i in range(4)]
+    layer = []
+    for l in range(2):
+        layer += [norm(R, Yd, ln[2 * l], XN), proj(w(768, 512, 500 + 5 * l), XN, Yq),
+                  proj(w(512, 384, 501 + 5 * l), A, Yo), norm(R, Yo, ln[2 * l + 1], XN),
+                  proj(w(1024, 512, 502 + 5 * l), XN, H, up=w(1024, 512, 503 + 5 * l)),
+                  proj(w(512, 1024, 504 + 5 * l), H, Yd)]
+    assert waits(layer) == 4 + 5
+    # invalid calls: the status
+    bad = [proj(w(256, 512, 600), X1, Yq), proj(w(256, 512, 601), X1, Yq, rows=0)]
+    assert waits(bad) == {v: k for k, v in nv.STATUS.items()}["NVFP4_E_ROWS"]
+    del keep
+
+
 def _dense(nv, W=FAKE, n=256, k=512, x=XF, rows=1, y=YF, dtype=0):
     return nv.lib().nvfp4_dense_gemv_bf16(W, n, k, x, rows, y, dtype, None)
 
