@@ -983,8 +983,11 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         }
         if (wait_next) ++waits;
         if (wave == 0 && wait_next) released = arrive_call(a, g, waits, lane);
+        // Without a wait before the next call no barrier ends this one either:
+        // the other waves start the next call while wave 0 still completes
+        // this one's shared strips, and meet it at the next segment's end.
         if (has_next) {
-            if (kLateFetch) __syncthreads();   // wave 0 has counted the call done
+            if (kLateFetch && wait_next) __syncthreads();   // wave 0 has counted the call done
             if ((kLateFetch || wave == 0 || norm_here) && nxt.fetch) {
                 // wave 0's writes are complete: its loads in flight delay only its polls
                 Cursor nc = nc0;
@@ -995,7 +998,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
             cur = nxt;
             nxt = prepare(c + 2);
             if (wave == 0 && wait_next && !released) wait_release(a, g, waits, lane);
-            __syncthreads();   // the next call starts in every wave
+            if (wait_next) __syncthreads();   // the next call starts in every wave
         }
     }
     if (SEQ && wave == 0) {
