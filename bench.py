@@ -362,8 +362,10 @@ CEILING_BYTES = 1 << 31     # the read-ceiling buffer: 2 GiB, far beyond the 256
 
 
 def read_ceiling(nv, torch, dev, buf, nbytes, ncalls):
-    """Per-call durations of the streaming-read kernel over nbytes, rotating
-    the start offset through the 2 GiB buffer."""
+    """Per-call durations of the streaming-read kernel over nbytes (at most
+    half the 2 GiB buffer), rotating the start offset through the buffer."""
+    if not 0 < nbytes <= CEILING_BYTES // 2:
+        raise ValueError("read ceiling of %d bytes: at most %d" % (nbytes, CEILING_BYTES // 2))
     span = (CEILING_BYTES - nbytes) // 4096 * 4096
     offs = [(i * 1_000_003 * 4096) % max(span, 4096) if span > 0 else 0 for i in range(ncalls + 20)]
     sink = torch.empty(256, dtype=torch.int32, device=dev)
@@ -736,15 +738,17 @@ def main():
         "bytes_per_launch": round(launch_bytes),
         "avg_launch_us": round(launch_us, 2),
     }
-    # the streaming-read ceiling for the same bytes per launch (the step's
-    # 1.86 GB launches), rotating through a 2 GiB buffer
+    # the streaming-read ceiling of long reads (1 GiB per call, the step's
+    # launch being longer), rotating through a 2 GiB buffer
     if not args.step_only:
-        cl = read_ceiling(nv, torch, dev, ceil_buf, int(launch_bytes) // 16 * 16, 20)
-        ceiling_gbs = launch_bytes / (pctl(cl, 50) * 1e-6) / 1e9
+        cbytes = min(int(launch_bytes) // 16 * 16, CEILING_BYTES // 2)
+        cl = read_ceiling(nv, torch, dev, ceil_buf, cbytes, 20)
+        ceiling_gbs = cbytes / (pctl(cl, 50) * 1e-6) / 1e9
         roofline["read_ceiling_GB_per_s"] = round(ceiling_gbs, 1)
+        roofline["read_ceiling_bytes_per_call"] = cbytes
         roofline["frac_of_read_ceiling"] = round(achieved / ceiling_gbs, 4)
-        log("read ceiling for %.2f GB launches: %.1f GB/s (%.1f%% of 8 TB/s); the step reaches %.1f%% of it"
-            % (launch_bytes / 1e9, ceiling_gbs, 100 * ceiling_gbs / HBM_PEAK_GBS, 100 * achieved / ceiling_gbs))
+        log("read ceiling for %.2f GB reads: %.1f GB/s (%.1f%% of 8 TB/s); the step reaches %.1f%% of it"
+            % (cbytes / 1e9, ceiling_gbs, 100 * ceiling_gbs / HBM_PEAK_GBS, 100 * achieved / ceiling_gbs))
 
     singles = None
     if args.layers == 64 and not args.step_only:

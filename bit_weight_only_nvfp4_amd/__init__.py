@@ -408,9 +408,15 @@ def nvfp4_read_ceiling(buf: torch.Tensor, nbytes: int | None = None, sink: torch
     """Read ``nbytes`` of ``buf`` (a device tensor) from byte ``offset`` once
     with the projection kernel's launch shape: the streaming-read ceiling.
     Returns the 256-word sink."""
-    nb = buf.numel() * buf.element_size() - offset if nbytes is None else nbytes
+    size = buf.numel() * buf.element_size()
+    nb = size - offset if nbytes is None else nbytes
+    if offset < 0 or nb < 0 or offset + nb > size:
+        raise ValueError("nvfp4_read_ceiling: bytes [%d, %d) are not inside the %d-byte buffer"
+                         % (offset, offset + nb, size))
     if sink is None:
         sink = torch.empty(256, dtype=torch.int32, device=buf.device)
+    if sink.numel() * sink.element_size() < 1024:
+        raise ValueError("nvfp4_read_ceiling: the sink must hold 256 32-bit words")
     _check("nvfp4_read_ceiling", lib().nvfp4_read_ceiling(buf.data_ptr() + offset, nb, sink.data_ptr(),
                                                           _stream(buf.device)))
     return sink

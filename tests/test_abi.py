@@ -552,3 +552,16 @@ def test_read_ceiling_argument_errors(nv):
     assert L.nvfp4_read_ceiling(FAKE, 0, YF, None) == E["NVFP4_E_SHAPE"]
     assert L.nvfp4_read_ceiling(FAKE, 1000, YF, None) == E["NVFP4_E_SHAPE"]
     assert L.nvfp4_read_ceiling(FAKE + 8, 1024, YF, None) == E["NVFP4_E_ALIGN"]
+
+
+def test_read_ceiling_binding_stays_inside_the_buffer(nv):
+    """The binding refuses a read past its tensor before calling the library
+    (the C entry point takes a raw pointer and cannot tell)."""
+    buf = torch.zeros(4096, dtype=torch.uint8)
+    sink = torch.zeros(256, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        nv.nvfp4_read_ceiling(buf, 8192, sink)
+    with pytest.raises(ValueError):
+        nv.nvfp4_read_ceiling(buf, 2048, sink, offset=3072)
+    with pytest.raises(ValueError):
+        nv.nvfp4_read_ceiling(buf, 1024, torch.zeros(16, dtype=torch.int32))
