@@ -613,6 +613,57 @@ def test_sequence_matches_individual_calls(nv):
         assert nv.counters_clear(ws), "counters not returned to zero"
 
 
+def test_sequence_independent_calls_and_hazards(nv):
+    """Calls that depend on no earlier call run without a wait, up to four at
+    once in workspace regions of their own: 12 independent split-K calls (every
+    region in use) equal the calls made one by one; so do a call that
+    overwrites an earlier call's input (it must wait for the reader), two
+    calls writing one buffer (the later one's result stays), and a chain."""
+    rng = np.random.default_rng(17)
+    shapes = [(200, 4096), (320, 2304), (130, 5120)]   # skinny: split-K pieces
+    for rows in (1, 5, 16):
+        ws_list = [_pack(nv, oracle.quantize(rng.standard_normal(shapes[i % 3], dtype=np.float32)
+                                             * np.float32(0.02))) for i in range(12)]
+        xs = [_x_dev(workloads.draw_x(rng, rows, shapes[i % 3][1])) for i in range(12)]
+        ys = [torch.empty((rows, shapes[i % 3][0]), dtype=torch.float32, device="cuda") for i in range(12)]
+        seq = nv.Sequence([(ws_list[i], None, xs[i], ys[i]) for i in range(12)])
+        assert seq.waits == 2   # a wait after every run of four
+        ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device="cuda")
+        seq.launch(ws)
+        torch.cuda.synchronize()
+        assert nv.counters_clear(ws)
+        for i in range(12):
+            alone = nv.nvfp4_gemv(ws_list[i], xs[i], out_dtype=torch.float32, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(alone.view(torch.int32), ys[i].view(torch.int32)), (rows, i)
+        # hazards: A reads xa; C overwrites xa (write after read); B and D write one buffer
+        # (write after write); E reads B's... D's output (read after write)
+        wA, wB, wC, wD, wE = (_pack(nv, oracle.quantize(rng.standard_normal((n, k), dtype=np.float32)
+                                                         * np.float32(0.02)))
+                              for n, k in ((256, 512), (384, 768), (512, 1024), (384, 512), (256, 384)))
+        xa0 = workloads.draw_x(rng, rows, 512)
+        xa = _x_dev(xa0)
+        xb, xc = _x_dev(workloads.draw_x(rng, rows, 768)), _x_dev(workloads.draw_x(rng, rows, 1024))
+        ya = torch.empty((rows, 256), dtype=torch.bfloat16, device="cuda")
+        yb = torch.empty((rows, 384), dtype=torch.bfloat16, device="cuda")
+        ye = torch.empty((rows, 256), dtype=torch.bfloat16, device="cuda")
+        calls = [(wA, None, xa, ya), (wB, None, xb, yb), (wC, None, xc, xa), (wD, None, xa, yb),
+                 (wE, None, yb, ye)]
+        seq = nv.Sequence(calls)
+        assert seq.waits == 3   # C (overwrites A's input), D (reads C's output), E (reads D's)
+        ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device="cuda")
+        seq.launch(ws)
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (ya, yb, ye, xa)]
+        xa.copy_(_x_dev(xa0))
+        for w, _, x, y in calls:
+            nv.nvfp4_gemv(w, x, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(got, (ya, yb, ye, xa)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), rows
+        assert nv.counters_clear(ws)
+
+
 def test_sequence_mixed_rows(nv):
     """Calls with different row counts in one sequence (one launch per run of
     equal row counts) equal the calls made one by one."""
