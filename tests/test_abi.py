@@ -417,6 +417,16 @@ def test_sequence_waits(nv):
                  proj(w(512, 1024, 5 * l + 4), H, Yd)]
     # layer 0: down waits (reads H); later layers: the pair waits too (overwrites what down read)
     assert waits(step) == 1 + 2 + 2
+    # the pair's output alternating between two buffers: down alone waits, and the
+    # runs between waits are down, qkv, o, pair (four calls)
+    H2 = XF + 10 * 16 * MB
+    step2 = []
+    for l in range(4):
+        h = (H, H2)[l % 2]
+        step2 += [proj(w(768, 512, 40 + 5 * l), X1, Yq), proj(w(512, 384, 41 + 5 * l), X2, Yo),
+                  proj(w(1024, 512, 42 + 5 * l), X1, h, up=w(1024, 512, 43 + 5 * l)),
+                  proj(w(512, 1024, 44 + 5 * l), h, Yd)]
+    assert waits(step2) == 4
     # independent calls: a wait after every run of 4
     ind = [proj(w(256, 512, 100 + i), XF + i * MB, 0x40000000 + i * MB) for i in range(9)]
     assert waits(ind) == 2
