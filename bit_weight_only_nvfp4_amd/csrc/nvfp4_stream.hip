@@ -311,15 +311,51 @@ __device__ __forceinline__ Cursor cursor_at(const CallDesc &d, const Geometry &q
     return c;
 }
 
-// Close segment k: reduce the waves' accumulators in wave order; then wave 0
-// either writes the strip's outputs, or stores this piece of a shared strip
-// in the partials and marks it in pub[] (strip fs or fs + 1).  Arrivals are
-// counted, and the last piece's workgroup sums the pieces, once the call's
-// tiles are done.  Every wave calls this for every segment, in order, and
-// leaves with its accumulators cleared.
+// Segment ends without a workgroup barrier (barrier_free_segments(ROWS)).
+// Buffer b (of red_buffers(ROWS))
+// of the wave-reduction slots serves segments b, b + red_buffers(ROWS), ...
+// of the workgroup's sequence, counted across calls; arr[b] counts the waves
+// other than wave 0 that have stored their slots for its segment, done[b] is
+// the last segment whose slots wave 0 has read from it.  The LDS executes
+// each wave's instructions in order, so a count that wave 0 reads comes after
+// the slots it counts, and a done that a wave reads after the reads it
+// reports; the signal fences keep the compiler from moving LDS accesses
+// across these words.
+struct SegSync {
+    unsigned arr[2];
+    int done[2];
+};
+
+// Wave-uniform spin until *w >= v, bounded: past kMaxPolls polls the wait
+// flag is set and the wave goes on (it never hangs).
+__device__ __forceinline__ void lds_wait_ge(const int *w, int v, const LaunchShared &a, int lane) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    unsigned polls = 0;
+    while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < v &&
+           polls < kMaxPolls) {
+        __builtin_amdgcn_s_sleep(1);
+        ++polls;
+    }
+    if (polls >= kMaxPolls && a.flags && lane == 0)
+        __hip_atomic_store(a.flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Close segment k (the workgroup's segment number seg, counted across calls):
+// every wave stores its accumulators' sums in its slot; the slots are summed
+// in wave order; then wave 0 either writes the strip's outputs, or stores
+// this piece of a shared strip in the partials and marks it in pub[] (strip
+// fs or fs + 1).  Arrivals are counted, and the last piece's workgroup sums
+// the pieces, once the call's tiles are done.  Every wave calls this for
+// every segment, in order, and leaves with its accumulators cleared and seg
+// advanced.  Without barriers (barrier_free_segments) a wave stores its slot
+// and goes on, and waits only where it would overwrite slots that wave 0 has
+// not read yet (a segment that used the same buffer); wave 0 waits for the
+// other waves' slots and sums them alone.  With barriers, the waves store
+// their slots, sum some rows each, and wave 0 reads the sums.
 //
-// This runs inside the tile loop, so its loops are fully unrolled with
-// wave-uniform guards: a rolled loop or a divergent branch there makes the
+// This runs inside the tile loop, so its loops over values are fully
+// unrolled with wave-uniform guards: a divergent branch there makes the
 // compiler assume that tile loads may still be in flight at the top of the
 // tile loop, and wait for them.
 template <int ROWS>
@@ -327,13 +363,23 @@ using Acc = float[2][4][core::XStageG<ROWS>::RS][core::XStageG<ROWS>::NV];
 
 template <int ROWS>
 __device__ __forceinline__ void finish_segment(const LaunchShared &a, const CallDesc &d, const Geometry &q, int g,
-                                               int k, float *red, const float (&sg)[2],
+                                               int k, float *red0, const float (&sg)[2],
                                                __amdgpu_buffer_rsrc_t yr, int wave, int sw, int nwc, int lane,
-                                               Acc<ROWS> &acc, int (&pub)[2]) {
+                                               Acc<ROWS> &acc, int (&pub)[2], int &seg, SegSync &ss) {
     using XS = core::XStageG<ROWS>;
     const bool pair = d.flags & kPair;
     constexpr int RR = red_rows(ROWS);   // rows per slot of `red`
-    __syncthreads();   // the previous segment's reads of `red` are done
+    constexpr int NBUF = red_buffers(ROWS);
+    constexpr bool kBarrierFree = barrier_free_segments(ROWS);
+    const int nwb = blockDim.x >> 6;
+    const int b = seg % NBUF;
+    float *red = red0 + (size_t)b * nwb * 2 * RR * kStripN;
+    if constexpr (kBarrierFree) {
+        // the slots of buffer b are free once wave 0 has read them for segment seg - NBUF
+        if (wave != 0) lds_wait_ge(&ss.done[b], seg - NBUF, a, lane);
+    } else {
+        __syncthreads();   // the previous segment's reads of `red` are done
+    }
     // Slots in position order (sw): the sums below run in that order.  A
     // pair's accumulators are its gate and up sums; a single projection's
     // are two halves of its sum (even and odd tiles of the wave).  Lane
@@ -364,16 +410,22 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
             for (int rs = 0; rs < XS::RS; ++rs)
 #pragma unroll
                 for (int v = 0; v < XS::NV; ++v) acc[m][fb][rs][v] = 0.0f;
-    __syncthreads();
-    // The slots of a row are summed in position order.  From 4 rows on the
-    // rows are spread over the waves (row r by wave r mod the waves), each
-    // sum stored over slot 0's entry, and wave 0 reads the sums after one
-    // more barrier: it writes every output, and summing every row's slots
-    // alone made the other waves wait for it at the next segment (16% of a
-    // long 8-row call).  Same order, same sums.
-    constexpr bool kSpread = ROWS >= 4;
-    const int nwb = blockDim.x >> 6;
-    if (kSpread) {
+    const int this_seg = seg++;
+    if constexpr (kBarrierFree) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (wave != 0) {
+            if (lane == 0) __hip_atomic_fetch_add(&ss.arr[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return;
+        }
+        lds_wait_ge(reinterpret_cast<const int *>(&ss.arr[b]), nwb - 1, a, lane);
+        if (lane == 0) __hip_atomic_store(&ss.arr[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+        __syncthreads();
+        // From 4 rows on the rows are spread over the waves (row r by wave r
+        // mod the waves), each sum stored over slot 0's entry, and wave 0
+        // reads the sums after one more barrier: summing every row's slots
+        // alone made the other waves wait for it at the next segment (16% of
+        // a long 8-row call).  Same order, same sums.
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -386,8 +438,9 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
                     red[(m * RR + r) * kStripN + lane] = t;
                 }
         __syncthreads();
+        if (wave != 0) return;
     }
-    if (wave != 0) return;
+    // The slots of a row are summed in position order.
     float v[2][ROWS];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -396,7 +449,7 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
             float t = 0.0f;
             if (m == 0 || pair) {
                 t = red[(m * RR + r) * kStripN + lane];
-                if (!kSpread) {
+                if constexpr (kBarrierFree) {
 #pragma unroll
                     for (int w = 1; w < kMaxWavesPerWg; ++w)
                         if (w < nwc) t += red[((w * 2 + m) * RR + r) * kStripN + lane];
@@ -404,6 +457,10 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
             }
             v[m][r] = t;
         }
+    if constexpr (kBarrierFree) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(&ss.done[b], this_seg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     const int sh = segment_shared(d, q, k);
     const bool head = sh == q.fs;
     const int np = head ? q.np0 : q.np1;
@@ -538,14 +595,21 @@ __device__ __forceinline__ void lane0_store(unsigned *p, unsigned v, int lane) {
     if (lane == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave 0: count this workgroup's piece of shared strip sh; true for the
-// workgroup whose count completes it, which clears the counter and sums the
-// strip.
-__device__ __forceinline__ bool arrive_piece(const LaunchShared &a, int sh, int np, int lane) {
-    unsigned *cnt = a.counters + sh * 32;
-    if (lane0_add(cnt, lane) != (unsigned)(np - 1)) return false;
-    lane0_store(cnt, 0u, lane);
-    return true;
+// Wave 0: count this workgroup's pieces of shared strips fs and fs + 1
+// (pub[h] set: a piece of strip fs + h was stored), lanes 0 and 1 at once, so
+// that two pieces cost one round trip to memory.  Bit h of the result is set
+// where this workgroup's count completes strip fs + h: it clears the counter
+// and sums the strip.
+__device__ __forceinline__ unsigned arrive_pieces(const LaunchShared &a, const Geometry &q, const int (&pub)[2],
+                                                  int lane) {
+    const bool mine = (lane == 0 && pub[0]) || (lane == 1 && pub[1]);
+    unsigned *cnt = a.counters + (q.fs + (lane & 1)) * 32;
+    const unsigned np = (unsigned)(lane == 1 ? q.np1 : q.np0);
+    unsigned old = 0;
+    if (mine) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = mine && old == np - 1u;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (unsigned)__ballot(last) & 3u;
 }
 
 // Wave 0: the wait between calls (epoch e = calls finished so far).  Each
@@ -725,13 +789,19 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
     __shared__ CallDesc s_calls[SEQ ? kSeqMax : 1];
     __shared__ unsigned s_fin;   // shared strips this workgroup completes (bits 0, 1)
     __shared__ float s_ss[4];    // a norm call's sums of squares, by wave of the stand-alone kernel
+    __shared__ SegSync s_seg;    // segment ends (finish_segment)
+    int seg = 0;                 // segments this workgroup has closed
+    if (tid < 2) {
+        s_seg.arr[tid] = 0u;
+        s_seg.done[tid] = tid - red_buffers(ROWS);
+    }
     constexpr int kDescWords = sizeof(CallDesc) / 4;
     if (SEQ) {
         const uint32_t *src = reinterpret_cast<const uint32_t *>(args.call);
         uint32_t *dst = reinterpret_cast<uint32_t *>(s_calls);
         for (int i = tid; i < a.ncalls * kDescWords; i += blockDim.x) dst[i] = src[i];
-        __syncthreads();
     }
+    __syncthreads();
     auto desc = [&](int c) {
         if (!SEQ) return args.call[0];
         CallDesc v;
@@ -872,7 +942,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         // close every segment that ends before position i
         auto close_before = [&](int i) {
             while (i >= cc.end) {
-                finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
+                finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub, seg, s_seg);
                 cc = cursor_at(d, q, g, cc.k + 1);
             }
         };
@@ -919,7 +989,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
             }
         }
         while (cc.k < q.nseg) {
-            finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub);
+            finish_segment<ROWS>(a, d, q, g, cc.k, red, sg, yr, wave, sw, nwc, lane, acc, pub, seg, s_seg);
             cc = cursor_at(d, q, g, cc.k + 1);
         }
         if (norm_here) norm_row<(ROWS <= 8)>(d, g, wave, nwb, lane, s_ss);
@@ -940,10 +1010,11 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         if (pieces && !spread) {
             if (wave == 0) {
                 wait_own_writes();   // the partials are visible before they are counted
+                const unsigned fin = arrive_pieces(a, q, pub, lane);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int np = h ? q.np1 : q.np0;
-                    if (pub[h] && arrive_piece(a, q.fs + h, np, lane)) {
+                    if (fin & (1u << h)) {
                         if (pair) final_sum<ROWS, 2>(a, d, q.fs + h, np, sg, yr, lane);
                         else final_sum<ROWS, 1>(a, d, q.fs + h, np, sg, yr, lane);
                     }
@@ -952,9 +1023,7 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         } else if (pieces) {
             if (wave == 0) {
                 wait_own_writes();   // the partials are visible before they are counted
-                unsigned fin = 0;
-                if (pub[0] && arrive_piece(a, q.fs, q.np0, lane)) fin |= 1u;
-                if (pub[1] && arrive_piece(a, q.fs + 1, q.np1, lane)) fin |= 2u;
+                const unsigned fin = arrive_pieces(a, q, pub, lane);
                 if (lane == 0) s_fin = fin;
             }
             __syncthreads();
@@ -978,13 +1047,16 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
                                                red[((2 * h + 1) * ROWS + r) * kStripN + lane], sg,
                                                d.G * d.F + q.fs + h, r, lane);
                 }
+                // the next segment's slots overwrite these sums
+                __syncthreads();
             }
         }
         if (wait_next) ++waits;
         if (wave == 0 && wait_next) released = arrive_call(a, g, waits, lane);
         // Without a wait before the next call no barrier ends this one either:
         // the other waves start the next call while wave 0 still completes
-        // this one's shared strips, and meet it at the next segment's end.
+        // this one's shared strips, and wave 0 catches up at the next
+        // segment's end (with barriers there, they meet it).
         if (has_next) {
             if (kLateFetch && wait_next) __syncthreads();   // wave 0 has counted the call done
             if ((kLateFetch || wave == 0 || norm_here) && nxt.fetch) {
@@ -1160,7 +1232,8 @@ size_t stream_lds_bytes(int krows, int waves) {
     const size_t lds_x = (size_t)waves * x_stage_bytes(krows);
     // the wave-reduction slots; they also hold the final sums of up to two
     // shared strips (4 x rows x 64 floats), hence at least two waves' worth
-    const size_t lds_red = (size_t)(waves < 2 ? 2 : waves) * 2 * red_rows(krows) * kStripN * sizeof(float);
+    const size_t lds_red = (size_t)red_buffers(krows) * (waves < 2 ? 2 : waves) * 2 * red_rows(krows) * kStripN *
+                           sizeof(float);
     // at least ~81 KB so that no CU ever holds two of these workgroups
     return lds_x + lds_red < kOneWorkgroupPerCuLds ? kOneWorkgroupPerCuLds : lds_x + lds_red;
 }
