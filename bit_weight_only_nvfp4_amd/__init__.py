@@ -30,7 +30,7 @@ NVFP4_ABI_VERSION = 2
 NVFP4_MAX_ROWS = 128
 NVFP4_OUT_BF16 = 0
 NVFP4_OUT_F32 = 1
-NVFP4_WS_WAIT_FLAG_OFFSET = 65536   # uint32 in a sequence workspace: a wait between calls gave up
+NVFP4_WS_WAIT_FLAG_OFFSET = 65536   # uint32 in a workspace: a bounded wait of a launch gave up
 
 STATUS = {
     0: "NVFP4_OK", -1: "NVFP4_E_NULL", -2: "NVFP4_E_SHAPE", -3: "NVFP4_E_ROWS", -4: "NVFP4_E_ALIGN",
@@ -433,8 +433,9 @@ def counters_clear(workspace: torch.Tensor) -> bool:
 
 
 def wait_flag(workspace: torch.Tensor) -> int:
-    """The workspace's wait flag (nonzero: a wait between calls of a launch of
-    several calls gave up); synchronizes with the device to read it."""
+    """The workspace's wait flag (nonzero: a bounded wait of a launch gave up,
+    between its calls or between the waves of a workgroup); synchronizes with
+    the device to read it."""
     off = NVFP4_WS_WAIT_FLAG_OFFSET
     if workspace.numel() < off + 4:
         return 0

@@ -167,12 +167,13 @@ __host__ __device__ constexpr int x_stage_bytes(int krows) { return 2 * ((krows 
 __host__ __device__ constexpr int red_rows(int krows) {
     return 8 * ((krows + 7) / 8 - 1) + 2 * (((krows < 8 ? krows : 8) + 1) / 2);
 }
-// Segment ends without a workgroup barrier (1-2 rows: each wave stores its
-// slot and goes on, wave 0 sums them once all are stored), or with barriers
-// and the rows' sums spread over the waves (from 4 rows on, where wave 0
-// summing every row alone costs more than the barriers).  Measured on the
-// decode step: 3% and 5% faster at 1 and 2 rows, 2.5% slower at 8 rows.
-__host__ __device__ constexpr bool barrier_free_segments(int krows) { return krows <= 2; }
+// Segment ends without a workgroup barrier (up to 4 rows: each wave stores
+// its slot and goes on, wave 0 sums them once all are stored), or with
+// barriers and the rows' sums spread over the waves (from 6 rows on, where
+// wave 0 summing every row alone costs more than the barriers).  Measured on
+// the decode step: 3%, 5% and 1% faster at 1, 2 and 4 rows, 2.5-5% slower at
+// 6-8 rows.
+__host__ __device__ constexpr bool barrier_free_segments(int krows) { return krows <= 4; }
 // Buffers of wave-reduction slots: two without barriers (consecutive segments
 // alternate, so a wave waits for wave 0's reads of a segment only two
 // segments later), else one.

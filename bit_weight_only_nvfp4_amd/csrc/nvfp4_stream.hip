@@ -907,13 +907,14 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         const float sg[2] = {cur.sg[0], cur.sg[1]};
         // The next call's first NB items, fetched while this call ends.  Wave
         // 0 fetches its own only once it has counted this call done: it writes
-        // every result, and waits for its writes to complete first.  At 2
+        // every result, and waits for its writes to complete first.  Up to 4
         // rows every wave waits until then (kLateFetch): the end of a call is a
         // chain of dependent round trips to memory (partial sums, counts, the
         // final sums, outputs, the wait), each slowed by any burst of loads in
-        // flight.  Measured on the decode step: 1% faster at 2 rows, 0.6%
-        // slower at 1 row, 4-6% slower at 4-8 rows (more arithmetic per byte).
-        constexpr bool kLateFetch = ROWS == 2;
+        // flight.  Measured on the decode step with barrier-free segment ends:
+        // 3.6% faster at 1 row, 1% at 4; at 6-8 rows (more arithmetic per
+        // byte, segment barriers) 4-6% slower.
+        constexpr bool kLateFetch = ROWS <= 4;
         // A workgroup normalizing a row (a norm call) fetches the next call's
         // first items only after it: its loads would return behind them.
         const bool norm_here = (d.flags & kNorm) && g < d.rows;

@@ -227,11 +227,13 @@ typedef struct nvfp4_call {
 } nvfp4_call;
 
 /* Byte offset, in a projection workspace, of the uint32 wait flag: a launch
- * of several calls (nvfp4_gemv_sequence) sets it to nonzero if one of its
- * waits between calls gave up (after 2^18 polls, about a second; it then goes
- * on so that no launch can hang, and that launch's results are not
- * reliable).  Nothing clears it but the caller: read it after a
- * synchronization to check a run of launches. */
+ * sets it to nonzero if one of its bounded waits gave up -- a wait between the
+ * calls of a launch of several calls (nvfp4_gemv_sequence), or, in a launch
+ * with a workspace, a wave of a workgroup waiting for the others at the end of
+ * a strip segment -- after 2^18 polls (well under a second); it then goes on
+ * so that no launch can hang, and that launch's results are not reliable.
+ * Nothing clears it but the caller: read it after a synchronization to check
+ * a run of launches. */
 #define NVFP4_WS_WAIT_FLAG_OFFSET 65536
 
 /* The first NVFP4_WS_STATE_BYTES of a projection workspace hold counters and
