@@ -613,6 +613,49 @@ def test_sequence_matches_individual_calls(nv):
         assert nv.counters_clear(ws), "counters not returned to zero"
 
 
+def test_sequence_many_short_segments(nv):
+    """Calls whose workgroups close several one-super-tile segments each (600
+    strips of 64 features, k = 256: two owned strips per workgroup plus a
+    leftover strip for some), so that at 1-4 rows, where segment ends take no
+    workgroup barrier, the waves without a tile in a segment run ahead to the
+    slot buffers of later segments and calls: 10 such calls -- single
+    projections and a gate/up pair, independent and chained -- in one
+    sequence equal the same calls made one by one, bit for bit, with the
+    workspace's counters and wait flag back at zero."""
+    rng = np.random.default_rng(21)
+    n, k = 64 * 600, 256
+    mats = [_pack(nv, oracle.quantize(rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)))
+            for _ in range(9)]
+    chain = _pack(nv, oracle.quantize(rng.standard_normal((256, n), dtype=np.float32) * np.float32(0.02)))
+    for rows in (1, 2, 4, 6):
+        print("sequence of short segments, rows=%d" % rows, flush=True)
+        x = _x_dev(workloads.draw_x(rng, rows, k))
+        ys = [torch.empty((rows, n), dtype=torch.bfloat16 if i % 2 else torch.float32, device="cuda")
+              for i in range(6)]
+        h = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
+        z = torch.empty((rows, 256), dtype=torch.float32, device="cuda")
+        calls = [(mats[i], None, x, ys[i]) for i in range(6)]
+        calls += [(mats[6], mats[7], x, h), (chain, None, h, z), (mats[8], None, x, ys[0]), (mats[0], None, x, ys[1])]
+        seq = nv.Sequence(calls)
+        assert seq.waits >= 2
+        ws = torch.zeros(max(seq.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        seq.launch(ws)
+        torch.cuda.synchronize()
+        fused = [t.clone() for t in ys + [h, z]]
+        assert nv.wait_flag(ws) == 0
+        assert nv.counters_clear(ws), "counters not returned to zero"
+        for i in range(6):
+            nv.nvfp4_gemv(mats[i], x, out=ys[i], out_dtype=ys[i].dtype, workspace=ws)
+        nv.nvfp4_gemv_dual_silu(mats[6], mats[7], x, out=h, workspace=ws)
+        nv.nvfp4_gemv(chain, h, out=z, out_dtype=torch.float32, workspace=ws)
+        nv.nvfp4_gemv(mats[8], x, out=ys[0], out_dtype=ys[0].dtype, workspace=ws)
+        nv.nvfp4_gemv(mats[0], x, out=ys[1], out_dtype=ys[1].dtype, workspace=ws)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(fused, ys + [h, z])):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (rows, i)
+        assert nv.counters_clear(ws), "counters not returned to zero"
+
+
 def test_sequence_independent_calls_and_hazards(nv):
     """Calls that depend on no earlier call run without a wait, up to four at
     once in workspace regions of their own: 12 independent split-K calls (every
