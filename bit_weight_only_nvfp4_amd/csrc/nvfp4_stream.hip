@@ -24,9 +24,14 @@
 //   * pieces of a strip are summed in piece order by the last to arrive (an
 //     arrival counter), so results are bitwise deterministic with no float
 //     atomics, and identical whether a call runs alone or in a sequence;
-//   * calls run in order: a call starts computing only after every workgroup
-//     has finished the previous one (a completion count per launch), so a call
-//     may read an earlier call's output as its activations.
+//   * a call that depends on an earlier call of the launch (reads what it
+//     writes, or writes what it reads or writes) starts only after every
+//     workgroup has finished every earlier call (a completion count per
+//     launch); independent calls follow each other without a wait, up to
+//     four at once, each with its own workspace region;
+//   * the waves of a workgroup meet only where they must: up to 4 rows a
+//     segment end takes no barrier (LDS counters), from 6 rows on it takes
+//     barriers and spreads the sums over the waves.
 // Everything one workgroup writes to global memory -- outputs, partial sums,
 // counters -- is written by its wave 0 with device-coherent (sc1) accesses, and
 // wave 0 is the only wave with no loads in flight across a call boundary, so it
@@ -421,7 +426,7 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
         if (lane == 0) __hip_atomic_store(&ss.arr[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
         __syncthreads();
-        // From 4 rows on the rows are spread over the waves (row r by wave r
+        // From 6 rows on the rows are spread over the waves (row r by wave r
         // mod the waves), each sum stored over slot 0's entry, and wave 0
         // reads the sums after one more barrier: summing every row's slots
         // alone made the other waves wait for it at the next segment (16% of
