@@ -62,11 +62,38 @@ KERNEL_SOURCES = ("bit_weight_only_nvfp4_amd/csrc/nvfp4_stream.hip", "bit_weight
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
 
 
+def _code_tokens(text: str) -> str:
+    """C++ source without its comments and with whitespace collapsed, so that
+    editing a comment does not make the traffic counters stale.  String and
+    character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the decode-step kernel's code (comments and layout ignored)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 
