@@ -729,6 +729,78 @@ def test_sequence_mixed_rows(nv):
     assert nv.counters_clear(ws)
 
 
+_RANDOM_LIST_DIMS = (256, 512, 1024, 1536)
+_random_pool = {}
+
+
+def _random_list_pool(nv):
+    """Two packed weights per (n, k) over _RANDOM_LIST_DIMS, built once."""
+    if not _random_pool:
+        rng = np.random.default_rng(999)
+        for n in _RANDOM_LIST_DIMS:
+            for k in _RANDOM_LIST_DIMS:
+                _random_pool[(n, k)] = [
+                    _pack(nv, oracle.quantize(rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.05)))
+                    for _ in range(2)]
+    return _random_pool
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_sequence_random_call_lists(nv, seed):
+    """Seeded random call lists -- single projections and gate/up pairs of
+    several shapes over a pool of activation buffers, so that calls read
+    earlier calls' outputs, overwrite what earlier calls read or write, or
+    depend on nothing (any mix of waits, runs of up to four and workspace
+    regions) -- at one row count per list: the sequence leaves every buffer
+    as the same calls made one by one do, bit for bit, with the workspace's
+    counters and wait flag back at zero."""
+    dims = _RANDOM_LIST_DIMS
+    rows = (1, 2, 4, 8)[seed]
+    pool = _random_list_pool(nv)
+    rng = np.random.default_rng(1000 + seed)
+    start = {d: [workloads.draw_x(rng, rows, d) for _ in range(3)] for d in dims}
+    plan = []
+    for _ in range(28):
+        k, n = int(rng.choice(dims)), int(rng.choice(dims))
+        i = int(rng.integers(3))
+        j = int(rng.integers(3))
+        if k == n and i == j:
+            j = (j + 1) % 3
+        pair = bool(rng.random() < 0.25)
+        plan.append((n, k, i, j, pair, int(rng.integers(2))))
+
+    def fresh():
+        return {d: [_x_dev(b) for b in start[d]] for d in dims}
+
+    def calls_of(bufs):
+        out = []
+        for n, k, i, j, pair, wi in plan:
+            w = pool[(n, k)][wi]
+            up = pool[(n, k)][1 - wi] if pair else None
+            out.append((w, up, bufs[k][i], bufs[n][j]))
+        return out
+
+    print("random call list seed=%d rows=%d" % (seed, rows), flush=True)
+    bufs = fresh()
+    seq = nv.Sequence(calls_of(bufs))
+    ws = torch.zeros(max(seq.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    seq.launch(ws)
+    torch.cuda.synchronize()
+    assert nv.wait_flag(ws) == 0
+    assert nv.counters_clear(ws), "counters not returned to zero"
+    ref = fresh()
+    for w, up, x, y in calls_of(ref):
+        if up is None:
+            nv.nvfp4_gemv(w, x, out=y, workspace=ws)
+        else:
+            nv.nvfp4_gemv_dual_silu(w, up, x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    for d in dims:
+        for i in range(3):
+            assert torch.equal(bufs[d][i].view(torch.int16), ref[d][i].view(torch.int16)), (seed, d, i, seq.waits)
+    assert nv.counters_clear(ws), "counters not returned to zero"
+
+
 def test_sequence_full_size_decode_step(nv):
     """Two full-size decode-step layers through one sequence (a shared launch
     per row count, the weight pipeline running across calls): the last layer's
