@@ -13,9 +13,10 @@
 // two weights exactly (a code has 2 significant bits; bf16 holds every
 // code * 2^e for e in -126..125).  The activations then feed the bf16 matrix
 // cores as stored: no activation staging, no scale multiply.
-//   * one workgroup per 64 features (four 16-feature products), 4 waves each
-//     over a quarter of k in steps of 256; two steps in flight (176
-//     registers, two waves per SIMD);
+//   * one workgroup per 64 features (four 16-feature products; 32 below
+//     32768 features, so that small matrices still give two workgroups per
+//     CU), 4 waves each over a quarter of k in steps of 256; two steps in
+//     flight (176 registers, two waves per SIMD);
 //   * per step a lane (q, n) takes k = 64 q .. 64 q + 63 of the step -- two
 //     MX blocks, so two scale bytes per feature block -- as 32 contiguous
 //     bytes of codes per feature block (a row's four lanes read 128
@@ -218,12 +219,23 @@ hipError_t launch_mx(const void *codes, const void *scales, int64_t n, int64_t k
     a.out_f32 = out_f32;
     const int64_t per = (k + kMxWaves - 1) / kMxWaves;
     a.kw = (int)((per + kMxStepK - 1) / kMxStepK * kMxStepK);
-    constexpr int FB = 4, BUFS = 2;
-    const unsigned grid = (unsigned)((n + 16 * FB - 1) / (16 * FB));
-    if (k % 256 == 0 && reinterpret_cast<uintptr_t>(scales) % 8 == 0)
-        hipLaunchKernelGGL((mx_kernel<FB, BUFS, true>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((mx_kernel<FB, BUFS, false>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+    constexpr int BUFS = 2;
+    const bool wide = k % 256 == 0 && reinterpret_cast<uintptr_t>(scales) % 8 == 0;
+    // Below 512 groups of 64 features (two workgroups per CU), groups of 32:
+    // twice the workgroups, the same sums (each feature's products and their
+    // order do not depend on the group size).  Measured on [17408 x 5120]:
+    // 20.0 us against 22.1 at 1 row, 24.1 against 25.3 at 8.
+    if (n < 32768) {
+        constexpr int FB = 2;
+        const unsigned grid = (unsigned)((n + 16 * FB - 1) / (16 * FB));
+        if (wide) hipLaunchKernelGGL((mx_kernel<FB, BUFS, true>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+        else hipLaunchKernelGGL((mx_kernel<FB, BUFS, false>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+    } else {
+        constexpr int FB = 4;
+        const unsigned grid = (unsigned)((n + 16 * FB - 1) / (16 * FB));
+        if (wide) hipLaunchKernelGGL((mx_kernel<FB, BUFS, true>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+        else hipLaunchKernelGGL((mx_kernel<FB, BUFS, false>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
