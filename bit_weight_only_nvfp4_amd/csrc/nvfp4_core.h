@@ -122,15 +122,13 @@ __device__ __forceinline__ void core_g(const uint4 (&wc)[kCodeChunks], const uin
         astep[rs] = live ? 64 : 0;
     }
     // E4M3 scale of feature block fb at k step ks
-    auto scale = [&](int fb, int ks) {
+    // E4M3 scales of feature block fb at k steps ks and ks + 1 (ks even): one
+    // packed conversion of the two bytes
+    auto scale_pair = [&](int fb, int ks) {
         const uint32_t w = sl[fb >> 1][2 * (fb & 1) + (ks >> 2)];
-        switch (ks & 3) {
-            case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
-            case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
-            case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
-            default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
-        }
+        return (ks & 2) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
     };
+    float sn[4];   // the scale of the odd k step, converted with the even one
     if constexpr (RS >= 2) {
         // Two or more row sets: the products of a k step are already 8 or more
         // in flight, enough to cover the matrix core's latency without the
@@ -154,7 +152,14 @@ __device__ __forceinline__ void core_g(const uint4 (&wc)[kCodeChunks], const uin
                 }
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) {
-                const float sc = scale(fb, ks);
+                float sc;
+                if ((ks & 1) == 0) {
+                    const auto p = scale_pair(fb, ks);
+                    sc = p[0];
+                    sn[fb] = p[1];
+                } else {
+                    sc = sn[fb];
+                }
 #pragma unroll
                 for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
@@ -200,7 +205,13 @@ __device__ __forceinline__ void core_g(const uint4 (&wc)[kCodeChunks], const uin
         if (ks < 8) {
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) {
-                sp[fb] = scale(fb, ks);
+                if ((ks & 1) == 0) {
+                    const auto p = scale_pair(fb, ks);
+                    sp[fb] = p[0];
+                    sn[fb] = p[1];
+                } else {
+                    sp[fb] = sn[fb];
+                }
 #pragma unroll
                 for (int rs = 0; rs < RS; ++rs) Dp[fb][rs] = D[fb][rs];
             }
