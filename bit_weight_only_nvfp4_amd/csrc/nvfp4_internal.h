@@ -141,6 +141,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Launch shape of the persistent streaming projection kernel.
 constexpr int kMaxWorkgroups = 256;      // one per CU on MI355X
 constexpr int kOwnerMinStrips = 160;     // from here on, whole strips per workgroup
+constexpr int kLeftoverPieces = 4;       // pieces per strip left over past whole strips per workgroup, at most
 constexpr size_t kOneWorkgroupPerCuLds = 82 * 1024;   // > half of the 160 KB LDS of a CU
 constexpr int kMaxWavesPerWg = 8;
 // Rows one kernel call computes; calls of more rows are cut into row chunks
@@ -184,6 +185,7 @@ struct StreamPlan {
     int rows, krows, nmat;    // rows of the call, rows of the kernel that runs it
     int strips, supers;       // S, T
     int G, F, R;              // workgroups, owned strips per workgroup, shared strips
+    int Gs;                   // the last Gs workgroups take the shared strips' units
     int waves;                // waves per workgroup taking part in the call
     int max_pieces;           // most pieces any shared strip is cut into
     size_t partial_bytes;     // fp32 partial sums [R][max_pieces][nmat][krows][64] (0 if no strip is cut)

@@ -43,6 +43,7 @@
 // workgroups; the first G*F strips are owned, F per workgroup; the R = S - G*F
 // remaining strips form R*T shared units split into G contiguous ranges
 // [g*RT/G, (g+1)*RT/G), cut at strip boundaries into pieces.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 #include <vector>
@@ -80,6 +81,9 @@ constexpr int kPair = 1, kOutF32 = 2, kNorm = 8, kGemma = 16;
 constexpr int kWaitBefore = 32;
 // Bits 8..9: the call's workspace region (counters and partial sums).
 constexpr int kRegionShift = 8;
+// Bits 16..23: the workgroups the shared strips are spread over, minus one
+// (the last of the call's G; the others own whole strips only).
+constexpr int kShareShift = 16;
 // x is written by the call before this one in the same launch: the activations
 // of a super-tile fetched before the call started are fetched again.
 constexpr int kReloadX = 4;
@@ -274,20 +278,27 @@ __device__ __forceinline__ Geometry make_geometry(const CallDesc &d, int g) {
     q.su0 = q.su1 = q.fs = q.nsh = q.nseg = q.total = 0;
     q.piece0 = q.np0 = q.np1 = 1;
     if (g >= d.G) return q;   // not taking part in this call
-    // g * U and (g + 1) * U stay below 256 * 2^24 = 2^32
-    const uint32_t U = (uint32_t)d.R * (uint32_t)d.T, G = (uint32_t)d.G, T = (uint32_t)d.T;
-    q.su0 = (int)((uint32_t)g * U / G);
-    q.su1 = (int)((uint32_t)(g + 1) * U / G);
+    // g * U and (g + 1) * U stay below 256 * 2^24 = 2^32.  The shared units
+    // are spread over the call's last G workgroups here (G <= the call's),
+    // s = 0 .. G - 1 in order: a call of fewer strips than workgroups runs on
+    // the first ones, so the last are the least loaded in a run of calls.
+    const uint32_t U = (uint32_t)d.R * (uint32_t)d.T, T = (uint32_t)d.T;
+    const uint32_t G = (uint32_t)((d.flags >> kShareShift) & 0xff) + 1u;
+    const int s = g - (d.G - (int)G);
+    if (s >= 0) {
+        q.su0 = (int)((uint32_t)s * U / G);
+        q.su1 = (int)((uint32_t)(s + 1) * U / G);
+    }
     q.fs = q.su1 > q.su0 ? (int)((uint32_t)q.su0 / T) : 0;
     q.nsh = q.su1 > q.su0 ? (int)((uint32_t)(q.su1 - 1) / T) - q.fs + 1 : 0;
     q.nseg = d.F + q.nsh;
     q.total = d.F * d.T + (q.su1 - q.su0);
     if (q.nsh > 0) {
         const int first = owner_wg32((uint32_t)q.fs * T, U, G);
-        q.piece0 = g - first;
+        q.piece0 = s - first;
         q.np0 = owner_wg32((uint32_t)(q.fs + 1) * T - 1u, U, G) - first + 1;
         // strip fs + 1 (used only when this range reaches it, i.e. fs + 1 < R)
-        q.np1 = owner_wg32(min((uint32_t)(q.fs + 2) * T - 1u, U - 1u), U, G) - g + 1;
+        q.np1 = owner_wg32(min((uint32_t)(q.fs + 2) * T - 1u, U - 1u), U, G) - s + 1;
     }
     return q;
 }
@@ -1172,6 +1183,7 @@ StreamPlan make_norm_plan(int64_t k, int rows) {
     pl.strips = 0;
     pl.supers = 1;
     pl.G = rows;      // workgroup r normalizes row r
+    pl.Gs = rows;
     pl.F = 0;
     pl.R = 0;
     pl.waves = 0;     // no tiles
@@ -1209,7 +1221,18 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
     // (9 KB each) in flight, so this sets the bytes in flight per CU -- enough
     // to cover the memory latency at full bandwidth.
     int waves = max_waves_for_rows(rows);
-    const long long per_wg = pl.F * (long long)T + (pl.R ? ((long long)pl.R * T + pl.G - 1) / pl.G : 0);
+    // Strips left over past whole strips per workgroup are spread over the
+    // last Gs workgroups, so that each is cut into about kLeftoverPieces
+    // pieces: every piece adds a partial sum, and the strip's completion waits
+    // for the last of them.
+    // (at least one unit each: a workgroup without units would be counted
+    // as a piece that never arrives).
+    pl.Gs = pl.G;
+    if (pl.F > 0 && pl.R > 0) {
+        const long long gs = std::min<long long>((long long)pl.R * kLeftoverPieces, (long long)pl.R * T);
+        if (gs < pl.G) pl.Gs = (int)gs;
+    }
+    const long long per_wg = pl.F * (long long)T + (pl.R ? ((long long)pl.R * T + pl.Gs - 1) / pl.Gs : 0);
     // When the others can take everything in their first fetch, wave 0 takes
     // no position: in a sequence each wave's first items arrive ahead of the
     // call, except wave 0's (it writes the results and cannot have loads in
@@ -1224,7 +1247,7 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
     if (pl.R > 0) {
         const long long U = (long long)pl.R * T;
         for (int sh = 0; sh < pl.R; ++sh) {
-            const int np = owner_wg((long long)sh * T + T - 1, U, pl.G) - owner_wg((long long)sh * T, U, pl.G) + 1;
+            const int np = owner_wg((long long)sh * T + T - 1, U, pl.Gs) - owner_wg((long long)sh * T, U, pl.Gs) + 1;
             if (np > pl.max_pieces) pl.max_pieces = np;
         }
     }
@@ -1405,7 +1428,7 @@ int build_launches(const StreamCall *calls, int ncalls, void *recs) {
             d.R = pl.R;
             d.max_pieces = pl.max_pieces;
             d.waves = pl.waves;
-            d.flags = (pl.nmat == 2 ? kPair : 0) | (sc.out_f32 ? kOutF32 : 0);
+            d.flags = (pl.nmat == 2 ? kPair : 0) | (sc.out_f32 ? kOutF32 : 0) | ((pl.Gs - 1) << kShareShift);
             d.rows = pl.rows;
             d.aux = nullptr;
             if (sc.norm) {

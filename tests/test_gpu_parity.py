@@ -512,6 +512,49 @@ def test_full_gate_up_rows1(nv):
     assert st["max_err_over_bound"] < 0.05
 
 
+# ---- strips left over past whole strips per workgroup ------------------------------
+
+@pytest.mark.parametrize("n,k,dual", [(16448, 5120, False), (16448, 512, True), (19200, 1024, False),
+                                      (32896, 256, True)])
+def test_leftover_strips(nv, n, k, dual):
+    """More strips of 64 features than workgroups: each workgroup owns whole
+    strips and the strips left over are cut into a few pieces on the last
+    workgroups -- also where the leftover holds fewer super-tiles than there
+    are workgroups (257 strips of 2 or 20 super-tiles, 514 strips of one).
+    Every leftover feature and 128 others are checked against the oracle at
+    rows 1 and 8, and the calls inside one sequence equal the calls made one
+    by one, bit for bit."""
+    rng = np.random.default_rng(n + k)
+    W = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    q = oracle.quantize(W)
+    w = _pack(nv, q)
+    if dual:
+        qu = oracle.quantize(rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02))
+        wu = _pack(nv, qu)
+    owned = (n // 64 // 256) * 256 * 64
+    sel = np.unique(np.concatenate([np.arange(owned, n), rng.choice(owned, 128, replace=False)]))
+    for rows in (1, 8):
+        print("leftover strips %dx%d dual=%d rows=%d" % (n, k, dual, rows), flush=True)
+        xb = workloads.draw_x(rng, rows, k)
+        if dual:
+            o32, o16 = _run_dual(nv, w, wu, xb)
+            d = oracle.gemv_dual_silu(q, qu, xb, sel=sel)
+            check.check_dual(o32[:, sel], o16[:, sel], d, label="leftover dual %dx%d r%d" % (n, k, rows))
+        else:
+            o32, o16 = _run_gemv(nv, w, xb)
+            ref, absd, ref16 = oracle.gemv(*q, xb, sel=sel)
+            check.check_gemv(o32[:, sel], o16[:, sel], ref, absd, ref16, label="leftover %dx%d r%d" % (n, k, rows))
+        x = _x_dev(xb)
+        ys = [torch.empty((rows, n), dtype=torch.float32, device="cuda") for _ in range(3)]
+        seq = nv.Sequence([(w, wu if dual else None, x, y) for y in ys])
+        ws = torch.zeros(seq.workspace_bytes, dtype=torch.uint8, device="cuda")
+        seq.launch(ws)
+        torch.cuda.synchronize()
+        assert nv.counters_clear(ws), "counters not returned to zero"
+        for y in ys:
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), o32.view(np.uint32)), rows
+
+
 # ---- the decode-step sweep: one layer, sampled outputs -------------------------------
 
 def test_sweep_layer_sampled(nv):
