@@ -575,6 +575,38 @@ def time_rotating(torch, launch, copies, reps):
     return start.elapsed_time(stop) * 1e3 / reps
 
 
+def time_long_call(nv, torch, dev, workloads, rows_list, reps, ceil_buf):
+    """One long projection call, [65536 x 16384] (604 MB packed, 512 strips of
+    64 super-tiles: two whole strips per workgroup, no split-K), back to back
+    over two distinct copies (1.2 GB): the tile loop's own streaming rate,
+    without the per-call and per-wait costs of the decode step's short calls;
+    beside it the read ceiling for the same bytes."""
+    n, k = 65536, 16384
+    qws = torch.empty(nv.nvfp4_quantize_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+    mats = []
+    for c in range(2):
+        W = workloads.draw_weights_device(n, k, 6_000_000 + c, dev)
+        mats.append(nv.nvfp4_quantize(W, workspace=qws))
+        del W
+    del qws
+    nb = packed_weight_bytes(n, k)
+    ceil_us = pctl(read_ceiling(nv, torch, dev, ceil_buf, nb, 20), 50)
+    res = {"shape": [n, k], "packed_bytes": nb, "copies": len(mats), "read_ceiling_us": round(ceil_us, 2),
+           "by_rows": {}}
+    for r in rows_list:
+        x = workloads.draw_x_device(r, k, 6_000_100 + r, dev)
+        y = torch.empty((r, n), dtype=torch.bfloat16, device=dev)
+        us = time_rotating(torch, lambda i: nv.nvfp4_gemv(mats[i], x, out=y), len(mats), reps)
+        gbs = nb / (us * 1e-6) / 1e9
+        res["by_rows"][str(r)] = {"us": round(us, 2), "GB_per_s": round(gbs, 1),
+                                  "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                                  "pct_of_read_ceiling": round(100 * ceil_us / us, 1)}
+        log("long call %dx%d rows=%d: %.2f us, %.1f GB/s (%.1f%% of 8 TB/s, %.1f%% of the read ceiling)"
+            % (n, k, r, us, gbs, 100 * gbs / HBM_PEAK_GBS, 100 * ceil_us / us))
+    del mats
+    return res
+
+
 def time_mx(nv, torch, dev, rows_list, reps):
     """The MXFP4 projection (nvfp4_mxfp4_gemv) on an lm-head-sized [151936 x
     5120] and a gate-sized [17408 x 5120] matrix: random codes and E8M0 scale
@@ -792,6 +824,9 @@ def main():
                                                 v["pct_hbm_peak_median"], v["read_ceiling_median_us"],
                                                 v["derived_floor_us"]))
 
+    long_call = None if args.step_only else time_long_call(
+        nv, torch, dev, workloads, [r for r in (1, 8) if r in rows_list] or [rows_list[0]], 20, ceil_buf)
+
     dense = None
     skip_formats = args.no_dense or args.step_only
     if not skip_formats:
@@ -842,6 +877,7 @@ def main():
         "wait_timeouts": wait_flag,
         "parity_sample": parity or None,
         "single_calls": singles,
+        "long_call": long_call,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_lm_head": dense,
