@@ -843,11 +843,23 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         s_seg.arr[tid] = 0u;
         s_seg.done[tid] = tid - red_buffers(ROWS);
     }
+    // This workgroup's geometry of every call of the launch, computed once
+    // here (one call per thread) rather than by every wave a call ahead: its
+    // divisions are no small part of a short call (measured: computing it
+    // twice per call made the 1-row decode step 5% longer).
+    __shared__ Geometry s_geo[SEQ ? kSeqMax : 1];
     constexpr int kDescWords = sizeof(CallDesc) / 4;
+    constexpr int kGeoWords = sizeof(Geometry) / 4;
+    static_assert(sizeof(Geometry) % 4 == 0, "geometries are read as words");
     if (SEQ) {
         const uint32_t *src = reinterpret_cast<const uint32_t *>(args.call);
         uint32_t *dst = reinterpret_cast<uint32_t *>(s_calls);
         for (int i = tid; i < a.ncalls * kDescWords; i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+        for (int c = tid; c < a.ncalls; c += blockDim.x) {
+            const CallDesc &dc = s_calls[c];
+            s_geo[c] = make_geometry(dc, !(dc.flags & kNorm) ? g : kMaxWorkgroups);
+        }
     }
     __syncthreads();
     auto desc = [&](int c) {
@@ -883,7 +895,14 @@ __global__ __launch_bounds__(max_waves_for_rows(ROWS) * 64) void seq_kernel(Kern
         const bool live = k < ncalls;
         p.d = desc(live ? k : ncalls - 1);
         const CallDesc &d = p.d;
-        p.q = make_geometry(d, live && !(d.flags & kNorm) ? g : kMaxWorkgroups);
+        if (SEQ && live) {
+            const uint32_t *gp = reinterpret_cast<const uint32_t *>(&s_geo[k]);
+            uint32_t *go = reinterpret_cast<uint32_t *>(&p.q);
+#pragma unroll
+            for (int i = 0; i < kGeoWords; ++i) go[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)gp[i]);
+        } else {
+            p.q = make_geometry(d, live && !(d.flags & kNorm) ? g : kMaxWorkgroups);
+        }
         const Geometry &q = p.q;
         p.nw = sw < d.waves && sw < q.total ? (q.total - sw + d.waves - 1) / d.waves : 0;
         p.fetch = p.nw > 0;
