@@ -119,6 +119,9 @@ def parse_args():
     ap.add_argument("--step-only", action="store_true",
                     help="time the decode step alone, for profiling: no stand-alone pair, norm-step, read-ceiling, "
                          "single-call or format timings (their launches would mix with the step's in a profile)")
+    ap.add_argument("--long-call-only", action="store_true",
+                    help="time the long [65536 x 16384] call alone at the --rows row counts, for profiling the "
+                         "tile loop without the decode step's per-call work; prints its figures as JSON")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("RDREQ_CSV", "WRITE_CSV", "LAUNCHES_PER_STEP"),
                     help="write the decode-step kernels' HBM traffic per launch from two rocprofv3 --pmc counter "
                          "collections (TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_64B_sum "
@@ -715,6 +718,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     rows_list = [int(r) for r in args.rows.split(",")]
+
+    if args.long_call_only:
+        lbuf = torch.zeros(CEILING_BYTES, dtype=torch.uint8, device=dev)
+        print(json.dumps({"long_call": time_long_call(nv, torch, dev, workloads, rows_list, args.steps, lbuf)}),
+              flush=True)
+        del lbuf
+        torch.cuda.synchronize()
+        return
 
     t0 = time.time()
     mats = build_sweep(nv, workloads, torch, dev, args.layers)
