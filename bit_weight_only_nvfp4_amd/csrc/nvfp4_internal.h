@@ -175,10 +175,14 @@ __host__ __device__ constexpr int red_rows(int krows) {
 // the decode step: 3%, 5% and 1% faster at 1, 2 and 4 rows, 2.5-5% slower at
 // 6-8 rows.
 __host__ __device__ constexpr bool barrier_free_segments(int krows) { return krows <= 4; }
-// Buffers of wave-reduction slots: two without barriers (consecutive segments
-// alternate, so a wave waits for wave 0's reads of a segment only two
-// segments later), else one.
-__host__ __device__ constexpr int red_buffers(int krows) { return barrier_free_segments(krows) ? 2 : 1; }
+// Buffers of wave-reduction slots, consecutive segments alternating: without
+// barriers a wave waits for wave 0's reads of a segment only two segments
+// later; with barriers (6-8 rows) a wave writing a segment's slots has passed
+// the previous segment's barriers, which wave 0 reaches only after reading
+// the sums of the one before, so no barrier opens a segment end (0.4-0.5%
+// faster decode step at 6 and 8 rows).  One buffer from 12 rows on, where
+// the LDS holds no second one: a barrier opens each segment end there.
+__host__ __device__ constexpr int red_buffers(int krows) { return krows <= 8 ? 2 : 1; }
 
 struct StreamPlan {
     int64_t n, k;

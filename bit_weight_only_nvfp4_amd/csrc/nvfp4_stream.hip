@@ -425,7 +425,7 @@ __device__ __forceinline__ void finish_segment(const LaunchShared &a, const Call
     if constexpr (kBarrierFree) {
         // the slots of buffer b are free once wave 0 has read them for segment seg - NBUF
         if (wave != 0) lds_wait_ge(&ss.done[b], seg - NBUF, a, lane);
-    } else {
+    } else if constexpr (NBUF == 1) {
         __syncthreads();   // the previous segment's reads of `red` are done
     }
     // Slots in position order (sw): the sums below run in that order.  A
