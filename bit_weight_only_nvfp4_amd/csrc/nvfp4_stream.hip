@@ -19,8 +19,10 @@
 //     and its results written, the first NB super-tiles of the next call are
 //     already in flight;
 //   * a workgroup owns whole strips of 64 features where it can (no split-K,
-//     no cross-workgroup traffic); the remaining units of work are cut into
-//     balanced pieces of strips ("stream-K");
+//     no cross-workgroup traffic); skinny shapes are cut into balanced pieces
+//     of strips over all workgroups ("stream-K"), and the strips left over
+//     past whole strips per workgroup into at most 4 pieces each, on the last
+//     workgroups (those a narrower call before them left idle);
 //   * pieces of a strip are summed in piece order by the last to arrive (an
 //     arrival counter), so results are bitwise deterministic with no float
 //     atomics, and identical whether a call runs alone or in a sequence;
@@ -31,7 +33,10 @@
 //     four at once, each with its own workspace region;
 //   * the waves of a workgroup meet only where they must: up to 4 rows a
 //     segment end takes no barrier (LDS counters), from 6 rows on it takes
-//     barriers and spreads the sums over the waves.
+//     barriers and spreads the sums over the waves;
+//   * the workgroup's geometry of every call is computed once per launch
+//     (LDS table), and up to 4 rows a tile's weights are read through a
+//     buffer resource over the super-tile (no per-load address arithmetic).
 // Everything one workgroup writes to global memory -- outputs, partial sums,
 // counters -- is written by its wave 0 with device-coherent (sc1) accesses, and
 // wave 0 is the only wave with no loads in flight across a call boundary, so it
@@ -41,8 +46,9 @@
 //
 // Work units of a call: strip s in [0, S) x super-tile u in [0, T).  G
 // workgroups; the first G*F strips are owned, F per workgroup; the R = S - G*F
-// remaining strips form R*T shared units split into G contiguous ranges
-// [g*RT/G, (g+1)*RT/G), cut at strip boundaries into pieces.
+// remaining strips form R*T shared units split into Gs contiguous ranges
+// [s*RT/Gs, (s+1)*RT/Gs) of the last Gs workgroups (s = g - (G - Gs); Gs = G
+// for skinny shapes), cut at strip boundaries into pieces.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
