@@ -64,6 +64,17 @@ def test_workspace_bytes(nv):
     assert w1 > 0 and w1 == nv.nvfp4_workspace_bytes(5120, 17408, 1)
     assert nv.nvfp4_workspace_bytes(5120, 17408, 8) > w1
     assert nv.nvfp4_workspace_bytes(17408, 5120, 1, dual=True) > nv.nvfp4_workspace_bytes(17408, 5120, 1) > 0
+    # Strips left over past one per workgroup: at most 4 pieces each, never more
+    # than the leftover's super-tiles; partial sums of R strips x pieces x
+    # matrices x rows x 64 fp32 after the 161 KiB of counters.
+    state, strip = 161 << 10, 64 * 4
+    assert nv.nvfp4_workspace_bytes(17408, 5120, 1, dual=True) == state + 16 * 4 * 2 * 1 * strip
+    assert nv.nvfp4_workspace_bytes(17408, 5120, 8, dual=True) == state + 16 * 4 * 2 * 8 * strip
+    assert nv.nvfp4_workspace_bytes(16448, 5120, 1) == state + 1 * 4 * strip     # 257 strips of 20 super-tiles
+    assert nv.nvfp4_workspace_bytes(16448, 512, 1) == state + 1 * 2 * strip      # 2 super-tiles: 2 pieces
+    assert nv.nvfp4_workspace_bytes(16448, 256, 1) == 0                          # one super-tile: one owner
+    assert nv.nvfp4_workspace_bytes(19200, 1024, 1) == state + 44 * 4 * strip    # 44 strips of 4 super-tiles
+    assert nv.nvfp4_workspace_bytes(32896, 256, 1, dual=True) == 0               # two leftover super-tiles
     # more than 16 rows run as row chunks, whose launch needs the counters and waits
     assert nv.nvfp4_workspace_bytes(256, 512, 16) == 0
     assert nv.nvfp4_workspace_bytes(256, 512, 17) == SEQ_WS
