@@ -132,7 +132,7 @@ static_assert(sizeof(CallDesc) % 4 == 0, "call descriptors are copied as words")
 
 constexpr int kSC1 = 16;                          // cache policy: device-coherent access
 constexpr int kNT = 2;                            // cache policy: nontemporal (streamed once)
-constexpr int kBufferLoadRowsCut = 4;
+constexpr int kBufferLoadRowsCut = 4;             // tile weight loads through a buffer resource up to here
 constexpr int kDroppedOffset = 0x7fffffff;        // past any buffer: loads read 0, stores are dropped
 constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit data format
 // Polls a wait between calls makes before it gives up (each poll is a round
@@ -1279,11 +1279,11 @@ StreamPlan make_stream_plan(int64_t n, int64_t k, int rows, int dual) {
     // to cover the memory latency at full bandwidth.
     int waves = max_waves_for_rows(rows);
     // Strips left over past whole strips per workgroup are spread over the
-    // last Gs workgroups, so that each is cut into about kLeftoverPieces
-    // pieces: every piece adds a partial sum, and the strip's completion waits
-    // for the last of them.
-    // (at least one unit each: a workgroup without units would be counted
-    // as a piece that never arrives).
+    // last Gs workgroups, so that each is cut into at most kLeftoverPieces
+    // pieces (every piece adds a partial sum, and the strip's completion waits
+    // for the last of them), and every one of those workgroups gets at least
+    // one unit (one without units would be counted as a piece that never
+    // arrives).
     pl.Gs = pl.G;
     if (pl.F > 0 && pl.R > 0) {
         const long long gs = std::min<long long>((long long)pl.R * kLeftoverPieces, (long long)pl.R * T);
