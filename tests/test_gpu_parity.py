@@ -844,6 +844,64 @@ def test_sequence_random_call_lists(nv, seed):
     assert nv.counters_clear(ws), "counters not returned to zero"
 
 
+_LEFTOVER_LIST_SHAPES = ((16448, 512), (16448, 1536), (512, 16448), (1536, 16448), (512, 512), (1536, 512),
+                         (512, 1536))
+_leftover_pool = {}
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_sequence_random_call_lists_leftover_strips(nv, seed):
+    """Random call lists as above over shapes with strips left over past one
+    per workgroup (257 strips of 2 and 6 super-tiles: 2 and 4 pieces on the
+    last workgroups), skinny shapes with k = 16448, and small ones, singles
+    and pairs, reading and overwriting each other's buffers: the sequence
+    equals the same calls made one by one, bit for bit, at 1 and 8 rows."""
+    rows = (1, 8)[seed]
+    if not _leftover_pool:
+        r0 = np.random.default_rng(4242)
+        for n, k in _LEFTOVER_LIST_SHAPES:
+            _leftover_pool[(n, k)] = [
+                _pack(nv, oracle.quantize(r0.standard_normal((n, k), dtype=np.float32) * np.float32(0.05)))
+                for _ in range(2)]
+    dims = (512, 1536, 16448)
+    rng = np.random.default_rng(2000 + seed)
+    start = {d: [workloads.draw_x(rng, rows, d) for _ in range(3)] for d in dims}
+    plan = []
+    for _ in range(24):
+        n, k = _LEFTOVER_LIST_SHAPES[int(rng.integers(len(_LEFTOVER_LIST_SHAPES)))]
+        i, j = int(rng.integers(3)), int(rng.integers(3))
+        if k == n and i == j:
+            j = (j + 1) % 3
+        plan.append((n, k, i, j, bool(rng.random() < 0.3), int(rng.integers(2))))
+
+    def fresh():
+        return {d: [_x_dev(b) for b in start[d]] for d in dims}
+
+    def calls_of(bufs):
+        return [(_leftover_pool[(n, k)][wi], _leftover_pool[(n, k)][1 - wi] if pair else None, bufs[k][i], bufs[n][j])
+                for n, k, i, j, pair, wi in plan]
+
+    print("random leftover-strip call list seed=%d rows=%d" % (seed, rows), flush=True)
+    bufs = fresh()
+    seq = nv.Sequence(calls_of(bufs))
+    ws = torch.zeros(max(seq.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    seq.launch(ws)
+    torch.cuda.synchronize()
+    assert nv.wait_flag(ws) == 0
+    assert nv.counters_clear(ws), "counters not returned to zero"
+    ref = fresh()
+    for w, up, x, y in calls_of(ref):
+        if up is None:
+            nv.nvfp4_gemv(w, x, out=y, workspace=ws)
+        else:
+            nv.nvfp4_gemv_dual_silu(w, up, x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    for d in dims:
+        for i in range(3):
+            assert torch.equal(bufs[d][i].view(torch.int16), ref[d][i].view(torch.int16)), (seed, d, i, seq.waits)
+    assert nv.counters_clear(ws), "counters not returned to zero"
+
+
 def test_sequence_full_size_decode_step(nv):
     """Two full-size decode-step layers through one sequence (a shared launch
     per row count, the weight pipeline running across calls): the last layer's
