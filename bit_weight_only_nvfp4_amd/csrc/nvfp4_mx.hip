@@ -13,10 +13,10 @@
 // two weights exactly (a code has 2 significant bits; bf16 holds every
 // code * 2^e for e in -126..125).  The activations then feed the bf16 matrix
 // cores as stored: no activation staging, no scale multiply.
-//   * one workgroup per 64 features (four 16-feature products; 32 below
-//     32768 features, so that small matrices still give two workgroups per
-//     CU), 4 waves each over a quarter of k in steps of 256; two steps in
-//     flight (176 registers, two waves per SIMD);
+//   * one workgroup per 64 features (four 16-feature products), 2 waves
+//     each over half of k in steps of 256; below 32768 features one per 32
+//     features with one wave over all of k, so that small matrices still
+//     give two workgroups per CU; two steps in flight per wave;
 //   * per step a lane (q, n) takes k = 64 q .. 64 q + 63 of the step -- two
 //     MX blocks, so two scale bytes per feature block -- as 32 contiguous
 //     bytes of codes per feature block (a row's four lanes read 128
@@ -29,7 +29,8 @@
 //     with no scale loads took 85 us instead of 126), so where k is a
 //     multiple of 256 the row's 8 scale bytes of a step are one 8-byte load
 //     shared by its four lanes: 104 us;
-//   * the waves' sums are added in LDS in wave order (deterministic).
+//   * the waves' sums are added in LDS in wave order (deterministic; a
+//     feature's sum depends on the matrix's width class, not on the rows).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,7 +44,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMxWaves = 4;
 constexpr int kMxStepK = 256;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kDeviceCoherent = 16;
@@ -152,11 +152,12 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
     return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? nan : rne);
 }
 
-// FB 16-feature blocks per workgroup, BUFS steps in flight per wave.
-template <int FB, int BUFS, bool WIDE>
-__global__ __launch_bounds__(kMxWaves * 64) void mx_kernel(MxArgs a) {
+// FB 16-feature blocks per workgroup, WAVES waves over parts of k, BUFS
+// steps in flight per wave.
+template <int FB, int WAVES, int BUFS, bool WIDE>
+__global__ __launch_bounds__(WAVES * 64) void mx_kernel(MxArgs a) {
     constexpr int kMxFeatures = 16 * FB;
-    __shared__ float red[kMxWaves][FB][16][16];   // [wave][feature block][row][feature]
+    __shared__ float red[WAVES][FB][16][16];   // [wave][feature block][row][feature]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, n16 = lane & 15;
@@ -189,11 +190,11 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_kernel(MxArgs a) {
     __syncthreads();
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, (uint32_t)((size_t)a.rows * a.n * (a.out_f32 ? 4 : 2)));
 #pragma unroll
-    for (int o = tid; o < 16 * kMxFeatures; o += kMxWaves * 64) {
+    for (int o = tid; o < 16 * kMxFeatures; o += WAVES * 64) {
         const int r = o / kMxFeatures, f = o % kMxFeatures;
         float t = red[0][f >> 4][r][f & 15];
 #pragma unroll
-        for (int w = 1; w < kMxWaves; ++w) t += red[w][f >> 4][r][f & 15];
+        for (int w = 1; w < WAVES; ++w) t += red[w][f >> 4][r][f & 15];
         const int at = r * a.n + f0 + f;
         const bool keep = r < a.rows && f < nf;
         if (a.out_f32)
@@ -217,24 +218,30 @@ hipError_t launch_mx(const void *codes, const void *scales, int64_t n, int64_t k
     a.k = (int)k;
     a.rows = rows;
     a.out_f32 = out_f32;
-    const int64_t per = (k + kMxWaves - 1) / kMxWaves;
-    a.kw = (int)((per + kMxStepK - 1) / kMxStepK * kMxStepK);
     constexpr int BUFS = 2;
     const bool wide = k % 256 == 0 && reinterpret_cast<uintptr_t>(scales) % 8 == 0;
-    // Below 512 groups of 64 features (two workgroups per CU), groups of 32:
-    // twice the workgroups, the same sums (each feature's products and their
-    // order do not depend on the group size).  Measured on [17408 x 5120]:
-    // 20.0 us against 22.1 at 1 row, 24.1 against 25.3 at 8.
+    // Below 512 groups of 64 features (two workgroups per CU), groups of 32
+    // features, one wave over all of k: twice the workgroups and 20 steps per
+    // wave at k = 5120 (17.5 us against 20.0 with four waves over quarters of
+    // k on [17408 x 5120] at 1 row, 21.6 against 24.1 at 8).  From there on,
+    // groups of 64 features, two waves over halves of k (105 us against 106
+    // with four waves, 120 with one, on [151936 x 5120]).
+    auto wave_k = [&](int waves) {
+        const int64_t per = (k + waves - 1) / waves;
+        return (int)((per + kMxStepK - 1) / kMxStepK * kMxStepK);
+    };
     if (n < 32768) {
-        constexpr int FB = 2;
+        constexpr int FB = 2, W = 1;
+        a.kw = wave_k(W);
         const unsigned grid = (unsigned)((n + 16 * FB - 1) / (16 * FB));
-        if (wide) hipLaunchKernelGGL((mx_kernel<FB, BUFS, true>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
-        else hipLaunchKernelGGL((mx_kernel<FB, BUFS, false>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+        if (wide) hipLaunchKernelGGL((mx_kernel<FB, W, BUFS, true>), dim3(grid), dim3(W * 64), 0, stream, a);
+        else hipLaunchKernelGGL((mx_kernel<FB, W, BUFS, false>), dim3(grid), dim3(W * 64), 0, stream, a);
     } else {
-        constexpr int FB = 4;
+        constexpr int FB = 4, W = 2;
+        a.kw = wave_k(W);
         const unsigned grid = (unsigned)((n + 16 * FB - 1) / (16 * FB));
-        if (wide) hipLaunchKernelGGL((mx_kernel<FB, BUFS, true>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
-        else hipLaunchKernelGGL((mx_kernel<FB, BUFS, false>), dim3(grid), dim3(kMxWaves * 64), 0, stream, a);
+        if (wide) hipLaunchKernelGGL((mx_kernel<FB, W, BUFS, true>), dim3(grid), dim3(W * 64), 0, stream, a);
+        else hipLaunchKernelGGL((mx_kernel<FB, W, BUFS, false>), dim3(grid), dim3(W * 64), 0, stream, a);
     }
     return hipGetLastError();
 }
