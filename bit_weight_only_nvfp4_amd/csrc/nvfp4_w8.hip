@@ -228,6 +228,11 @@ hipError_t launch_w8(const void *codes, const void *scales, int64_t n, int64_t k
     a.k = (int)k;
     a.rows = rows;
     a.out_f32 = out_f32;
+    // 16 features per workgroup where that still leaves two workgroups per CU
+    // (28.2 us against 31.0 on [17408 x 5120] at 1 row, 35.6 against 35.7 at
+    // 8), else 32 ([5120 x 17408]: 30.7 us against 34.2 with 16).  Either way
+    // each feature's sum runs over the same 4 quarters of k in the same order.
+    if (n >= 16 * 512) return launch_cfg<1, 4, 2>(a, n, k, stream);
     return launch_cfg<2, 4, 2>(a, n, k, stream);
 }
 
