@@ -40,7 +40,9 @@ def _run(nv, c, s, xb):
     return a, y16.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("n,k", [(1, 128), (65, 4096), (200, 768), (1000, 5120), (64, 17408), (130, 128)])
+# from 8192 features on the kernel runs 16 features per workgroup, below 32
+@pytest.mark.parametrize("n,k", [(1, 128), (65, 4096), (200, 768), (1000, 5120), (64, 17408), (130, 128),
+                                 (8200, 1024)])
 def test_w8_random(nv, n, k):
     rng = np.random.default_rng(n * 17 + k)
     c, s = oracle.w8_quantize((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
@@ -51,7 +53,7 @@ def test_w8_random(nv, n, k):
         check.check_gemv(y32, y16, ref, absd, ref16, label="w8g32 %dx%d rows=%d" % (n, k, rows))
 
 
-@pytest.mark.parametrize("n,k", [(64, 256), (97, 4096), (300, 2048)])
+@pytest.mark.parametrize("n,k", [(64, 256), (97, 4096), (300, 2048), (8211, 256)])
 def test_w8_exact_arithmetic(nv, n, k):
     """Scales 2^-3..2^-1 (exact fp16), codes +-127, x = q / 4 with |q| <= 3:
     each product is a multiple of 2^-5 of magnitude < 48, so every partial sum
