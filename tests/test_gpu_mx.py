@@ -49,7 +49,8 @@ def _run(nv, c, s, xb):
     return a, y16.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-# groups of 32 features below 32768 (the first six), of 64 from there on (the last two)
+# groups of 32 features with one wave over all of k below 32768 (the first six), of 64 with two
+# waves over halves of k from there on (the last two)
 @pytest.mark.parametrize("n,k", [(1, 32), (65, 4128), (200, 800), (1000, 5120), (64, 17408), (130, 96),
                                  (32800, 256), (40000, 288)])
 def test_mx_random(nv, n, k):
